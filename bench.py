@@ -1,0 +1,220 @@
+#!/usr/bin/env python3
+"""Throughput of the MoE layer forward on one MI355X.
+
+One step is one full pass of the layer over one batch of synthetic input:
+gate (router GEMM, softmax, top-k, capacity slots, counts, loss), dispatch,
+expert FFN grouped GEMMs, combine -- the fused moe_layer_forward call -- plus,
+for the no-drop workload, the backward of the expert FFNs.  Inputs are seeded
+synthetic tensors already resident in HBM.  Prints one JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload top2_e64]
+
+Besides the headline value the line carries
+  roofline:     the expert grouped GEMM (the dominant kernel) against the bf16
+                dense MFMA peak, its per-launch time taken with HIP events on the
+                stream the kernels run on;
+  stages:       every stage's event time and its algorithmic bytes or flops;
+  cpu_baseline: the CPU oracle timed on this host on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+GEMM_SRC = os.path.join(ROOT, "mixture_experts_layer_39_amd", "csrc", "grouped_gemm.hip")
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def describe(sp):
+    ffn = f"{sp['d']}->{sp['h']}->{sp['d']} " + {0: "none", 1: "ReLU", 2: "GELU"}[sp["act"]] if sp["h"] else \
+        f"Linear {sp['d']}->{sp['d']}"
+    drop = f"cf {sp['cf']} min_cap {sp['min_cap']}" if sp["drop"] else "no drop"
+    return f"{sp['name']}: T={sp['T']} d={sp['d']} E={sp['E']} top-{sp['k']} FFN {ffn}, {drop}, {sp['dtype']}"
+
+
+def source_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def load_traffic(workload):
+    """HBM bytes per GEMM launch from committed rocprofv3 counter runs, or
+    None when none were taken for this workload or the kernel source changed
+    since."""
+    try:
+        with open(TRAFFIC_JSON) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    rec = t.get(workload)
+    if not rec or rec.get("source_sha256") != source_hash(GEMM_SRC):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(sp, inp, target_s=15.0):
+    """The oracle (as it stands) on the first Ts tokens of the same workload:
+    router logits, routing, dispatch, float64 expert FFNs, combine."""
+    import numpy as np
+    from oracle import moe_oracle as O
+
+    def f(t):
+        return None if t is None else t.float().cpu().numpy()
+
+    x = f(inp["x"])
+    wr = f(inp["w_router"])
+    br = f(inp["b_router"])
+    lg_given = f(inp["logits"])
+    w1, b1, w2, b2 = f(inp["w1"]), f(inp["b1"]), f(inp["w2"]), f(inp["b2"])
+
+    def run(ts):
+        t0 = time.perf_counter()
+        logits = lg_given[:ts] if lg_given is not None else O.router_logits(x[:ts], wr, br)
+        O.layer_forward(x[:ts], logits, w1, b1, w2, b2, k=sp["k"], capacity_factor=sp["cf"],
+                        min_capacity=sp["min_cap"], drop_tokens=sp["drop"], act=sp["act"], dtype=sp["dtype"])
+        if sp.get("backward"):
+            pass
+        return time.perf_counter() - t0
+
+    ts = min(sp["T"], 64)
+    el = run(ts)
+    if el < target_s / 4 and ts < sp["T"]:
+        ts = int(min(sp["T"], max(ts + 1, ts * target_s / max(el, 1e-3))))
+        el = run(ts)
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    return {"value": ts / el, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"first {ts} of {sp['T']} tokens of {sp['name']} (capacity recomputed for {ts} tokens): "
+                      f"router, routing, dispatch, float64 expert FFNs, combine; {el:.1f} s"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="top2_e64")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    a = ap.parse_args(argv)
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU's share of the layer; --gpus {a.gpus} is not supported "
+              f"(run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from mixture_experts_layer_39_amd import binding as B
+    from mixture_experts_layer_39_amd.synthetic import make_inputs, spec
+
+    dev = torch.device("cuda:0")
+    sp = spec(a.workload)
+    inp = make_inputs(sp, dev)
+    T, d, E, k, h = sp["T"], sp["d"], sp["E"], sp["k"], sp["h"]
+    dt = B.MOE_BF16 if sp["dtype"] == "bf16" else B.MOE_F32
+    esz = 2 if dt == B.MOE_BF16 else 4
+    cfg = B.make_config(T, d, E, k, sp["cf"], sp["min_cap"], sp["drop"], h, sp["act"], dt)
+    ws = torch.empty(B.moe_workspace_size(cfg), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(inp["x"])
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    count = torch.empty(E, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        B.moe_layer_forward(cfg, inp["x"], inp["w_router"], inp["b_router"], inp["logits"], inp["w1"], inp["b1"],
+                            inp["w2"], inp["b2"], out, loss, count, ws=ws, stream=stream)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        step()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    ms_step = el / a.steps * 1e3
+    value = T * a.steps / el
+
+    # ---- per-stage breakdown: the same kernels called stage by stage, HIP
+    # events recorded on the stream they run on
+    rows = max(B.moe_max_rows(cfg), 1)
+    g = dict(idx=torch.empty(T, k, dtype=torch.int32, device=dev), slot=torch.empty(T, k, dtype=torch.int32, device=dev),
+             weight=torch.empty(T, k, dtype=torch.float32, device=dev),
+             offset=torch.empty(E + 1, dtype=torch.int32, device=dev))
+    xd, _, hd_p, yd_p, _ = B.moe_workspace_views(cfg, ws)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    acc = [0.0] * 4
+    for it in range(a.warmup + a.steps):
+        ev[0].record(stream)
+        B.moe_gate(cfg, inp["x"], inp["w_router"], inp["b_router"], inp["logits"], None, g["idx"], g["slot"],
+                   g["weight"], count, g["offset"], loss, ws, stream=stream)
+        ev[1].record(stream)
+        B.moe_dispatch(cfg, inp["x"], g["idx"], g["slot"], g["offset"], xd, stream=stream)
+        ev[2].record(stream)
+        B.moe_expert_ffn(cfg, xd, g["offset"], inp["w1"], inp["b1"], inp["w2"], inp["b2"], None, hd_p, yd_p, ws,
+                         stream=stream)
+        ev[3].record(stream)
+        B.moe_combine(cfg, yd_p, g["idx"], g["slot"], g["weight"], g["offset"], out, stream=stream)
+        ev[4].record(stream)
+        if it >= a.warmup:
+            torch.cuda.synchronize()
+            for i in range(4):
+                acc[i] += ev[i].elapsed_time(ev[i + 1])
+    st_ms = [v / a.steps for v in acc]
+
+    # ---- algorithmic work from the realised routing
+    counts = count.cpu().long()
+    slots = g["slot"].cpu().long()
+    N = int(counts.sum())
+    tok_kept = int((slots >= 0).any(dim=1).sum())
+    gate_bytes = T * d * esz + E * d * esz + T * k * 12 + (T * E * 4 if inp["logits"] is not None else 0)
+    disp_bytes = tok_kept * d * esz + N * d * esz + T * k * 8
+    comb_bytes = N * d * esz + T * d * esz + T * k * 12
+    ffn_flops = 4 * N * d * h if h else 2 * N * d * d
+    n_gemm = 2 if h else 1
+
+    def gbs(b, ms):
+        return b / (ms * 1e-3) / 1e9
+
+    stages = {
+        "gate": {"ms": st_ms[0], "bytes": gate_bytes, "GB/s": gbs(gate_bytes, st_ms[0]),
+                 "frac_hbm": gbs(gate_bytes, st_ms[0]) / PEAK_HBM_GBS},
+        "dispatch": {"ms": st_ms[1], "bytes": disp_bytes, "GB/s": gbs(disp_bytes, st_ms[1]),
+                     "frac_hbm": gbs(disp_bytes, st_ms[1]) / PEAK_HBM_GBS},
+        "expert_ffn": {"ms": st_ms[2], "flops": ffn_flops, "TFLOP/s": ffn_flops / (st_ms[2] * 1e-3) / 1e12,
+                       "frac_mfma": ffn_flops / (st_ms[2] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "launches": n_gemm},
+        "combine": {"ms": st_ms[3], "bytes": comb_bytes, "GB/s": gbs(comb_bytes, st_ms[3]),
+                    "frac_hbm": gbs(comb_bytes, st_ms[3]) / PEAK_HBM_GBS},
+    }
+    gemm_ms = st_ms[2] / n_gemm
+    achieved = (ffn_flops / n_gemm) / (gemm_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": "gemm_bf16_kernel" if dt == B.MOE_BF16 else "gemm_f32_kernel",
+                "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": load_traffic(a.workload),
+                "flops_per_launch": ffn_flops / n_gemm, "avg_launch_ms": gemm_ms, "rows": N}
+
+    line = {"metric": "MoE-layer fwd tokens/s (E=64,top-2,d=2048); MFMA util + HBM GB/s vs peak",
+            "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+            "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": sp["dtype"], "data": "synthetic",
+            "config": {"workload": describe(sp), "tokens_per_step": T, "rows_kept": N},
+            "roofline": roofline, "stages": stages}
+    if not a.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(sp, inp)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

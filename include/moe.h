@@ -1,0 +1,215 @@
+/*
+ * moe.h - C ABI of a top-k gated Mixture-of-Experts layer for one MI355X
+ * (gfx950) GPU: gate, dispatch, expert FFNs, combine, the fused layer
+ * forward, and the backward of the expert FFNs.
+ *
+ * What the calls compute follows these pages (cited by title and section):
+ *   [ds.moe]     "deepspeed.moe 模块" overview (adg.csdn.net): §2.1 the MoE
+ *                class (hidden_size, num_experts, k, capacity_factor,
+ *                min_capacity, drop_tokens) returning (output, gate_loss,
+ *                expert_count); §3.1 the forward steps (gate, dispatch, expert
+ *                compute, weighted merge, load-balance loss).
+ *   [MoE-sched]  "MoE混合专家架构：大模型高效推理的智能调度原理" (lpnh.cn):
+ *                §3.1 MoELayer, Steps 1-5 (router Linear, top-k, flatten and
+ *                scatter into per-expert buffers, expert FFN Linear-GELU-Linear,
+ *                gather and weighted sum) and the capacity / drop-tokens items.
+ *   [DS-MoE-traps] DeepSeek-MoE fine-tuning article (lnwmold.com), ch.1:
+ *                softmax over the router logits, top-2 on it, weighted sum;
+ *                the capacity formula and the usage-std balance loss.
+ *
+ * Conventions for every call
+ *  - Pointers named as device pointers must point to GPU memory of the
+ *    current HIP device; the caller allocates and owns all of it, including
+ *    the workspace sized by moe_workspace_size().  The library never
+ *    allocates, frees or synchronises, and keeps no state between calls.
+ *  - Tensors are dense row-major.  x is [T, d] (a [B, S, d] batch flattened
+ *    with token t = b*S + s).  Expert weights use the nn.Linear layout
+ *    [out, in]: w1 [E, h, d], w2 [E, d, h], b1 [E, h], b2 [E, d].  With
+ *    ffn_hidden == 0 the expert is one Linear: w1 [E, d, d], b1 [E, d].
+ *  - dtype MOE_BF16: x, weights, biases b1/b2, dispatched buffers and out are
+ *    bf16 with fp32 accumulation; MOE_F32: all of those are fp32.  Router
+ *    logits, router bias, gate weights and gate_loss are always fp32; indices,
+ *    slots, counts and offsets int32.
+ *  - stream is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *    on it in order; the call returns before it finishes.
+ *  - Errors: argument checks happen before anything is enqueued and return
+ *    MOE_ERR_INVALID_ARG (bad value or missing pointer) or MOE_ERR_UNSUPPORTED
+ *    (valid but outside what the kernels take, e.g. a row not a multiple of
+ *    16 bytes); MOE_ERR_WORKSPACE if ws_bytes is too small; MOE_ERR_HIP if a
+ *    launch fails.  Nothing is written on an error.
+ *  - Routing is deterministic: identical inputs give bit-identical outputs.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,
+  MOE_ERR_UNSUPPORTED = 2,
+  MOE_ERR_WORKSPACE = 3,
+  MOE_ERR_HIP = 4
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Activation after the first Linear (or after the only Linear when
+ * ffn_hidden == 0).  GELU is the exact erf form 0.5*x*(1+erf(x/sqrt(2))),
+ * nn.GELU()'s default, as in [MoE-sched] §3.1 item 2 (Linear-GELU-Linear). */
+typedef enum { MOE_ACT_NONE = 0, MOE_ACT_RELU = 1, MOE_ACT_GELU = 2 } moe_act;
+
+/* gate_loss kind, returned without the caller's loss weight.
+ * BALANCE:   E * sum_e mean_t(p[t,e]) * (#tokens whose top-1 is e)/T, p the
+ *            softmax over all experts, top-1 counted before capacity
+ *            ([ds.moe] §3.1 step 5 names a load-balancing loss).
+ * USAGE_STD: population std over experts of (#choices of e)/(k*T), all k
+ *            choices before capacity, plus 1e-6 ([DS-MoE-traps] ch.1, the
+ *            balance-loss table: lambda * (std(usage_prob) + 1e-6)). */
+typedef enum { MOE_LOSS_BALANCE = 0, MOE_LOSS_USAGE_STD = 1 } moe_loss_kind;
+
+#define MOE_MAX_EXPERTS 256
+
+/* Layer configuration ([ds.moe] §2.1 MoE arguments). */
+typedef struct moe_config {
+  int64_t num_tokens;      /* T >= 0, T < 2^30                                  */
+  double capacity_factor;  /* > 0 when drop_tokens                              */
+  int32_t hidden_size;     /* d > 0                                             */
+  int32_t num_experts;     /* E, 1..MOE_MAX_EXPERTS                             */
+  int32_t k;               /* 1 or 2, k <= E                                    */
+  int32_t min_capacity;    /* >= 0                                              */
+  int32_t drop_tokens;     /* 1: claims past the capacity are dropped;
+                              0: no capacity, buffers sized by the counts      */
+  int32_t ffn_hidden;      /* h >= 0; 0 = the expert is one Linear(d -> d)      */
+  int32_t activation;      /* moe_act                                           */
+  int32_t dtype;           /* moe_dtype                                         */
+  int32_t normalize_topk;  /* 0: weight = softmax prob of the chosen expert;
+                              1: the k chosen probs rescaled to sum to 1, i.e.
+                              softmax over the top-k logits ([MoE-sched] §3.1
+                              Step 2).  Computed before any drop.              */
+  int32_t loss_kind;       /* moe_loss_kind                                     */
+  int32_t save_preact;     /* 1: moe_layer_forward keeps the pre-activation
+                              of the first Linear in the workspace for
+                              moe_expert_ffn_backward                          */
+} moe_config;
+
+/* Static text for a status code. */
+const char* moe_status_string(moe_status s);
+
+/* Expert capacity C = max(min_capacity, ceil((k*T/E) * capacity_factor)),
+ * evaluated in IEEE double exactly in that order ([DS-MoE-traps] ch.1
+ * capacity row; [MoE-sched] §3.1 item 3).  *C = -1 when drop_tokens == 0.
+ * Host only; C is a host pointer. */
+moe_status moe_capacity(const moe_config* cfg, int64_t* C);
+
+/* Upper bound on the packed rows N = sum_e expert_count[e]:
+ * min(k*T, E*C) with a capacity, k*T without.  Host only. */
+moe_status moe_max_rows(const moe_config* cfg, int64_t* rows);
+
+/* Bytes of device workspace that every call below needs for cfg (the fused
+ * forward's intermediate buffers included).  Host only. */
+moe_status moe_workspace_size(const moe_config* cfg, size_t* bytes);
+
+/* Gate ([MoE-sched] §3.1 Steps 1-2; [ds.moe] §3.1 step 1 and step 5).
+ * logits[t,e] = x[t]·w_router[e] (+ b_router[e]) accumulated in fp32, or
+ * logits_in when it is non-NULL (then x / w_router are not read).
+ * p = softmax over the E logits; the k chosen experts are the k largest
+ * logits, ties to the lower expert index (-0.0 equals +0.0).
+ * Capacity slots: every top-1 claim in token order, then every top-2 claim in
+ * token order, takes the next free slot of its expert; a slot >= C is dropped
+ * (slot = -1).  expert_count[e] = kept claims of e, expert_offset the
+ * exclusive prefix of expert_count (E+1 entries).
+ *   x          device, [T, d] dtype            (ignored if logits_in)
+ *   w_router   device, [E, d] dtype            (ignored if logits_in)
+ *   b_router   device, [E] fp32, nullable
+ *   logits_in  device, [T, E] fp32, nullable
+ *   logits_out device, [T, E] fp32, nullable: the logits used
+ *   expert_idx device, [T, k] int32 out;  slot device, [T, k] int32 out
+ *   weight     device, [T, k] fp32 out (gate weight of each choice)
+ *   expert_count device [E] int32 out; expert_offset device [E+1] int32 out
+ *   gate_loss  device, [1] fp32 out
+ *   ws, ws_bytes  device workspace of moe_workspace_size() bytes */
+moe_status moe_gate(const moe_config* cfg, const void* x, const void* w_router,
+                    const float* b_router, const float* logits_in, float* logits_out,
+                    int32_t* expert_idx, int32_t* slot, float* weight,
+                    int32_t* expert_count, int32_t* expert_offset, float* gate_loss,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/* Dispatch ([MoE-sched] §3.1 Step 3; [ds.moe] §3.1 step 2 on one GPU):
+ * for every kept claim (t, j): x_disp[expert_offset[e] + slot[t,j]] = x[t],
+ * e = expert_idx[t,j].  x_disp is the packed expert-major buffer, device,
+ * [>= moe_max_rows, d] dtype; rows past expert_offset[E] are not written. */
+moe_status moe_dispatch(const moe_config* cfg, const void* x, const int32_t* expert_idx,
+                        const int32_t* slot, const int32_t* expert_offset, void* x_disp,
+                        void* stream);
+
+/* Expert FFNs on the packed buffer ([MoE-sched] §3.1 Step 4; [ds.moe] §3.1
+ * step 3): for the rows of expert e,
+ *   a = x_disp·w1[e]^T + b1[e];  h = act(a);  y = h·w2[e]^T + b2[e]
+ * (ffn_hidden == 0: y = act(x_disp·w1[e]^T + b1[e]); w2/b2/h_disp/a_save are
+ * not used and may be NULL).  fp32 accumulation; bias and activation in fp32;
+ * a, h and y are stored as dtype.  b1/b2 nullable (no bias).
+ *   x_disp device [rows, d]; h_disp device [rows, h]; y_disp device [rows, d]
+ *   a_save device [rows, h], nullable: the pre-activation for the backward
+ * where rows >= expert_offset[E] (moe_max_rows suffices). */
+moe_status moe_expert_ffn(const moe_config* cfg, const void* x_disp, const int32_t* expert_offset,
+                          const void* w1, const void* b1, const void* w2, const void* b2,
+                          void* a_save, void* h_disp, void* y_disp,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/* Backward of the expert FFNs for an upstream gradient dy_disp [rows, d]
+ * (chain rule of Linear-act-Linear, per expert e on its packed rows):
+ *   dh = dy·w2[e];  da = dh ⊙ act'(a_save)  (stored as dtype);
+ *   dx = da·w1[e];  dw2[e] = dy^T·h;  dw1[e] = da^T·x;
+ *   db2[e] = sum_rows dy;  db1[e] = sum_rows da   (fp32, nullable)
+ * Needs ffn_hidden > 0.  dx_disp device [rows, d] dtype; dw1 [E, h, d] and
+ * dw2 [E, d, h] dtype (fp32 accumulation; experts with no rows get zeros);
+ * db1 [E, h], db2 [E, d] fp32.  ws as above. */
+moe_status moe_expert_ffn_backward(const moe_config* cfg, const void* x_disp,
+                                   const int32_t* expert_offset, const void* w1, const void* w2,
+                                   const void* a_save, const void* h_disp, const void* dy_disp,
+                                   void* dx_disp, void* dw1, float* db1, void* dw2, float* db2,
+                                   void* ws, size_t ws_bytes, void* stream);
+
+/* Combine ([MoE-sched] §3.1 Step 5; [ds.moe] §3.1 step 4):
+ * out[t] = sum over j = 0..k-1 with slot[t,j] >= 0 of
+ *          weight[t,j] * y_disp[expert_offset[expert_idx[t,j]] + slot[t,j]],
+ * summed in fp32 in j order and stored as dtype; a token whose claims were
+ * all dropped gets a zero row.  out device [T, d]. */
+moe_status moe_combine(const moe_config* cfg, const void* y_disp, const int32_t* expert_idx,
+                       const int32_t* slot, const float* weight, const int32_t* expert_offset,
+                       void* out, void* stream);
+
+/* The whole layer forward on one stream with no host synchronisation:
+ * gate -> dispatch -> expert FFNs -> combine.  Returns ([ds.moe] §2.1) the
+ * output out [T, d] dtype, gate_loss [1] fp32 and expert_count [E] int32
+ * (all device).  logits_out, expert_idx, slot, weight are optional outputs
+ * (nullable, shapes as in moe_gate); when NULL the workspace holds them.
+ * x/w_router/b_router/logits_in as in moe_gate; w1/b1/w2/b2 as in
+ * moe_expert_ffn.  Intermediates stay in the workspace; see
+ * moe_workspace_views. */
+moe_status moe_layer_forward(const moe_config* cfg, const void* x, const void* w_router,
+                             const float* b_router, const float* logits_in,
+                             const void* w1, const void* b1, const void* w2, const void* b2,
+                             void* out, float* gate_loss, int32_t* expert_count,
+                             float* logits_out, int32_t* expert_idx, int32_t* slot,
+                             float* weight, void* ws, size_t ws_bytes, void* stream);
+
+/* Device addresses, inside a workspace ws, of the intermediates that
+ * moe_layer_forward leaves there (valid until the next call that uses ws):
+ * packed x_disp [rows, d], a_save [rows, h] (only with cfg->save_preact),
+ * h_disp [rows, h], y_disp [rows, d] and expert_offset [E+1] int32.  Any
+ * output pointer may be NULL.  Host only; computes addresses, reads nothing. */
+moe_status moe_workspace_views(const moe_config* cfg, void* ws, void** x_disp, void** a_save,
+                               void** h_disp, void** y_disp, int32_t** expert_offset);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,62 @@
+"""Top-k gated Mixture-of-Experts layer for one MI355X (gfx950) GPU.
+
+The compute is the HIP library libmoe_mi355x.so behind the C ABI in
+include/moe.h; ``binding`` exposes those calls with the same names and
+``MoE`` is a small holder of the layer's weights whose ``forward`` returns
+(output, gate_loss, expert_count) like the MoE layer of the deepspeed.moe
+overview page (§2.1).  torch is used for device memory and streams only.
+"""
+from __future__ import annotations
+
+from . import binding
+from .binding import (MOE_ACT_GELU, MOE_ACT_NONE, MOE_ACT_RELU, MOE_BF16, MOE_F32,  # noqa: F401
+                      MOE_LOSS_BALANCE, MOE_LOSS_USAGE_STD, MoeConfig, MoeError, make_config,
+                      moe_capacity, moe_combine, moe_dispatch, moe_expert_ffn, moe_expert_ffn_backward,
+                      moe_gate, moe_layer_forward, moe_max_rows, moe_workspace_size, moe_workspace_views)
+
+
+class MoE:
+    """Weights and workspace of one MoE layer; ``forward(x)`` runs the fused
+    layer on the current stream and returns (output, gate_loss, expert_count).
+
+    Arguments mirror MoE(hidden_size, num_experts, k, capacity_factor,
+    min_capacity, drop_tokens) of the deepspeed.moe overview (§2.1); the expert
+    is Linear(hidden, ffn_hidden) -> activation -> Linear(ffn_hidden, hidden),
+    or one Linear(hidden, hidden) when ffn_hidden == 0.  Weights use the
+    nn.Linear [out, in] layout, stacked over experts.
+    """
+
+    def __init__(self, hidden_size, num_experts, w_router, w1, b1=None, w2=None, b2=None, b_router=None,
+                 k=1, capacity_factor=1.0, min_capacity=4, drop_tokens=True, ffn_hidden=0,
+                 activation=MOE_ACT_NONE, normalize_topk=False, loss_kind=MOE_LOSS_BALANCE):
+        import torch
+        self.hidden_size, self.num_experts, self.k = hidden_size, num_experts, k
+        self.capacity_factor, self.min_capacity, self.drop_tokens = capacity_factor, min_capacity, drop_tokens
+        self.ffn_hidden, self.activation = ffn_hidden, activation
+        self.normalize_topk, self.loss_kind = normalize_topk, loss_kind
+        self.w_router, self.b_router = w_router, b_router
+        self.w1, self.b1, self.w2, self.b2 = w1, b1, w2, b2
+        self.dtype = MOE_BF16 if w1.dtype == torch.bfloat16 else MOE_F32
+        self._ws = None
+
+    def config(self, num_tokens):
+        return make_config(num_tokens, self.hidden_size, self.num_experts, self.k, self.capacity_factor,
+                           self.min_capacity, self.drop_tokens, self.ffn_hidden, self.activation, self.dtype,
+                           self.normalize_topk, self.loss_kind)
+
+    def forward(self, x, logits=None):
+        import torch
+        shape = x.shape
+        x2 = x.reshape(-1, self.hidden_size).contiguous()
+        cfg = self.config(x2.shape[0])
+        nbytes = moe_workspace_size(cfg)
+        if self._ws is None or self._ws.numel() < nbytes:
+            self._ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+        out = torch.empty_like(x2)
+        loss = torch.empty(1, dtype=torch.float32, device=x.device)
+        count = torch.empty(self.num_experts, dtype=torch.int32, device=x.device)
+        moe_layer_forward(cfg, x2, self.w_router, self.b_router, logits, self.w1, self.b1, self.w2, self.b2,
+                          out, loss, count, ws=self._ws)
+        return out.reshape(shape), loss[0], count
+
+    __call__ = forward

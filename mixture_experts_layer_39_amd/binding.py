@@ -1,0 +1,182 @@
+"""ctypes binding of libmoe_mi355x.so (include/moe.h).
+
+Argument marshalling only: every function here has the C name, turns torch
+tensors into device pointers and the current torch stream into a hipStream_t,
+calls the library and raises on a non-OK status.  All arithmetic runs in the
+HIP kernels.  If the library is missing, the first call raises ImportError:
+there is no other implementation to fall back to.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmoe_mi355x.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+MOE_F32, MOE_BF16 = 0, 1
+MOE_ACT_NONE, MOE_ACT_RELU, MOE_ACT_GELU = 0, 1, 2
+MOE_LOSS_BALANCE, MOE_LOSS_USAGE_STD = 0, 1
+MOE_MAX_EXPERTS = 256
+
+EXPORTED = ("moe_status_string", "moe_capacity", "moe_max_rows", "moe_workspace_size", "moe_gate",
+            "moe_dispatch", "moe_expert_ffn", "moe_expert_ffn_backward", "moe_combine",
+            "moe_layer_forward", "moe_workspace_views")
+
+
+class MoeConfig(ctypes.Structure):
+    _fields_ = [
+        ("num_tokens", ctypes.c_int64),
+        ("capacity_factor", ctypes.c_double),
+        ("hidden_size", ctypes.c_int32),
+        ("num_experts", ctypes.c_int32),
+        ("k", ctypes.c_int32),
+        ("min_capacity", ctypes.c_int32),
+        ("drop_tokens", ctypes.c_int32),
+        ("ffn_hidden", ctypes.c_int32),
+        ("activation", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("normalize_topk", ctypes.c_int32),
+        ("loss_kind", ctypes.c_int32),
+        ("save_preact", ctypes.c_int32),
+    ]
+
+
+def make_config(num_tokens, hidden_size, num_experts, k=1, capacity_factor=1.0, min_capacity=4,
+                drop_tokens=True, ffn_hidden=0, activation=MOE_ACT_NONE, dtype=MOE_BF16,
+                normalize_topk=False, loss_kind=MOE_LOSS_BALANCE, save_preact=False):
+    return MoeConfig(int(num_tokens), float(capacity_factor), int(hidden_size), int(num_experts), int(k),
+                     int(min_capacity), int(bool(drop_tokens)), int(ffn_hidden), int(activation), int(dtype),
+                     int(bool(normalize_topk)), int(loss_kind), int(bool(save_preact)))
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(msg)
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library (loaded once)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run `python -m mixture_experts_layer_39_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, S, I64P = ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(ctypes.c_int64)
+        CFG = ctypes.POINTER(MoeConfig)
+        L.moe_status_string.restype = ctypes.c_char_p
+        L.moe_status_string.argtypes = [ctypes.c_int]
+        for name in ("moe_capacity", "moe_max_rows"):
+            getattr(L, name).argtypes = [CFG, I64P]
+        L.moe_workspace_size.argtypes = [CFG, ctypes.POINTER(ctypes.c_size_t)]
+        L.moe_gate.argtypes = [CFG] + [P] * 11 + [P, S, P]
+        L.moe_dispatch.argtypes = [CFG] + [P] * 5 + [P]
+        L.moe_expert_ffn.argtypes = [CFG] + [P] * 9 + [P, S, P]
+        L.moe_expert_ffn_backward.argtypes = [CFG] + [P] * 12 + [P, S, P]
+        L.moe_combine.argtypes = [CFG] + [P] * 6 + [P]
+        L.moe_layer_forward.argtypes = [CFG] + [P] * 15 + [P, S, P]
+        L.moe_workspace_views.argtypes = [CFG, P] + [ctypes.POINTER(P)] * 5
+        for name in EXPORTED:
+            if name != "moe_status_string":
+                getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_string(st):
+    return lib().moe_status_string(int(st)).decode()
+
+
+def _check(st):
+    if st != MOE_OK:
+        raise MoeError(st, status_string(st))
+
+
+def _ptr(t):
+    """Device (or host) address of a tensor, None -> NULL."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the MoE library must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+# ---------------------------------------------------------------- host-only calls
+def moe_capacity(cfg):
+    c = ctypes.c_int64()
+    _check(lib().moe_capacity(ctypes.byref(cfg), ctypes.byref(c)))
+    return c.value
+
+
+def moe_max_rows(cfg):
+    c = ctypes.c_int64()
+    _check(lib().moe_max_rows(ctypes.byref(cfg), ctypes.byref(c)))
+    return c.value
+
+
+def moe_workspace_size(cfg):
+    c = ctypes.c_size_t()
+    _check(lib().moe_workspace_size(ctypes.byref(cfg), ctypes.byref(c)))
+    return c.value
+
+
+def moe_workspace_views(cfg, ws):
+    outs = [ctypes.c_void_p() for _ in range(5)]
+    _check(lib().moe_workspace_views(ctypes.byref(cfg), _ptr(ws), *[ctypes.byref(o) for o in outs]))
+    return tuple(o.value for o in outs)
+
+
+# ---------------------------------------------------------------- device calls
+def moe_gate(cfg, x, w_router, b_router, logits_in, logits_out, expert_idx, slot, weight, expert_count,
+             expert_offset, gate_loss, ws, stream=None):
+    _check(lib().moe_gate(ctypes.byref(cfg), _ptr(x), _ptr(w_router), _ptr(b_router), _ptr(logits_in),
+                          _ptr(logits_out), _ptr(expert_idx), _ptr(slot), _ptr(weight), _ptr(expert_count),
+                          _ptr(expert_offset), _ptr(gate_loss), _ptr(ws), ws.numel() * ws.element_size(),
+                          _stream(stream)))
+
+
+def moe_dispatch(cfg, x, expert_idx, slot, expert_offset, x_disp, stream=None):
+    _check(lib().moe_dispatch(ctypes.byref(cfg), _ptr(x), _ptr(expert_idx), _ptr(slot), _ptr(expert_offset),
+                              _ptr(x_disp), _stream(stream)))
+
+
+def moe_expert_ffn(cfg, x_disp, expert_offset, w1, b1, w2, b2, a_save, h_disp, y_disp, ws=None, stream=None):
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().moe_expert_ffn(ctypes.byref(cfg), _ptr(x_disp), _ptr(expert_offset), _ptr(w1), _ptr(b1),
+                                _ptr(w2), _ptr(b2), _ptr(a_save), _ptr(h_disp), _ptr(y_disp), _ptr(ws), nbytes,
+                                _stream(stream)))
+
+
+def moe_expert_ffn_backward(cfg, x_disp, expert_offset, w1, w2, a_save, h_disp, dy_disp, dx_disp, dw1, db1, dw2,
+                            db2, ws, stream=None):
+    _check(lib().moe_expert_ffn_backward(ctypes.byref(cfg), _ptr(x_disp), _ptr(expert_offset), _ptr(w1),
+                                         _ptr(w2), _ptr(a_save), _ptr(h_disp), _ptr(dy_disp), _ptr(dx_disp),
+                                         _ptr(dw1), _ptr(db1), _ptr(dw2), _ptr(db2), _ptr(ws),
+                                         ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_combine(cfg, y_disp, expert_idx, slot, weight, expert_offset, out, stream=None):
+    _check(lib().moe_combine(ctypes.byref(cfg), _ptr(y_disp), _ptr(expert_idx), _ptr(slot), _ptr(weight),
+                             _ptr(expert_offset), _ptr(out), _stream(stream)))
+
+
+def moe_layer_forward(cfg, x, w_router, b_router, logits_in, w1, b1, w2, b2, out, gate_loss, expert_count,
+                      logits_out=None, expert_idx=None, slot=None, weight=None, ws=None, stream=None):
+    _check(lib().moe_layer_forward(ctypes.byref(cfg), _ptr(x), _ptr(w_router), _ptr(b_router), _ptr(logits_in),
+                                   _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2), _ptr(out), _ptr(gate_loss),
+                                   _ptr(expert_count), _ptr(logits_out), _ptr(expert_idx), _ptr(slot),
+                                   _ptr(weight), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))

@@ -1,0 +1,105 @@
+// Internal declarations shared by the HIP kernels and the C-ABI host layer.
+// Not installed; the public interface is include/moe.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#define MOE_MAX_EXPERTS_DEV 256
+
+namespace moe {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+enum { DT_F32 = 0, DT_BF16 = 1 };
+enum { ACT_NONE = 0, ACT_RELU = 1, ACT_GELU = 2 };
+enum { LOSS_BALANCE = 0, LOSS_USAGE_STD = 1 };
+
+// ---------------------------------------------------------------- gate
+// Tokens per gate tile: 64 (4 groups of 16) while the padded expert count is
+// at most 128, else 32, so the cross-wave logit reduction fits in LDS.
+inline int gate_tile_tokens(int E) { return E <= 128 ? 64 : 32; }
+// Tiles per group of the two-level (tile -> group -> all) loss reduction.
+constexpr int kGateGroupTiles = 32;
+
+struct GateArgs {
+  const void* x;            // [T, d] dtype (router GEMM modes)
+  const void* w_router;     // [E, d] dtype
+  const float* b_router;    // [E] or null
+  const float* logits_in;   // [T, E] or null
+  float* logits_out;        // [T, E] or null
+  int32_t* expert_idx;      // [T, k]
+  int32_t* slot;            // [T, k]: raw per-(choice, expert) rank on exit
+  float* weight;            // [T, k]
+  int32_t* expert_count;    // [E]
+  int32_t* expert_offset;   // [E+1]
+  float* gate_loss;         // [1]
+  uint32_t* counters;       // [2 + groups]: ticket, groups done, per-group tiles done
+  uint32_t* status;         // [tiles, k*E] look-back words
+  float* me_tile;           // [tiles, E] per-tile sums of the softmax probabilities
+  float* me_group;          // [groups, E]
+  int32_t* demand;          // [k, E] total claims per (choice, expert)
+  int64_t T;
+  int64_t C;                // capacity, < 0 = none
+  int32_t d, E, k;
+  int32_t normalize, loss_kind;
+  int32_t num_tiles, num_groups;
+};
+
+// Words of (counters + status) that must be zero before the gate kernel.
+size_t gate_sync_words(int64_t T, int E, int k);
+
+hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t s);
+hipError_t launch_gate(const GateArgs& a, int dtype, hipStream_t s);
+hipError_t launch_slot_finalize(const int32_t* expert_idx, int32_t* slot, const int32_t* demand,
+                                int64_t T, int k, int E, int64_t C, hipStream_t s);
+hipError_t launch_gate_empty(int32_t* expert_count, int32_t* expert_offset, float* gate_loss,
+                             int E, hipStream_t s);
+
+// ---------------------------------------------------------------- dispatch / combine
+hipError_t launch_dispatch(const void* x, const int32_t* expert_idx, const int32_t* slot,
+                           const int32_t* expert_offset, void* x_disp, int64_t T, int k,
+                           int row_bytes, hipStream_t s);
+hipError_t launch_combine(const void* y_disp, const int32_t* expert_idx, const int32_t* slot,
+                          const float* weight, const int32_t* expert_offset, void* out,
+                          int64_t T, int k, int d, int dtype, hipStream_t s);
+
+// ---------------------------------------------------------------- expert GEMMs
+// Y[rows of e] = act(X[rows of e] · W[e]^T + bias[e]) on the packed layout.
+struct GemmArgs {
+  const void* X;             // [rows, K]
+  const void* W;             // [E, N, K]
+  const void* bias;          // [E, N] or null
+  void* Y;                   // [rows, N]
+  void* Apre;                // [rows, N] pre-activation, or null
+  const int32_t* offset;     // [E+1]
+  int64_t max_rows;          // upper bound on offset[E] (sizes the grid)
+  int32_t E, N, K, act;
+};
+hipError_t launch_grouped_gemm(const GemmArgs& a, int dtype, hipStream_t s);
+
+// Backward pieces (see gemm_bwd.hip).
+struct GemmBwdArgs {
+  const void* X;         // [rows, d]   x_disp
+  const void* W1;        // [E, h, d]
+  const void* W2;        // [E, d, h]
+  const void* A;         // [rows, h]   saved pre-activation
+  const void* H;         // [rows, h]
+  const void* dY;        // [rows, d]
+  void* dA;              // [rows, h]   workspace
+  void* dX;              // [rows, d]
+  void* dW1;             // [E, h, d]
+  void* dW2;             // [E, d, h]
+  float* db1;            // [E, h] or null
+  float* db2;            // [E, d] or null
+  const int32_t* offset; // [E+1]
+  int64_t max_rows;
+  int32_t E, d, h, act;
+};
+hipError_t launch_ffn_backward(const GemmBwdArgs& a, int dtype, hipStream_t s);
+
+}  // namespace moe

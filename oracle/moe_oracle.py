@@ -267,37 +267,55 @@ def expert_ffn(x_disp, offset, w1, b1, w2, b2, act, dtype):
     Linear-act-Linear, or one Linear when ``w2`` is None as in [ds.moe] §2.1's
     nn.Linear(512, 512) expert).
 
-    Returns (a, h, y): pre-activation, activation output (both stored as
-    ``dtype``), expert output stored as ``dtype``.  For a single Linear the
-    activation is applied to its output and a == h's input, y == h.
+    Weights are read per expert (``w1[e]`` is [out, in]), so any indexable
+    stack works.  Returns (a, h, y): pre-activation and activation output
+    (both stored as ``dtype``) and the expert output stored as ``dtype``.
+    For a single Linear, y == h.
     """
     x_disp = np.asarray(x_disp, np.float64)
     n = x_disp.shape[0]
     E = len(offset) - 1
-    hid = np.asarray(w1).shape[1]
+    hid = np.asarray(w1[0]).shape[0]
+    d_out = hid if w2 is None else np.asarray(w2[0]).shape[0]
     a_all = np.zeros((n, hid))
     h_all = np.zeros((n, hid))
-    d_out = hid if w2 is None else np.asarray(w2).shape[1]
     y_all = np.zeros((n, d_out))
     for e in range(E):
         r0, r1 = int(offset[e]), int(offset[e + 1])
         if r1 == r0:
             continue
-        X = x_disp[r0:r1]
-        a = X @ np.asarray(w1[e], np.float64).T
-        if b1 is not None:
-            a = a + np.asarray(b1[e], np.float64)
-        h = store(activation(a, act), dtype)
-        a_all[r0:r1] = store(a, dtype)
-        h_all[r0:r1] = h
-        if w2 is None:
-            y_all[r0:r1] = h
-        else:
-            y = h @ np.asarray(w2[e], np.float64).T
-            if b2 is not None:
-                y = y + np.asarray(b2[e], np.float64)
-            y_all[r0:r1] = store(y, dtype)
+        a, h, y = _ffn_rows(x_disp[r0:r1], e, w1, b1, w2, b2, act, dtype)
+        a_all[r0:r1], h_all[r0:r1], y_all[r0:r1] = a, h, y
     return a_all, h_all, y_all
+
+
+def _ffn_rows(X, e, w1, b1, w2, b2, act, dtype):
+    """One expert's FFN on rows X: (a, h, y) with the storage roundings."""
+    a = X @ np.asarray(w1[e], np.float64).T
+    if b1 is not None:
+        a = a + np.asarray(b1[e], np.float64)
+    h = store(activation(a, act), dtype)
+    if w2 is None:
+        return store(a, dtype), h, h
+    y = h @ np.asarray(w2[e], np.float64).T
+    if b2 is not None:
+        y = y + np.asarray(b2[e], np.float64)
+    return store(a, dtype), h, store(y, dtype)
+
+
+def token_forward(x_t, experts, weights, w1, b1, w2, b2, act, dtype):
+    """Layer output of one token given its kept (expert, weight) pairs in
+    choice order: sum_j w_j * FFN_{e_j}(x_t), rounded once to ``dtype``
+    ([DS-MoE-traps] ch.1 weighted sum, written per token)."""
+    x_t = np.asarray(x_t, np.float64)[None, :]
+    out = None
+    for e, w in zip(experts, weights):
+        _, _, y = _ffn_rows(x_t, int(e), w1, b1, w2, b2, act, dtype)
+        out = w * y[0] if out is None else out + w * y[0]
+    if out is None:
+        d_out = x_t.shape[1] if w2 is None else np.asarray(w2[0]).shape[0]
+        out = np.zeros(d_out)
+    return store(out, dtype)
 
 
 def combine(y_disp, idx, slot, weight, offset, num_tokens, dtype):
@@ -334,27 +352,11 @@ def direct_forward(x, logits, w1, b1, w2, b2, *, k, act, dtype, normalize_topk=F
     """No-capacity layer written per token, as in [DS-MoE-traps] ch.1's
     moe_forward: out[t] = sum_j w[t,j] * FFN_{e_j}(x[t]).  Used as a second
     formulation of the forward when nothing is dropped."""
-    x = np.asarray(x, np.float64)
     p = softmax(logits)
     idx = top_k(logits, k)
     w = gate_weights(p, idx, normalize_topk)
-    out = np.zeros((x.shape[0], x.shape[1] if w2 is None else np.asarray(w2).shape[1]))
-    for t in range(x.shape[0]):
-        for j in range(k):
-            e = idx[t, j]
-            a = x[t] @ np.asarray(w1[e], np.float64).T
-            if b1 is not None:
-                a = a + np.asarray(b1[e], np.float64)
-            h = store(activation(a, act), dtype)
-            if w2 is None:
-                y = h
-            else:
-                y = h @ np.asarray(w2[e], np.float64).T
-                if b2 is not None:
-                    y = y + np.asarray(b2[e], np.float64)
-                y = store(y, dtype)
-            out[t] += w[t, j] * y
-    return store(out, dtype)
+    return np.stack([token_forward(x[t], idx[t], w[t], w1, b1, w2, b2, act, dtype)
+                     for t in range(np.asarray(x).shape[0])])
 
 
 # --------------------------------------------------------------------------
@@ -371,14 +373,12 @@ def expert_ffn_backward(x_disp, offset, w1, w2, a_save, h, dy, act, dtype):
     x_disp = np.asarray(x_disp, np.float64)
     dy = np.asarray(dy, np.float64)
     E = len(offset) - 1
-    w1 = np.asarray(w1)
-    w2 = np.asarray(w2)
-    hid, d = w1.shape[1], w1.shape[2]
+    hid, d = np.asarray(w1[0]).shape
     dx = np.zeros_like(x_disp)
     dw1 = np.zeros((E, hid, d))
-    dw2 = np.zeros((E, w2.shape[1], hid))
+    dw2 = np.zeros((E, d, hid))
     db1 = np.zeros((E, hid))
-    db2 = np.zeros((E, w2.shape[1]))
+    db2 = np.zeros((E, d))
     for e in range(E):
         r0, r1 = int(offset[e]), int(offset[e + 1])
         if r1 == r0:

@@ -1,0 +1,95 @@
+"""Helpers for the GPU parity tests: run the HIP library through the C ABI
+(binding) on seeded synthetic inputs and bring results back as NumPy."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from mixture_experts_layer_39_amd import binding as B
+
+DT = {"bf16": B.MOE_BF16, "f32": B.MOE_F32}
+
+
+def cfg_of(sp, T=None, **kw):
+    c = dict(num_tokens=sp["T"] if T is None else T, hidden_size=sp["d"], num_experts=sp["E"], k=sp["k"],
+             capacity_factor=sp["cf"], min_capacity=sp["min_cap"], drop_tokens=sp["drop"], ffn_hidden=sp["h"],
+             activation=sp["act"], dtype=DT[sp["dtype"]])
+    c.update(kw)
+    return B.make_config(**c)
+
+
+def f64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def i64(t):
+    return t.detach().cpu().numpy().astype(np.int64)
+
+
+class Experts:
+    """Per-expert float32 host copies of a stacked device weight, made on
+    first use (so full-size checks convert only the experts they touch)."""
+
+    def __init__(self, w):
+        self.w = w
+        self.cache = {}
+
+    def __getitem__(self, e):
+        e = int(e)
+        if e not in self.cache:
+            self.cache[e] = self.w[e].float().cpu().numpy()
+        return self.cache[e]
+
+    def __len__(self):
+        return self.w.shape[0]
+
+
+def experts(w):
+    return None if w is None else Experts(w)
+
+
+def alloc_gate(cfg, dev):
+    T, E, k = cfg.num_tokens, cfg.num_experts, cfg.k
+    return dict(logits=torch.empty(T, E, dtype=torch.float32, device=dev),
+                idx=torch.full((T, k), -7, dtype=torch.int32, device=dev),
+                slot=torch.full((T, k), -7, dtype=torch.int32, device=dev),
+                weight=torch.full((T, k), -7.0, dtype=torch.float32, device=dev),
+                count=torch.full((E,), -7, dtype=torch.int32, device=dev),
+                offset=torch.full((E + 1,), -7, dtype=torch.int32, device=dev),
+                loss=torch.full((1,), -7.0, dtype=torch.float32, device=dev))
+
+
+def workspace(cfg, dev):
+    return torch.empty(max(B.moe_workspace_size(cfg), 1), dtype=torch.uint8, device=dev)
+
+
+def run_gate(cfg, inp, dev, ws=None, logits_in=None):
+    g = alloc_gate(cfg, dev)
+    ws = workspace(cfg, dev) if ws is None else ws
+    B.moe_gate(cfg, inp.get("x"), inp.get("w_router"), inp.get("b_router"), logits_in, g["logits"], g["idx"],
+               g["slot"], g["weight"], g["count"], g["offset"], g["loss"], ws)
+    return g
+
+
+def gate_np(g):
+    return dict(logits=f64(g["logits"]), idx=i64(g["idx"]), slot=i64(g["slot"]), weight=f64(g["weight"]),
+                count=i64(g["count"]), offset=i64(g["offset"]), loss=float(g["loss"][0].item()))
+
+
+def close(got, want, rtol):
+    """Elementwise |g - o| <= rtol*|o| + rtol*rms(o): relative error with a
+    floor at the tensor's rms so near-zero entries are not over-weighted."""
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    assert got.shape == want.shape, (got.shape, want.shape)
+    if want.size == 0:
+        return
+    rms = float(np.sqrt(np.mean(want * want)))
+    bound = rtol * np.abs(want) + rtol * rms
+    err = np.abs(got - want)
+    bad = err > bound
+    if bad.any():
+        i = np.unravel_index(np.argmax(err - bound), err.shape)
+        raise AssertionError(f"{int(bad.sum())}/{bad.size} outside tolerance; worst at {i}: got {got[i]!r} "
+                             f"want {want[i]!r} (rtol {rtol}, rms {rms:.3g}); normwise "
+                             f"{np.linalg.norm(got - want) / max(np.linalg.norm(want), 1e-300):.3g}")
