@@ -54,6 +54,32 @@ __device__ __forceinline__ float act_apply(float v, int act) {
   return v;
 }
 
+// GELU(x) = x * Phi(x) with erf from Abramowitz & Stegun, Handbook of
+// Mathematical Functions, formula 7.1.26: for z >= 0,
+//   erf(z) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-z^2),
+//   t = 1 / (1 + p z),  |error| <= 1.5e-7,
+// extended to z < 0 by oddness.  Branch-free: one reciprocal, one exp.
+__device__ __forceinline__ float gelu_fast(float x) {
+  const float z = fabsf(x) * 0.7071067811865476f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.f));
+  float poly = fmaf(1.061405429f, t, -1.453152027f);
+  poly = fmaf(poly, t, 1.421413741f);
+  poly = fmaf(poly, t, -0.284496736f);
+  poly = fmaf(poly, t, 0.254829592f);
+  poly *= t;
+  const float e = __builtin_amdgcn_exp2f(-z * z * 1.4426950408889634f);
+  const float erf_abs = fmaf(-poly, e, 1.f);
+  const float erf_v = __builtin_copysignf(erf_abs, x);
+  return 0.5f * x * (1.f + erf_v);
+}
+
+template <int ACT>
+__device__ __forceinline__ float act_fixed(float v) {
+  if constexpr (ACT == ACT_RELU) return fmaxf(v, 0.f);
+  else if constexpr (ACT == ACT_GELU) return gelu_fast(v);
+  else return v;
+}
+
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   const bf16 l = static_cast<bf16>(lo);
   const bf16 h = static_cast<bf16>(hi);
@@ -267,6 +293,265 @@ __global__ __launch_bounds__(WT * WF * 64) void gemm_bf16_kernel(GemmArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Large-tile bf16 kernel (K a multiple of 64): 256 tokens x 256 features per
+// workgroup, 4 waves each owning 128 x 128 of it (16 MFMA 32x32x16 tiles, 256
+// accumulators per lane), one workgroup per CU.
+//  * Operands go from global memory straight into LDS (buffer_load ... lds),
+//    no register staging.  Each instruction moves 8 rows x 128 bytes; the
+//    16-byte chunk c of row r lands in slot c ^ (r & 7), so the fragment
+//    reads of 8 consecutive rows hit 8 different bank groups.  Rows past the
+//    expert's last token or past N lie outside the buffer's range and read as
+//    zero.
+//  * Double-buffered 64-wide K steps: the next step's loads are issued right
+//    after the barrier and land while the current step's 64 MFMAs run.
+//  * An expert's rows are split into ceil(M/256) tiles of equal size rounded
+//    up to 32; the two token-side waves take alternate 32-row blocks and skip
+//    blocks past the tile's rows, so a short tile costs proportionally less.
+namespace big {
+constexpr int BT = 256, BF = 256, BKB = 128;  // BKB: bytes of one row's K step
+constexpr int TILE_BYTES = 256 * BKB;          // one operand tile
+constexpr int STAGE = 2 * TILE_BYTES;          // X tile + W tile
+constexpr int LDS = 2 * STAGE;                 // double buffered
+}  // namespace big
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+
+struct BigTile {
+  const GemmArgs& a;
+  unsigned char* smem;
+  int nk, wt, wf, h, r32, e, row0, mbase, mvalid, n0;
+};
+
+// Read one accumulator element out of its AGPR at the point of use.  Without
+// this the compiler copies all 256 accumulators into VGPRs when the K loop
+// ends and spills part of them to scratch.
+__device__ __forceinline__ float agpr_read(float v) {
+  float r;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(r) : "a"(v));
+  return r;
+}
+
+// The accumulator block blk = ff*4 + tt, read out of its AGPRs (constant
+// indices inside each case; blocks with tt >= NB do not exist).
+template <int NB>
+__device__ __forceinline__ void acc_block(const f32x16 (&acc)[4][4], int blk, float (&v)[16]) {
+  switch (blk) {
+#define MOE_AB(FF, TT)                                              \
+  case FF * 4 + TT:                                                 \
+    if constexpr (TT < NB) {                                        \
+      _Pragma("unroll") for (int r = 0; r < 16; ++r) v[r] = agpr_read(acc[FF][TT][r]); \
+    }                                                               \
+    break;
+    MOE_AB(0, 0) MOE_AB(0, 1) MOE_AB(0, 2) MOE_AB(0, 3)
+    MOE_AB(1, 0) MOE_AB(1, 1) MOE_AB(1, 2) MOE_AB(1, 3)
+    MOE_AB(2, 0) MOE_AB(2, 1) MOE_AB(2, 2) MOE_AB(2, 3)
+    MOE_AB(3, 0) MOE_AB(3, 1) MOE_AB(3, 2) MOE_AB(3, 3)
+#undef MOE_AB
+    default: break;
+  }
+}
+
+// Epilogue of one 32x32 accumulator: this lane's 16 consecutive features f0..
+// of token row rloc (tile-relative): + bias (from LDS), optional
+// pre-activation store, activation, bf16 store (two 16-byte vectors).
+template <int ACT>
+__device__ __forceinline__ void big_store(float (&v)[16], const BigTile& t, int rloc, int fl, const float* s_bias) {
+  const GemmArgs& a = t.a;
+  const int N = a.N;
+  const int f0 = t.n0 + fl;
+  const int64_t grow = (int64_t)t.row0 + t.mbase + rloc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) v[r] += s_bias[fl + r];
+  if (a.Apre) {
+    uint4* p = reinterpret_cast<uint4*>(static_cast<bf16*>(a.Apre) + grow * N + f0);
+    p[0] = make_uint4(pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7]));
+    p[1] = make_uint4(pack2(v[8], v[9]), pack2(v[10], v[11]), pack2(v[12], v[13]), pack2(v[14], v[15]));
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) v[r] = act_fixed<ACT>(v[r]);
+  uint4* p = reinterpret_cast<uint4*>(static_cast<bf16*>(a.Y) + grow * N + f0);
+  p[0] = make_uint4(pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7]));
+  p[1] = make_uint4(pack2(v[8], v[9]), pack2(v[10], v[11]), pack2(v[12], v[13]), pack2(v[14], v[15]));
+}
+
+// One wave's share of a tile with NB valid 32-row token blocks (NB in 0..4):
+// every wave runs the same K steps and barriers; MFMAs of absent blocks are
+// not issued at all.  Accumulators live only inside this function.
+template <int NB, int ACT, typename Issue>
+__device__ __forceinline__ void big_tile(const BigTile& t, Issue& issue, const float* s_bias) {
+  using namespace big;
+  const GemmArgs& a = t.a;
+  unsigned char* smem = t.smem;
+  const int nk = t.nk, wt = t.wt, wf = t.wf, h = t.h, r32 = t.r32, mvalid = t.mvalid, n0 = t.n0;
+  const int N = a.N;
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  // fragment reads of sub-step i (chunk h*4+i of each 128-byte row, slot
+  // chunk ^ (row & 7)); two register sets so that sub-step i+1 is read while
+  // sub-step i's MFMAs run
+  bf16x8 fa[2][4], fb[2][NB > 0 ? NB : 1];
+  auto frag = [&](const unsigned char* Xs, const unsigned char* Ws, int i, bf16x8 (&A)[4],
+                  bf16x8 (&Bx)[NB > 0 ? NB : 1]) {
+    const int sw = (((h * 4 + i) ^ (r32 & 7)) * 16);
+#pragma unroll
+    for (int ff = 0; ff < 4; ++ff)
+      A[ff] = *reinterpret_cast<const bf16x8*>(Ws + (wf * 128 + ff * 32 + r32) * BKB + sw);
+#pragma unroll
+    for (int tt = 0; tt < NB; ++tt)
+      Bx[tt] = *reinterpret_cast<const bf16x8*>(Xs + ((wt + 2 * tt) * 32 + r32) * BKB + sw);
+  };
+  auto mfmas = [&](int c) {
+#pragma unroll
+    for (int tt = 0; tt < NB; ++tt)
+#pragma unroll
+      for (int ff = 0; ff < 4; ++ff)
+        acc[ff][tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[c][ff], fb[c][tt], acc[ff][tt], 0, 0, 0);
+  };
+  // Stage s holds K step s (mod 2).  Sub-step i of a step uses fragment set
+  // i & 1; the reads for sub-step i+1 are issued as one block ahead of sub-step
+  // i's MFMAs.  The one barrier per step sits before sub-step 3: by then every
+  // wave has read all of the current stage (so the loads two steps ahead may
+  // overwrite it) and the next stage has landed (so its first fragments can
+  // be read while sub-step 3 computes).
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_s_barrier();
+  if (nk > 1) issue(1, 64);
+  frag(smem, smem + TILE_BYTES, 0, fa[0], fb[0]);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    const unsigned char* Xs = smem + cur * STAGE;
+    const unsigned char* Ws = Xs + TILE_BYTES;
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      frag(Xs, Ws, i + 1, fa[(i + 1) & 1], fb[(i + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(i & 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (kt + 1 < nk) {
+      __builtin_amdgcn_s_waitcnt(0);  // own loads of the next stage and own reads of this one
+      __builtin_amdgcn_s_barrier();
+      if (kt + 2 < nk) issue(cur, (kt + 2) * 64);
+      const unsigned char* Xn = smem + (cur ^ 1) * STAGE;
+      frag(Xn, Xn + TILE_BYTES, 0, fa[0], fb[0]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    mfmas(1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // one compact loop over the accumulator blocks keeps the epilogue small
+  // enough to stay in the instruction cache
+#pragma nounroll
+  for (int blk = 0; blk < 16; ++blk) {
+    const int ff = blk >> 2, tt = blk & 3;
+    const int rloc = (wt + 2 * tt) * 32 + r32;
+    const int fl = wf * 128 + ff * 32 + h * 16;   // feature offset within the tile
+    if (tt >= NB || n0 + fl >= N) continue;
+    float v[16];
+    acc_block<NB>(acc, blk, v);
+    if (rloc < mvalid) big_store<ACT>(v, t, rloc, fl, s_bias);
+  }
+}
+
+template <int ACT>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void gemm_bf16_big_kernel(GemmArgs a) {
+  using namespace big;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __shared__ int s_pref[MOE_MAX_EXPERTS_DEV + 1];
+  __shared__ float s_bias[BF];
+
+  const int E = a.E, N = a.N, K = a.K;
+  const int ntf = (N + BF - 1) / BF;
+  tile_prefix<BT>(a.offset, E, s_pref);
+  __syncthreads();
+  const int total = s_pref[E] * ntf;
+  const int share = (total + kXcds - 1) / kXcds;
+  const int loc = blockIdx.x / kXcds;
+  const int tile = (blockIdx.x % kXcds) * share + loc;
+  if (loc >= share || tile >= total) return;
+  const TileCoord tc = tile_coord(tile, s_pref, E, ntf);
+
+  // the wave index is uniform across the wave; say so, so that descriptor
+  // and LDS-base choices below stay in scalar registers
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wt = wave >> 1, wf = wave & 1;
+  const int row0 = a.offset[tc.e];
+  const int mrows = a.offset[tc.e + 1] - row0;
+  const int nmt = s_pref[tc.e + 1] - s_pref[tc.e];
+  const int per = (((mrows + nmt - 1) / nmt) + 31) & ~31;   // rows per tile, balanced
+  const int mbase = tc.mt * per;
+  const int mvalid = min(per, mrows - mbase);
+  const int nvb = (mvalid + 31) >> 5;                        // valid 32-row blocks
+  const int n0 = tc.nf * BF;
+
+  const bf16* Xp = static_cast<const bf16*>(a.X) + (int64_t)(row0 + mbase) * K;
+  const bf16* Wp = static_cast<const bf16*>(a.W) + ((int64_t)tc.e * N + n0) * K;
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(Xp, (uint32_t)mvalid * K * 2);
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(Wp, (uint32_t)min(BF, N - n0) * K * 2);
+
+  // this lane's source row / chunk for each of its 16 load instructions:
+  // waves 0-1 fill the X tile, waves 2-3 the W tile (weight rows permuted so
+  // the MFMA row m = lane&31 reads feature ((m>>2)&1)*16 + (m>>3)*4 + (m&3))
+  const bool loads_w = wave >= 2;
+  const int lrow = lane >> 3;                 // row within the 8-row group
+  const int chunk = (lane & 7) ^ lrow;        // logical chunk held by this slot
+  // Load i of this wave covers tile rows (wave&1)*128 + i*8 .. +7.  For X the
+  // source row is that row; for W it is the permuted feature, which works out
+  // to a per-lane part ((lrow>>2)&1)*16 + (lrow&3) plus a wave-uniform part
+  // (i>>2)*32 + (i&3)*4, so each load needs one VGPR offset and one SGPR offset.
+  const uint32_t row_bytes = (uint32_t)K * 2;
+  const uint32_t vbase = (uint32_t)(loads_w ? (((lrow >> 2) & 1) * 16 + (lrow & 3)) : lrow) * row_bytes + chunk * 16;
+  const uint32_t sbase = (uint32_t)(wave & 1) * 128 * row_bytes;
+  const __amdgpu_buffer_rsrc_t lr = loads_w ? wr : xr;
+  const int lds_op = loads_w ? TILE_BYTES : 0;
+
+  auto issue = [&](int stage, int k0) {
+    unsigned char* base = smem + stage * STAGE + lds_op + (wave & 1) * 128 * BKB;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t g = loads_w ? (uint32_t)((i >> 2) * 32 + (i & 3) * 4) : (uint32_t)(i * 8);
+      // the row part goes in the per-lane offset, which the buffer range check
+      // always covers (rows past the end read as zero); only the position
+      // along K, which stays inside a valid row, goes in the scalar offset
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(lr, (__attribute__((address_space(3))) void*)(base + i * 8 * BKB), 16,
+                                               vbase + sbase + g * row_bytes, (uint32_t)k0 * 2, 0, 0);
+    }
+  };
+
+  const int nk = K / 64;
+  const int h = lane >> 5, r32 = lane & 31;
+  // this wave's token blocks are wt, wt+2, wt+4, wt+6; the valid ones are a
+  // prefix of that list, fixed for the whole K loop
+  const int nbw = nvb > wt ? min(4, (nvb - wt + 1) >> 1) : 0;
+  BigTile t{a, smem, nk, wt, wf, h, r32, tc.e, row0, mbase, mvalid, n0};
+  issue(0, 0);
+  // this tile's bias in LDS (visible after the first barrier in big_tile)
+  {
+    const int f = n0 + tid;
+    s_bias[tid] = (a.bias && f < N) ? static_cast<float>(static_cast<const bf16*>(a.bias)[(int64_t)tc.e * N + f]) : 0.f;
+  }
+  switch (nbw) {
+    case 4: big_tile<4, ACT>(t, issue, s_bias); break;
+    case 3: big_tile<3, ACT>(t, issue, s_bias); break;
+    case 2: big_tile<2, ACT>(t, issue, s_bias); break;
+    case 1: big_tile<1, ACT>(t, issue, s_bias); break;
+    default: big_tile<0, ACT>(t, issue, s_bias); break;
+  }
+
+}
+
 // fp32: one thread per output element (used for the small fp32 layers).
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
   const int n = blockIdx.x * 64 + (threadIdx.x & 63);
@@ -306,10 +591,35 @@ hipError_t launch_bf16(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int ACT>
+hipError_t launch_bf16_big_t(const GemmArgs& a, hipStream_t s) {
+  auto kern = gemm_bf16_big_kernel<ACT>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, big::LDS);
+  if (e != hipSuccess) return e;
+  const int64_t max_mtiles = (a.max_rows + big::BT - 1) / big::BT + a.E;
+  const int64_t ntf = (a.N + big::BF - 1) / big::BF;
+  int64_t grid = max_mtiles * ntf;
+  grid = (grid + kXcds - 1) / kXcds * kXcds;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), big::LDS, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bf16_big(const GemmArgs& a, hipStream_t s) {
+  if (a.act == ACT_GELU) return launch_bf16_big_t<ACT_GELU>(a, s);
+  if (a.act == ACT_RELU) return launch_bf16_big_t<ACT_RELU>(a, s);
+  return launch_bf16_big_t<ACT_NONE>(a, s);
+}
+
 }  // namespace
 
 hipError_t launch_grouped_gemm(const GemmArgs& a, int dtype, hipStream_t s) {
   if (a.max_rows <= 0) return hipSuccess;
+  // the large-tile kernel needs whole 64-wide K steps, whole 16-feature
+  // output groups, and byte offsets of one operand tile below 2^31 (buffer
+  // offsets are 32-bit)
+  if (dtype == DT_BF16 && a.K % 64 == 0 && a.N % 16 == 0 && (int64_t)256 * a.K * 2 < (int64_t(1) << 31))
+    return launch_bf16_big(a, s);
   if (dtype == DT_BF16) return launch_bf16<128, 128, 2, 2>(a, s);
   dim3 grid((a.N + 63) / 64, (unsigned)((a.max_rows + 3) / 4));
   hipLaunchKernelGGL(gemm_f32_kernel, grid, dim3(256), 0, s, a);
