@@ -167,9 +167,10 @@ moe_status moe_expert_ffn(const moe_config* cfg, const void* x_disp, const int32
  *   dh = dy·w2[e];  da = dh ⊙ act'(a_save)  (stored as dtype);
  *   dx = da·w1[e];  dw2[e] = dy^T·h;  dw1[e] = da^T·x;
  *   db2[e] = sum_rows dy;  db1[e] = sum_rows da   (fp32, nullable)
- * Needs ffn_hidden > 0.  dx_disp device [rows, d] dtype; dw1 [E, h, d] and
- * dw2 [E, d, h] dtype (fp32 accumulation; experts with no rows get zeros);
- * db1 [E, h], db2 [E, d] fp32.  ws as above. */
+ * Needs ffn_hidden > 0; MOE_ERR_UNSUPPORTED unless dtype is MOE_BF16 and d
+ * and h are multiples of 16.  dx_disp device [rows, d] bf16; dw1 [E, h, d]
+ * and dw2 [E, d, h] bf16 (fp32 accumulation; experts with no rows get
+ * zeros); db1 [E, h], db2 [E, d] fp32.  ws as above (it also holds dA). */
 moe_status moe_expert_ffn_backward(const moe_config* cfg, const void* x_disp,
                                    const int32_t* expert_offset, const void* w1, const void* w2,
                                    const void* a_save, const void* h_disp, const void* dy_disp,

@@ -297,6 +297,8 @@ moe_status moe_expert_ffn_backward(const moe_config* cfg, const void* x_disp, co
   if (!x_disp || !expert_offset || !w1 || !w2 || !a_save || !h_disp || !dy_disp || !dx_disp || !dw1 || !dw2 ||
       !ws)
     return MOE_ERR_INVALID_ARG;
+  // the backward kernels are bf16 only and write 16-element row segments
+  if (cfg->dtype != MOE_BF16 || cfg->hidden_size % 16 || cfg->ffn_hidden % 16) return MOE_ERR_UNSUPPORTED;
   const Layout L = layout_of(cfg);
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   GemmBwdArgs b;

@@ -183,6 +183,11 @@ def test_device_entry_points_validate_before_launch():
                                      FAKE, 1 << 40, None) == B.MOE_ERR_INVALID_ARG
     ws2 = B.moe_workspace_size(cfg2)
     assert L.moe_expert_ffn_backward(c2, *([FAKE] * 12), FAKE, ws2 - 1, None) == B.MOE_ERR_WORKSPACE
+    # backward kernels: bf16 only, d and h multiples of 16
+    cfg3 = _cfg(hidden_size=24, ffn_hidden=32, activation=B.MOE_ACT_GELU)
+    assert L.moe_expert_ffn_backward(ctypes.byref(cfg3), *([FAKE] * 12), FAKE, 1 << 40, None) == B.MOE_ERR_UNSUPPORTED
+    cfg4 = _cfg(hidden_size=32, ffn_hidden=64, activation=B.MOE_ACT_GELU, dtype=B.MOE_F32)
+    assert L.moe_expert_ffn_backward(ctypes.byref(cfg4), *([FAKE] * 12), FAKE, 1 << 40, None) == B.MOE_ERR_UNSUPPORTED
     # fused forward
     assert L.moe_layer_forward(c, FAKE, FAKE, None, None, FAKE, None, None, None, FAKE, FAKE, None, None, None,
                                None, None, FAKE, ws_need, None) == B.MOE_ERR_INVALID_ARG
