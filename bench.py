@@ -75,14 +75,17 @@ def cpu_baseline(sp, inp, target_s=15.0):
     br = f(inp["b_router"])
     lg_given = f(inp["logits"])
     w1, b1, w2, b2 = f(inp["w1"]), f(inp["b1"]), f(inp["w2"]), f(inp["b2"])
+    dy = f(inp.get("dy"))
 
     def run(ts):
         t0 = time.perf_counter()
         logits = lg_given[:ts] if lg_given is not None else O.router_logits(x[:ts], wr, br)
-        O.layer_forward(x[:ts], logits, w1, b1, w2, b2, k=sp["k"], capacity_factor=sp["cf"],
-                        min_capacity=sp["min_cap"], drop_tokens=sp["drop"], act=sp["act"], dtype=sp["dtype"])
+        r = O.layer_forward(x[:ts], logits, w1, b1, w2, b2, k=sp["k"], capacity_factor=sp["cf"],
+                            min_capacity=sp["min_cap"], drop_tokens=sp["drop"], act=sp["act"], dtype=sp["dtype"])
         if sp.get("backward"):
-            pass
+            n = int(r["expert_offset"][-1])
+            O.expert_ffn_backward(r["x_disp"], r["expert_offset"], w1, w2, r["a"], r["h"], dy[:n], sp["act"],
+                                  sp["dtype"])
         return time.perf_counter() - t0
 
     ts = min(sp["T"], 64)
@@ -97,7 +100,8 @@ def cpu_baseline(sp, inp, target_s=15.0):
         cores = os.cpu_count() or 1
     return {"value": ts / el, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
             "sample": f"first {ts} of {sp['T']} tokens of {sp['name']} (capacity recomputed for {ts} tokens): "
-                      f"router, routing, dispatch, float64 expert FFNs, combine; {el:.1f} s"}
+                      f"router, routing, dispatch, float64 expert FFNs, combine"
+                      f"{', expert FFN backward' if sp.get('backward') else ''}; {el:.1f} s"}
 
 
 def main(argv=None):
@@ -107,7 +111,18 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="top2_e64")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 5 times (scales HBM byte counters)")
     a = ap.parse_args(argv)
+    if a.copy_calibration:
+        import torch
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read_per_launch": src.numel() * 4, "copy_bytes_written_per_launch": src.numel() * 4}))
+        return 0
     if a.gpus != 1:
         print(f"bench.py measures one GPU's share of the layer; --gpus {a.gpus} is not supported "
               f"(run with --gpus 1)", file=sys.stderr)
@@ -124,16 +139,31 @@ def main(argv=None):
     T, d, E, k, h = sp["T"], sp["d"], sp["E"], sp["k"], sp["h"]
     dt = B.MOE_BF16 if sp["dtype"] == "bf16" else B.MOE_F32
     esz = 2 if dt == B.MOE_BF16 else 4
-    cfg = B.make_config(T, d, E, k, sp["cf"], sp["min_cap"], sp["drop"], h, sp["act"], dt)
+    cfg = B.make_config(T, d, E, k, sp["cf"], sp["min_cap"], sp["drop"], h, sp["act"], dt,
+                        save_preact=bool(sp.get("backward")))
     ws = torch.empty(B.moe_workspace_size(cfg), dtype=torch.uint8, device=dev)
     out = torch.empty_like(inp["x"])
     loss = torch.empty(1, dtype=torch.float32, device=dev)
     count = torch.empty(E, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
 
+    bwd = bool(sp.get("backward"))
+    if bwd:
+        rows = B.moe_max_rows(cfg)
+        xd_p, a_p, h_p, _, off_p = B.moe_workspace_views(cfg, ws)
+        dx = torch.empty(rows, d, dtype=torch.bfloat16, device=dev)
+        dw1 = torch.empty_like(inp["w1"])
+        dw2 = torch.empty_like(inp["w2"])
+
+    def backward():
+        B.moe_expert_ffn_backward(cfg, xd_p, off_p, inp["w1"], inp["w2"], a_p, h_p, inp["dy"], dx, dw1, None, dw2,
+                                  None, ws, stream=stream)
+
     def step():
         B.moe_layer_forward(cfg, inp["x"], inp["w_router"], inp["b_router"], inp["logits"], inp["w1"], inp["b1"],
                             inp["w2"], inp["b2"], out, loss, count, ws=ws, stream=stream)
+        if bwd:
+            backward()
 
     for _ in range(a.warmup):
         step()
@@ -152,9 +182,9 @@ def main(argv=None):
     g = dict(idx=torch.empty(T, k, dtype=torch.int32, device=dev), slot=torch.empty(T, k, dtype=torch.int32, device=dev),
              weight=torch.empty(T, k, dtype=torch.float32, device=dev),
              offset=torch.empty(E + 1, dtype=torch.int32, device=dev))
-    xd, _, hd_p, yd_p, _ = B.moe_workspace_views(cfg, ws)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
-    acc = [0.0] * 4
+    xd, a_p, hd_p, yd_p, _ = B.moe_workspace_views(cfg, ws)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    acc = [0.0] * 5
     for it in range(a.warmup + a.steps):
         ev[0].record(stream)
         B.moe_gate(cfg, inp["x"], inp["w_router"], inp["b_router"], inp["logits"], None, g["idx"], g["slot"],
@@ -162,14 +192,18 @@ def main(argv=None):
         ev[1].record(stream)
         B.moe_dispatch(cfg, inp["x"], g["idx"], g["slot"], g["offset"], xd, stream=stream)
         ev[2].record(stream)
-        B.moe_expert_ffn(cfg, xd, g["offset"], inp["w1"], inp["b1"], inp["w2"], inp["b2"], None, hd_p, yd_p, ws,
-                         stream=stream)
+        B.moe_expert_ffn(cfg, xd, g["offset"], inp["w1"], inp["b1"], inp["w2"], inp["b2"], a_p if bwd else None,
+                         hd_p, yd_p, ws, stream=stream)
         ev[3].record(stream)
         B.moe_combine(cfg, yd_p, g["idx"], g["slot"], g["weight"], g["offset"], out, stream=stream)
         ev[4].record(stream)
+        if bwd:
+            B.moe_expert_ffn_backward(cfg, xd, g["offset"], inp["w1"], inp["w2"], a_p, hd_p, inp["dy"], dx, dw1,
+                                      None, dw2, None, ws, stream=stream)
+        ev[5].record(stream)
         if it >= a.warmup:
             torch.cuda.synchronize()
-            for i in range(4):
+            for i in range(5):
                 acc[i] += ev[i].elapsed_time(ev[i + 1])
     st_ms = [v / a.steps for v in acc]
 
@@ -197,9 +231,18 @@ def main(argv=None):
         "combine": {"ms": st_ms[3], "bytes": comb_bytes, "GB/s": gbs(comb_bytes, st_ms[3]),
                     "frac_hbm": gbs(comb_bytes, st_ms[3]) / PEAK_HBM_GBS},
     }
+    if bwd:
+        bflops = 2 * ffn_flops   # dgrad (dH, dX) + wgrad (dW2, dW1): 4 GEMMs of 2*N*d*h
+        stages["expert_ffn_backward"] = {"ms": st_ms[4], "flops": bflops,
+                                         "TFLOP/s": bflops / (st_ms[4] * 1e-3) / 1e12,
+                                         "frac_mfma": bflops / (st_ms[4] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                                         "launches": 4}
     gemm_ms = st_ms[2] / n_gemm
     achieved = (ffn_flops / n_gemm) / (gemm_ms * 1e-3) / 1e12
-    roofline = {"bound": "mfma", "kernel": "gemm_bf16_kernel" if dt == B.MOE_BF16 else "gemm_f32_kernel",
+    # the expert GEMM: one kernel template launched once per Linear (the GELU
+    # and the plain instantiation for a two-Linear expert), equal FLOPs each
+    roofline = {"bound": "mfma", "kernel": "gemm_bf16_big_kernel (expert FFN GEMM, per launch)" if dt == B.MOE_BF16
+                else "gemm_f32_kernel",
                 "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / PEAK_BF16_TFLOPS, "traffic": load_traffic(a.workload),
                 "flops_per_launch": ffn_flops / n_gemm, "avg_launch_ms": gemm_ms, "rows": N}
@@ -208,7 +251,8 @@ def main(argv=None):
             "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
             "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
             "dtype": sp["dtype"], "data": "synthetic",
-            "config": {"workload": describe(sp), "tokens_per_step": T, "rows_kept": N},
+            "config": {"workload": describe(sp) + (" + expert FFN backward" if bwd else ""),
+                       "tokens_per_step": T, "rows_kept": N},
             "roofline": roofline, "stages": stages}
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(sp, inp)
