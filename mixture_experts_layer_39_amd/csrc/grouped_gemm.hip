@@ -401,7 +401,7 @@ __device__ __forceinline__ void big_tile(const BigTile& t, Issue& issue, const f
   bf16x8 fa[2][4], fb[2][NB > 0 ? NB : 1];
   auto frag = [&](const unsigned char* Xs, const unsigned char* Ws, int i, bf16x8 (&A)[4],
                   bf16x8 (&Bx)[NB > 0 ? NB : 1]) {
-    const int sw = (((h * 4 + i) ^ (r32 & 7)) * 16);
+    const int sw = (((h * 4 + i) ^ ((r32 >> 1) & 7)) * 16);
 #pragma unroll
     for (int ff = 0; ff < 4; ++ff)
       A[ff] = *reinterpret_cast<const bf16x8*>(Ws + (wf * 128 + ff * 32 + r32) * BKB + sw);
@@ -506,13 +506,19 @@ void gemm_bf16_big_kernel(GemmArgs a) {
   // the MFMA row m = lane&31 reads feature ((m>>2)&1)*16 + (m>>3)*4 + (m&3))
   const bool loads_w = wave >= 2;
   const int lrow = lane >> 3;                 // row within the 8-row group
-  const int chunk = (lane & 7) ^ lrow;        // logical chunk held by this slot
+  // chunk c of tile row r sits in slot c ^ ((r >> 1) & 7): sixteen consecutive
+  // rows read at one chunk hit sixteen different 16-byte bank groups.  For
+  // load i the rows are 8i + lrow (+ a multiple of 16 per wave), so
+  // (r >> 1) & 7 = 4 * (i & 1) + (lrow >> 1): two lane patterns, even and odd i.
+  const int chunk_e = (lane & 7) ^ (lrow >> 1);
+  const int chunk_o = (lane & 7) ^ (4 + (lrow >> 1));
   // Load i of this wave covers tile rows (wave&1)*128 + i*8 .. +7.  For X the
   // source row is that row; for W it is the permuted feature, which works out
   // to a per-lane part ((lrow>>2)&1)*16 + (lrow&3) plus a wave-uniform part
   // (i>>2)*32 + (i&3)*4, so each load needs one VGPR offset and one SGPR offset.
   const uint32_t row_bytes = (uint32_t)K * 2;
-  const uint32_t vbase = (uint32_t)(loads_w ? (((lrow >> 2) & 1) * 16 + (lrow & 3)) : lrow) * row_bytes + chunk * 16;
+  const uint32_t vrow = (uint32_t)(loads_w ? (((lrow >> 2) & 1) * 16 + (lrow & 3)) : lrow) * row_bytes;
+  const uint32_t vbase_e = vrow + chunk_e * 16, vbase_o = vrow + chunk_o * 16;
   const uint32_t sbase = (uint32_t)(wave & 1) * 128 * row_bytes;
   const __amdgpu_buffer_rsrc_t lr = loads_w ? wr : xr;
   const int lds_op = loads_w ? TILE_BYTES : 0;
@@ -526,7 +532,8 @@ void gemm_bf16_big_kernel(GemmArgs a) {
       // always covers (rows past the end read as zero); only the position
       // along K, which stays inside a valid row, goes in the scalar offset
       __builtin_amdgcn_raw_ptr_buffer_load_lds(lr, (__attribute__((address_space(3))) void*)(base + i * 8 * BKB), 16,
-                                               vbase + sbase + g * row_bytes, (uint32_t)k0 * 2, 0, 0);
+                                               ((i & 1) ? vbase_o : vbase_e) + sbase + g * row_bytes,
+                                               (uint32_t)k0 * 2, 0, 0);
     }
   };
 
