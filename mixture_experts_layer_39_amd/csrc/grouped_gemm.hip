@@ -32,6 +32,9 @@
 // The fp32 path (small problems only) is a plain FMA kernel.
 #include <math.h>
 
+#include <algorithm>
+#include <utility>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -295,16 +298,21 @@ __global__ __launch_bounds__(WT * WF * 64) void gemm_bf16_kernel(GemmArgs a) {
 
 // ---------------------------------------------------------------------------
 // Large-tile bf16 kernel (K a multiple of 64): 256 tokens x 256 features per
-// workgroup, 4 waves each owning 128 x 128 of it (16 MFMA 32x32x16 tiles, 256
-// accumulators per lane), one workgroup per CU.
+// tile, 4 waves each owning 128 x 128 of it (16 MFMA 32x32x16 tiles, 256
+// accumulators per lane), one persistent workgroup per CU.
 //  * Operands go from global memory straight into LDS (buffer_load ... lds),
 //    no register staging.  Each instruction moves 8 rows x 128 bytes; the
-//    16-byte chunk c of row r lands in slot c ^ (r & 7), so the fragment
-//    reads of 8 consecutive rows hit 8 different bank groups.  Rows past the
-//    expert's last token or past N lie outside the buffer's range and read as
-//    zero.
-//  * Double-buffered 64-wide K steps: the next step's loads are issued right
-//    after the barrier and land while the current step's 64 MFMAs run.
+//    16-byte chunk c of row r lands in slot c ^ ((r >> 1) & 7), so the
+//    fragment reads of 16 consecutive rows hit 16 different bank groups.
+//    Rows past the expert's last token or past N lie outside the buffer's
+//    range and read as zero.
+//  * Double-buffered 64-wide K steps: the loads of step s+2 are issued right
+//    after the barrier of step s and land while step s+1's MFMAs run.
+//  * Persistent: the grid is one workgroup per CU; each workgroup walks a
+//    strided run of tiles inside its XCD's contiguous share, so the tiles
+//    running together on one XCD share operands in its L2.  The first K step
+//    of the next tile is loaded while the current tile finishes its last step
+//    and its epilogue, and the tile prefix is computed once per workgroup.
 //  * An expert's rows are split into ceil(M/256) tiles of equal size rounded
 //    up to 32; the two token-side waves take alternate 32-row blocks and skip
 //    blocks past the tile's rows, so a short tile costs proportionally less.
@@ -319,12 +327,82 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-
+// One output tile as this wave sees it.
 struct BigTile {
-  const GemmArgs& a;
-  unsigned char* smem;
-  int nk, wt, wf, h, r32, e, row0, mbase, mvalid, n0;
+  int row0, mbase, mvalid, n0, e;
+  int nbw;                        // this wave's valid 32-row token blocks (0..4)
+  __amdgpu_buffer_rsrc_t lr;      // the operand rows this wave loads (X or W)
 };
+
+// Per-workgroup constants of the big kernel.
+struct BigCtx {
+  unsigned char* smem;
+  int nk, wt, wf, h, r32, wave, lds_op;
+  uint32_t vbase_e, vbase_o, sbase, row_bytes;
+};
+
+__device__ __forceinline__ BigTile big_tile_desc(const GemmArgs& a, const BigCtx& c, int tile, const int* s_pref,
+                                                 int ntf) {
+  using namespace big;
+  const TileCoord tc = tile_coord(tile, s_pref, a.E, ntf);
+  BigTile t;
+  t.e = tc.e;
+  t.row0 = a.offset[tc.e];
+  const int mrows = a.offset[tc.e + 1] - t.row0;
+  const int nmt = s_pref[tc.e + 1] - s_pref[tc.e];
+  const int per = (((mrows + nmt - 1) / nmt) + 31) & ~31;   // rows per tile, balanced
+  t.mbase = tc.mt * per;
+  t.mvalid = min(per, mrows - t.mbase);
+  t.n0 = tc.nf * BF;
+  const int nvb = (t.mvalid + 31) >> 5;                      // valid 32-row blocks
+  // this wave's token blocks are wt, wt+2, wt+4, wt+6; the valid ones are a
+  // prefix of that list
+  t.nbw = nvb > c.wt ? min(4, (nvb - c.wt + 1) >> 1) : 0;
+  if (c.wave >= 2) {
+    const bf16* Wp = static_cast<const bf16*>(a.W) + ((int64_t)tc.e * a.N + t.n0) * a.K;
+    t.lr = make_rsrc(Wp, (uint32_t)min(BF, a.N - t.n0) * c.row_bytes);
+  } else {
+    const bf16* Xp = static_cast<const bf16*>(a.X) + (int64_t)(t.row0 + t.mbase) * a.K;
+    t.lr = make_rsrc(Xp, (uint32_t)t.mvalid * c.row_bytes);
+  }
+  return t;
+}
+
+// The DMA loads of one 64-wide K step (at element k0) of this wave's operand
+// rows into a stage: 16 instructions of 8 rows x 128 bytes.  Waves 0-1 fill
+// the X tile, waves 2-3 the W tile (weight rows permuted so the MFMA row
+// m = lane&31 reads feature ((m>>2)&1)*16 + (m>>3)*4 + (m&3)).
+__device__ __forceinline__ void big_issue(const BigCtx& c, __amdgpu_buffer_rsrc_t lr, int stage, int k0) {
+  using namespace big;
+  unsigned char* base = c.smem + stage * STAGE + c.lds_op + (c.wave & 1) * 128 * BKB;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t g = c.wave >= 2 ? (uint32_t)((i >> 2) * 32 + (i & 3) * 4) : (uint32_t)(i * 8);
+    // the row part goes in the per-lane offset, which the buffer range check
+    // always covers (rows past the end read as zero); only the position
+    // along K, which stays inside a valid row, goes in the scalar offset
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(lr, (__attribute__((address_space(3))) void*)(base + i * 8 * BKB), 16,
+                                             ((i & 1) ? c.vbase_o : c.vbase_e) + c.sbase + g * c.row_bytes,
+                                             (uint32_t)k0 * 2, 0, 0);
+  }
+}
+
+// Load number i (0..15) of big_issue alone.
+__device__ __forceinline__ void big_issue_one(const BigCtx& c, __amdgpu_buffer_rsrc_t lr, int stage, int k0, int i) {
+  using namespace big;
+  unsigned char* base = c.smem + stage * STAGE + c.lds_op + (c.wave & 1) * 128 * BKB;
+  const uint32_t g = c.wave >= 2 ? (uint32_t)((i >> 2) * 32 + (i & 3) * 4) : (uint32_t)(i * 8);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(lr, (__attribute__((address_space(3))) void*)(base + i * 8 * BKB), 16,
+                                           ((i & 1) ? c.vbase_o : c.vbase_e) + c.sbase + g * c.row_bytes,
+                                           (uint32_t)k0 * 2, 0, 0);
+}
+
+// This tile's bias (zero without one) into LDS for the epilogue.
+__device__ __forceinline__ void big_bias(const GemmArgs& a, const BigTile& t, float* s_bias) {
+  const int f = t.n0 + threadIdx.x;
+  s_bias[threadIdx.x] =
+      (a.bias && f < a.N) ? static_cast<float>(static_cast<const bf16*>(a.bias)[(int64_t)t.e * a.N + f]) : 0.f;
+}
 
 // Read one accumulator element out of its AGPR at the point of use.  Without
 // this the compiler copies all 256 accumulators into VGPRs when the K loop
@@ -359,8 +437,8 @@ __device__ __forceinline__ void acc_block(const f32x16 (&acc)[4][4], int blk, fl
 // of token row rloc (tile-relative): + bias (from LDS), optional
 // pre-activation store, activation, bf16 store (two 16-byte vectors).
 template <int ACT>
-__device__ __forceinline__ void big_store(float (&v)[16], const BigTile& t, int rloc, int fl, const float* s_bias) {
-  const GemmArgs& a = t.a;
+__device__ __forceinline__ void big_store(const GemmArgs& a, float (&v)[16], const BigTile& t, int rloc, int fl,
+                                          const float* s_bias) {
   const int N = a.N;
   const int f0 = t.n0 + fl;
   const int64_t grow = (int64_t)t.row0 + t.mbase + rloc;
@@ -380,13 +458,17 @@ __device__ __forceinline__ void big_store(float (&v)[16], const BigTile& t, int 
 
 // One wave's share of a tile with NB valid 32-row token blocks (NB in 0..4):
 // every wave runs the same K steps and barriers; MFMAs of absent blocks are
-// not issued at all.  Accumulators live only inside this function.
-template <int NB, int ACT, typename Issue>
-__device__ __forceinline__ void big_tile(const BigTile& t, Issue& issue, const float* s_bias) {
+// not issued at all.  Accumulators live only inside this function.  K step s
+// of this tile sits in stage (s + sb) & 1; its step 0 was issued before the
+// call.  If there is a next tile, its step 0 is issued into the stage this
+// tile's step nk-2 used (the other stage when nk == 1), which is stage 0 of
+// the next tile's numbering with sb' = (sb + nk) & 1.
+template <int NB, int ACT>
+__device__ __forceinline__ void big_tile(const GemmArgs& a, const BigCtx& c, const BigTile& t, int sb, bool has_next,
+                                         __amdgpu_buffer_rsrc_t next_lr, const float* s_bias) {
   using namespace big;
-  const GemmArgs& a = t.a;
-  unsigned char* smem = t.smem;
-  const int nk = t.nk, wt = t.wt, wf = t.wf, h = t.h, r32 = t.r32, mvalid = t.mvalid, n0 = t.n0;
+  unsigned char* smem = c.smem;
+  const int nk = c.nk, wt = c.wt, wf = c.wf, h = c.h, r32 = c.r32;
   const int N = a.N;
   f32x16 acc[4][4];
 #pragma unroll
@@ -395,58 +477,97 @@ __device__ __forceinline__ void big_tile(const BigTile& t, Issue& issue, const f
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  // fragment reads of sub-step i (chunk h*4+i of each 128-byte row, slot
-  // chunk ^ (row & 7)); two register sets so that sub-step i+1 is read while
-  // sub-step i's MFMAs run
+  // Fragment registers: two sets, so that sub-step i+1's fragments are read
+  // while sub-step i's MFMAs run (sub-step i uses set i & 1).  Sub-step i of
+  // a 64-wide K step reads chunk h*4+i of each 128-byte row (slot chunk ^
+  // ((row >> 1) & 7)).
   bf16x8 fa[2][4], fb[2][NB > 0 ? NB : 1];
-  auto frag = [&](const unsigned char* Xs, const unsigned char* Ws, int i, bf16x8 (&A)[4],
-                  bf16x8 (&Bx)[NB > 0 ? NB : 1]) {
+  constexpr int NM = 4 * NB;       // MFMAs per sub-step
+  constexpr int NR = 4 + NB;       // fragment reads per sub-step
+  // fragment read r of sub-step i from a stage into a set, in the order the
+  // MFMAs consume them: token block 0, the four weight blocks, then the other
+  // token blocks
+  auto read1 = [&](int stage, int i, int set, int r) {
+    const unsigned char* Xs = smem + stage * STAGE;
+    const unsigned char* Ws = Xs + TILE_BYTES;
     const int sw = (((h * 4 + i) ^ ((r32 >> 1) & 7)) * 16);
-#pragma unroll
-    for (int ff = 0; ff < 4; ++ff)
-      A[ff] = *reinterpret_cast<const bf16x8*>(Ws + (wf * 128 + ff * 32 + r32) * BKB + sw);
-#pragma unroll
-    for (int tt = 0; tt < NB; ++tt)
-      Bx[tt] = *reinterpret_cast<const bf16x8*>(Xs + ((wt + 2 * tt) * 32 + r32) * BKB + sw);
+    if (NB > 0 && r == 0) {
+      fb[set][0] = *reinterpret_cast<const bf16x8*>(Xs + (wt * 32 + r32) * BKB + sw);
+    } else {
+      const int q = NB > 0 ? r - 1 : r;   // 0..3: weight block, 4..: token block q - 3
+      if (q < 4)
+        fa[set][q] = *reinterpret_cast<const bf16x8*>(Ws + (wf * 128 + q * 32 + r32) * BKB + sw);
+      else
+        fb[set][q - 3] = *reinterpret_cast<const bf16x8*>(Xs + ((wt + 2 * (q - 3)) * 32 + r32) * BKB + sw);
+    }
   };
-  auto mfmas = [&](int c) {
-#pragma unroll
-    for (int tt = 0; tt < NB; ++tt)
-#pragma unroll
-      for (int ff = 0; ff < 4; ++ff)
-        acc[ff][tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[c][ff], fb[c][tt], acc[ff][tt], 0, 0, 0);
+  // MFMA j of a sub-step: token block j / 4 with weight block j % 4
+  auto mfma1 = [&](int set, int j) {
+    const int tt = j >> 2, ff = j & 3;
+    acc[ff][tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][ff], fb[set][tt], acc[ff][tt], 0, 0, 0);
   };
-  // Stage s holds K step s (mod 2).  Sub-step i of a step uses fragment set
-  // i & 1; the reads for sub-step i+1 are issued as one block ahead of sub-step
-  // i's MFMAs.  The one barrier per step sits before sub-step 3: by then every
-  // wave has read all of the current stage (so the loads two steps ahead may
-  // overwrite it) and the next stage has landed (so its first fragments can
-  // be read while sub-step 3 computes).
+  // One sub-step in a fixed issue order: each MFMA is followed by its share
+  // of the next sub-step's fragment reads (one after each of the first NR
+  // MFMAs) and, when loading, of the 16 global->LDS loads, so that the memory
+  // instructions issue in the shadow of the MFMAs instead of in a bubble.
+  auto substep = [&](auto loads, int mset, int rstage, int ri, int rset, __amdgpu_buffer_rsrc_t llr, int lstage,
+                     int lk0) {
+    constexpr bool LOADS = decltype(loads)::value;
+    constexpr int NJ = NM > NR ? NM : NR;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      if (j < NM) mfma1(mset, j);
+      if constexpr (LOADS) {
+        if constexpr (NM > 0) {
+#pragma unroll
+          for (int q = j * 16 / NM; q < (j + 1) * 16 / NM && j < NM; ++q) big_issue_one(c, llr, lstage, lk0, q);
+        } else {
+          if (j == 0) {
+#pragma unroll
+            for (int q = 0; q < 16; ++q) big_issue_one(c, llr, lstage, lk0, q);
+          }
+        }
+      }
+      if (j < NR && ri >= 0) read1(rstage, ri, rset, j);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  using NoLoads = std::integral_constant<bool, false>;
+  using Loads = std::integral_constant<bool, true>;
+  const __amdgpu_buffer_rsrc_t no_lr = make_rsrc(a.X, 0);
+  // Stage s holds K step s (mod 2, offset by sb).  The one barrier per step
+  // sits before sub-step 3: by then every wave has read all of the current
+  // stage (so the loads two steps ahead may overwrite it) and the next stage
+  // has landed (so its first fragments can be read while sub-step 3
+  // computes).  The last step is peeled off so that in the loop sub-step 3's
+  // operands are known to have arrived at the barrier's wait.  What sub-step
+  // 3 of step kt loads into the stage it has just finished: step kt+2 of this
+  // tile, else step 0 of the next tile, else nothing (a descriptor with no
+  // records: the loads return zeros and touch no memory).
+  const __amdgpu_buffer_rsrc_t tail_lr = has_next ? next_lr : no_lr;
   __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_s_barrier();
-  if (nk > 1) issue(1, 64);
-  frag(smem, smem + TILE_BYTES, 0, fa[0], fb[0]);
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const unsigned char* Xs = smem + cur * STAGE;
-    const unsigned char* Ws = Xs + TILE_BYTES;
+  if (nk > 1) big_issue(c, t.lr, (sb + 1) & 1, 64);
+  else big_issue(c, tail_lr, (sb + 1) & 1, 0);
 #pragma unroll
-    for (int i = 0; i < 3; ++i) {
-      frag(Xs, Ws, i + 1, fa[(i + 1) & 1], fb[(i + 1) & 1]);
-      __builtin_amdgcn_sched_barrier(0);
-      mfmas(i & 1);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if (kt + 1 < nk) {
-      __builtin_amdgcn_s_waitcnt(0);  // own loads of the next stage and own reads of this one
-      __builtin_amdgcn_s_barrier();
-      if (kt + 2 < nk) issue(cur, (kt + 2) * 64);
-      const unsigned char* Xn = smem + (cur ^ 1) * STAGE;
-      frag(Xn, Xn + TILE_BYTES, 0, fa[0], fb[0]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    mfmas(1);
-    __builtin_amdgcn_sched_barrier(0);
+  for (int r = 0; r < NR; ++r) read1(sb, 0, 0, r);
+  __builtin_amdgcn_sched_barrier(0);
+  for (int kt = 0; kt + 1 < nk; ++kt) {
+    const int cur = (kt + sb) & 1;
+    substep(NoLoads{}, 0, cur, 1, 1, no_lr, 0, 0);
+    substep(NoLoads{}, 1, cur, 2, 0, no_lr, 0, 0);
+    substep(NoLoads{}, 0, cur, 3, 1, no_lr, 0, 0);
+    __builtin_amdgcn_s_waitcnt(0);  // own loads of the next stage and own reads of this one
+    __builtin_amdgcn_s_barrier();
+    const bool more = kt + 2 < nk;
+    substep(Loads{}, 1, cur ^ 1, 0, 0, more ? t.lr : tail_lr, cur, more ? (kt + 2) * 64 : 0);
+  }
+  {
+    const int cur = (nk - 1 + sb) & 1;
+    substep(NoLoads{}, 0, cur, 1, 1, no_lr, 0, 0);
+    substep(NoLoads{}, 1, cur, 2, 0, no_lr, 0, 0);
+    substep(NoLoads{}, 0, cur, 3, 1, no_lr, 0, 0);
+    substep(NoLoads{}, 1, cur, -1, 0, no_lr, 0, 0);
   }
 
   // one compact loop over the accumulator blocks keeps the epilogue small
@@ -456,10 +577,10 @@ __device__ __forceinline__ void big_tile(const BigTile& t, Issue& issue, const f
     const int ff = blk >> 2, tt = blk & 3;
     const int rloc = (wt + 2 * tt) * 32 + r32;
     const int fl = wf * 128 + ff * 32 + h * 16;   // feature offset within the tile
-    if (tt >= NB || n0 + fl >= N) continue;
+    if (tt >= NB || t.n0 + fl >= N) continue;
     float v[16];
     acc_block<NB>(acc, blk, v);
-    if (rloc < mvalid) big_store<ACT>(v, t, rloc, fl, s_bias);
+    if (rloc < t.mvalid) big_store<ACT>(a, v, t, rloc, fl, s_bias);
   }
 }
 
@@ -469,94 +590,77 @@ void gemm_bf16_big_kernel(GemmArgs a) {
   using namespace big;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __shared__ int s_pref[MOE_MAX_EXPERTS_DEV + 1];
-  __shared__ float s_bias[BF];
+  __shared__ float s_bias[2][BF];   // alternate tiles use alternate halves
 
   const int E = a.E, N = a.N, K = a.K;
   const int ntf = (N + BF - 1) / BF;
   tile_prefix<BT>(a.offset, E, s_pref);
   __syncthreads();
   const int total = s_pref[E] * ntf;
+  // this XCD's contiguous share of the tiles, walked with stride L by its L
+  // workgroups (XCDs take workgroups round-robin)
+  const int per_xcd = gridDim.x / kXcds;
   const int share = (total + kXcds - 1) / kXcds;
-  const int loc = blockIdx.x / kXcds;
-  const int tile = (blockIdx.x % kXcds) * share + loc;
-  if (loc >= share || tile >= total) return;
-  const TileCoord tc = tile_coord(tile, s_pref, E, ntf);
+  const int xcd = blockIdx.x % kXcds;
+  const int t_end = min(total, (xcd + 1) * share);
+  int tile = xcd * share + (int)blockIdx.x / kXcds;
+  if (tile >= t_end) return;
 
   // the wave index is uniform across the wave; say so, so that descriptor
   // and LDS-base choices below stay in scalar registers
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wt = wave >> 1, wf = wave & 1;
-  const int row0 = a.offset[tc.e];
-  const int mrows = a.offset[tc.e + 1] - row0;
-  const int nmt = s_pref[tc.e + 1] - s_pref[tc.e];
-  const int per = (((mrows + nmt - 1) / nmt) + 31) & ~31;   // rows per tile, balanced
-  const int mbase = tc.mt * per;
-  const int mvalid = min(per, mrows - mbase);
-  const int nvb = (mvalid + 31) >> 5;                        // valid 32-row blocks
-  const int n0 = tc.nf * BF;
-
-  const bf16* Xp = static_cast<const bf16*>(a.X) + (int64_t)(row0 + mbase) * K;
-  const bf16* Wp = static_cast<const bf16*>(a.W) + ((int64_t)tc.e * N + n0) * K;
-  const __amdgpu_buffer_rsrc_t xr = make_rsrc(Xp, (uint32_t)mvalid * K * 2);
-  const __amdgpu_buffer_rsrc_t wr = make_rsrc(Wp, (uint32_t)min(BF, N - n0) * K * 2);
-
-  // this lane's source row / chunk for each of its 16 load instructions:
-  // waves 0-1 fill the X tile, waves 2-3 the W tile (weight rows permuted so
-  // the MFMA row m = lane&31 reads feature ((m>>2)&1)*16 + (m>>3)*4 + (m&3))
-  const bool loads_w = wave >= 2;
-  const int lrow = lane >> 3;                 // row within the 8-row group
-  // chunk c of tile row r sits in slot c ^ ((r >> 1) & 7): sixteen consecutive
-  // rows read at one chunk hit sixteen different 16-byte bank groups.  For
-  // load i the rows are 8i + lrow (+ a multiple of 16 per wave), so
-  // (r >> 1) & 7 = 4 * (i & 1) + (lrow >> 1): two lane patterns, even and odd i.
+  BigCtx c;
+  c.smem = smem;
+  c.nk = K / 64;
+  c.wt = wave >> 1;
+  c.wf = wave & 1;
+  c.h = lane >> 5;
+  c.r32 = lane & 31;
+  c.wave = wave;
+  c.lds_op = wave >= 2 ? TILE_BYTES : 0;
+  c.row_bytes = (uint32_t)K * 2;
+  // this lane's source row / chunk for each of its 16 load instructions.
+  // Chunk c of tile row r sits in slot c ^ ((r >> 1) & 7): sixteen
+  // consecutive rows read at one chunk hit sixteen different 16-byte bank
+  // groups.  For load i the rows are 8i + lrow (+ a multiple of 16 per wave),
+  // so (r >> 1) & 7 = 4 * (i & 1) + (lrow >> 1): two lane patterns, even and
+  // odd i.  Load i of this wave covers tile rows (wave&1)*128 + i*8 .. +7.
+  // For X the source row is that row; for W it is the permuted feature, which
+  // works out to a per-lane part ((lrow>>2)&1)*16 + (lrow&3) plus a
+  // wave-uniform part (i>>2)*32 + (i&3)*4, so each load needs one VGPR offset
+  // and one SGPR offset.
+  const int lrow = lane >> 3;
   const int chunk_e = (lane & 7) ^ (lrow >> 1);
   const int chunk_o = (lane & 7) ^ (4 + (lrow >> 1));
-  // Load i of this wave covers tile rows (wave&1)*128 + i*8 .. +7.  For X the
-  // source row is that row; for W it is the permuted feature, which works out
-  // to a per-lane part ((lrow>>2)&1)*16 + (lrow&3) plus a wave-uniform part
-  // (i>>2)*32 + (i&3)*4, so each load needs one VGPR offset and one SGPR offset.
-  const uint32_t row_bytes = (uint32_t)K * 2;
-  const uint32_t vrow = (uint32_t)(loads_w ? (((lrow >> 2) & 1) * 16 + (lrow & 3)) : lrow) * row_bytes;
-  const uint32_t vbase_e = vrow + chunk_e * 16, vbase_o = vrow + chunk_o * 16;
-  const uint32_t sbase = (uint32_t)(wave & 1) * 128 * row_bytes;
-  const __amdgpu_buffer_rsrc_t lr = loads_w ? wr : xr;
-  const int lds_op = loads_w ? TILE_BYTES : 0;
+  const uint32_t vrow = (uint32_t)(wave >= 2 ? (((lrow >> 2) & 1) * 16 + (lrow & 3)) : lrow) * c.row_bytes;
+  c.vbase_e = vrow + chunk_e * 16;
+  c.vbase_o = vrow + chunk_o * 16;
+  c.sbase = (uint32_t)(wave & 1) * 128 * c.row_bytes;
 
-  auto issue = [&](int stage, int k0) {
-    unsigned char* base = smem + stage * STAGE + lds_op + (wave & 1) * 128 * BKB;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const uint32_t g = loads_w ? (uint32_t)((i >> 2) * 32 + (i & 3) * 4) : (uint32_t)(i * 8);
-      // the row part goes in the per-lane offset, which the buffer range check
-      // always covers (rows past the end read as zero); only the position
-      // along K, which stays inside a valid row, goes in the scalar offset
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(lr, (__attribute__((address_space(3))) void*)(base + i * 8 * BKB), 16,
-                                               ((i & 1) ? vbase_o : vbase_e) + sbase + g * row_bytes,
-                                               (uint32_t)k0 * 2, 0, 0);
+  BigTile cur = big_tile_desc(a, c, tile, s_pref, ntf);
+  big_issue(c, cur.lr, 0, 0);
+  big_bias(a, cur, s_bias[0]);
+  int sb = 0, par = 0;
+  for (;;) {
+    const int next = tile + per_xcd;
+    const bool has_next = next < t_end;
+    BigTile nt = cur;
+    if (has_next) nt = big_tile_desc(a, c, next, s_pref, ntf);
+    switch (cur.nbw) {
+      case 4: big_tile<4, ACT>(a, c, cur, sb, has_next, nt.lr, s_bias[par]); break;
+      case 3: big_tile<3, ACT>(a, c, cur, sb, has_next, nt.lr, s_bias[par]); break;
+      case 2: big_tile<2, ACT>(a, c, cur, sb, has_next, nt.lr, s_bias[par]); break;
+      case 1: big_tile<1, ACT>(a, c, cur, sb, has_next, nt.lr, s_bias[par]); break;
+      default: big_tile<0, ACT>(a, c, cur, sb, has_next, nt.lr, s_bias[par]); break;
     }
-  };
-
-  const int nk = K / 64;
-  const int h = lane >> 5, r32 = lane & 31;
-  // this wave's token blocks are wt, wt+2, wt+4, wt+6; the valid ones are a
-  // prefix of that list, fixed for the whole K loop
-  const int nbw = nvb > wt ? min(4, (nvb - wt + 1) >> 1) : 0;
-  BigTile t{a, smem, nk, wt, wf, h, r32, tc.e, row0, mbase, mvalid, n0};
-  issue(0, 0);
-  // this tile's bias in LDS (visible after the first barrier in big_tile)
-  {
-    const int f = n0 + tid;
-    s_bias[tid] = (a.bias && f < N) ? static_cast<float>(static_cast<const bf16*>(a.bias)[(int64_t)tc.e * N + f]) : 0.f;
+    if (!has_next) break;
+    sb = (sb + c.nk) & 1;
+    par ^= 1;
+    big_bias(a, nt, s_bias[par]);   // visible after the next tile's first barrier
+    cur = nt;
+    tile = next;
   }
-  switch (nbw) {
-    case 4: big_tile<4, ACT>(t, issue, s_bias); break;
-    case 3: big_tile<3, ACT>(t, issue, s_bias); break;
-    case 2: big_tile<2, ACT>(t, issue, s_bias); break;
-    case 1: big_tile<1, ACT>(t, issue, s_bias); break;
-    default: big_tile<0, ACT>(t, issue, s_bias); break;
-  }
-
 }
 
 // fp32: one thread per output element (used for the small fp32 layers).
@@ -598,16 +702,31 @@ hipError_t launch_bf16(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Number of compute units of the current device (the persistent grid).
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 template <int ACT>
 hipError_t launch_bf16_big_t(const GemmArgs& a, hipStream_t s) {
   auto kern = gemm_bf16_big_kernel<ACT>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, big::LDS);
   if (e != hipSuccess) return e;
+  // at most one workgroup per CU (LDS use allows no more), never more than
+  // the worst-case tile count, a whole number per XCD
   const int64_t max_mtiles = (a.max_rows + big::BT - 1) / big::BT + a.E;
   const int64_t ntf = (a.N + big::BF - 1) / big::BF;
-  int64_t grid = max_mtiles * ntf;
-  grid = (grid + kXcds - 1) / kXcds * kXcds;
+  int64_t grid = std::min<int64_t>(max_mtiles * ntf, device_cus());
+  grid = std::max<int64_t>(kXcds, grid / kXcds * kXcds);
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), big::LDS, s, a);
   return hipGetLastError();
 }
