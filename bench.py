@@ -88,10 +88,15 @@ def cpu_baseline(sp, inp, target_s=15.0):
                                   sp["dtype"])
         return time.perf_counter() - t0
 
+    # grow the sample until it takes a good part of the target time (a small
+    # sample's time is mostly per-expert overhead, so one extrapolation from
+    # it undershoots)
     ts = min(sp["T"], 64)
     el = run(ts)
-    if el < target_s / 4 and ts < sp["T"]:
-        ts = int(min(sp["T"], max(ts + 1, ts * target_s / max(el, 1e-3))))
+    for _ in range(4):
+        if el >= target_s / 2 or ts >= sp["T"]:
+            break
+        ts = int(min(sp["T"], max(2 * ts, ts * target_s / max(el, 1e-3))))
         el = run(ts)
     try:
         from threadpoolctl import threadpool_info

@@ -27,12 +27,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 
-// Round-to-nearest-even fp32 -> bf16 pair packed into one word.
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  const bf16 l = static_cast<bf16>(lo);
-  const bf16 h = static_cast<bf16>(hi);
-  return (uint32_t)__builtin_bit_cast(uint16_t, l) | ((uint32_t)__builtin_bit_cast(uint16_t, h) << 16);
-}
 
 __global__ __launch_bounds__(256) void dispatch_kernel(const u32x4* __restrict__ x,
                                                        const int32_t* __restrict__ expert_idx,

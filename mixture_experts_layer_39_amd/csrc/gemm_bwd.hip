@@ -58,11 +58,7 @@ __device__ __forceinline__ int lds_row_of_feature(int f) {
   return ((f >> 2) & 3) * 8 + (f >> 4) * 4 + (f & 3);
 }
 
-__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-  const bf16 l = static_cast<bf16>(lo);
-  const bf16 h = static_cast<bf16>(hi);
-  return (uint32_t)__builtin_bit_cast(uint16_t, l) | ((uint32_t)__builtin_bit_cast(uint16_t, h) << 16);
-}
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) { return pack_bf16x2(lo, hi); }
 
 // erf by Abramowitz & Stegun 7.1.26 (|error| <= 1.5e-7), odd extension.
 __device__ __forceinline__ float erf_as(float z) {

@@ -83,11 +83,7 @@ __device__ __forceinline__ float act_fixed(float v) {
   else return v;
 }
 
-__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-  const bf16 l = static_cast<bf16>(lo);
-  const bf16 h = static_cast<bf16>(hi);
-  return (uint32_t)__builtin_bit_cast(uint16_t, l) | ((uint32_t)__builtin_bit_cast(uint16_t, h) << 16);
-}
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) { return pack_bf16x2(lo, hi); }
 
 // Tile scheduler shared by the kernels: per-expert row-tile prefix (exclusive)
 // in s_pref[0..E], computed by wavefront 0.  E <= 256.

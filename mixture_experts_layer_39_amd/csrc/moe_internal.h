@@ -15,6 +15,15 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
+// Two floats to two bf16 (round to nearest even) in one 32-bit word, lo in
+// the low half: a single v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+  const bf16x2v r = __builtin_convertvector((f32x2){lo, hi}, bf16x2v);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
 enum { DT_F32 = 0, DT_BF16 = 1 };
 enum { ACT_NONE = 0, ACT_RELU = 1, ACT_GELU = 2 };
 enum { LOSS_BALANCE = 0, LOSS_USAGE_STD = 1 };
