@@ -1,6 +1,6 @@
 // Gate of the MoE layer: router GEMM, softmax, top-k, capacity slots,
-// expert counts and gate_loss, as one single-pass kernel plus a small slot
-// fix-up kernel.
+// expert counts and gate_loss, as three kernels: the gate proper, a scan over
+// tiles, and a slot fix-up.
 //
 // What is computed ("MoE混合专家架构：大模型高效推理的智能调度原理" §3.1,
 // MoELayer Steps 1-3; "deepspeed.moe 模块" overview §3.1 steps 1 and 5;
@@ -12,9 +12,8 @@
 //   plus (for j = 1) the total choice-0 demand of e; dropped if >= C.
 //
 // Design (gfx950):
-//  * One workgroup (4 waves) per tile of 64 tokens (32 when E > 128).  Tiles
-//    are numbered by an atomic ticket, so every lower tile is already
-//    resident when a tile looks back at it.
+//  * Gate kernel: one workgroup (4 waves) per tile of 64 tokens (32 when
+//    E > 128); tiles never wait for one another.
 //  * Router GEMM on MFMA v_mfma_f32_16x16x32_bf16 with experts on the MFMA
 //    row side and tokens on the column side: a lane ends up holding 4
 //    consecutive experts of one token, and a token's E logits sit in the 4
@@ -24,12 +23,17 @@
 //    partial logits are summed through LDS in a fixed order.
 //  * Softmax and top-k are per-lane scans plus two xor-shuffles; ties go to
 //    the lower index because every comparison is (value, index).
-//  * Ranks inside the tile come from an LDS scan; ranks across tiles from a
-//    decoupled look-back over per-(choice, expert) status words, one thread
-//    per column, so the whole prefix sum is one pass over the tokens.
-//  * Softmax column sums for the loss are reduced tile -> group of 32 tiles
-//    -> all, each level by the last arriving workgroup, always summing in
-//    index order, so the loss is bit-identical run to run.
+//  * Ranks inside the tile come from an LDS scan; each tile writes its
+//    per-(choice, expert) counts and softmax column sums.
+//  * Scan kernel: one workgroup per (choice, expert) column turns the
+//    column's tile counts into exclusive prefixes (tile order) and its total
+//    demand, and sums the column's probability mass in a fixed order, so the
+//    results are bit-identical run to run.  (A single-pass decoupled
+//    look-back chained one cross-XCD load per tile and took ~4x longer.)
+//  * Fix-up kernel: slot = tile prefix + rank (+ choice-0 demand for
+//    choice 1), dropped at or past the capacity; its last workgroup forms
+//    the expert counts, offsets and the loss.  Kernel boundaries order all of
+//    this, so no kernel waits on another workgroup.
 #include <math.h>
 
 #include "moe_internal.h"
@@ -37,18 +41,8 @@
 namespace moe {
 namespace {
 
-constexpr uint32_t ST_AGG = 1u << 30;   // word holds this tile's own count
-constexpr uint32_t ST_INC = 2u << 30;   // word holds the inclusive prefix
-constexpr uint32_t ST_VAL = (1u << 30) - 1u;
-
 enum { MODE_LOGITS_IN = 0, MODE_BF16 = 1, MODE_F32 = 2 };
 
-__device__ __forceinline__ uint32_t ld_agent(const uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_agent(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 __device__ __forceinline__ bf16x8 ld_bf16x8(const bf16* p) {
   return *reinterpret_cast<const bf16x8*>(p);
@@ -75,21 +69,13 @@ __global__ __launch_bounds__(256) void gate_kernel(GateArgs a) {
   f32x4* red = reinterpret_cast<f32x4*>(smem);                       // [4][TG][NET][64]
   int* s_sel = reinterpret_cast<int*>(smem + RED_BYTES);              // [2][TT]
   int* s_rnk = s_sel + 2 * TT;                                        // [2][TT]
-  int* s_cnt = s_rnk + 2 * TT;                                        // [2*EP]
-  int* s_base = s_cnt + 2 * EP;                                       // [2*EP]
-  float* s_me = reinterpret_cast<float*>(s_base + 2 * EP);            // [TG][EP]
-  double* s_dme = reinterpret_cast<double*>(s_me + TG * EP);          // [EP]
-  __shared__ int s_tile;
-  __shared__ int s_last;
-
+  float* s_me = reinterpret_cast<float*>(s_rnk + 2 * TT);             // [TG][EP]
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, n = lane & 15, q = lane >> 4;
   const int E = a.E, K = a.k, KE = a.k * a.E;
   const int64_t T = a.T;
 
-  if (tid == 0) s_tile = (int)atomicAdd(&a.counters[0], 1u);
-  __syncthreads();
-  const int tile = s_tile;
+  const int tile = blockIdx.x;
   const int64_t t0 = (int64_t)tile * TT;
 
   // ------------------------------------------------------------ logits
@@ -306,7 +292,7 @@ __global__ __launch_bounds__(256) void gate_kernel(GateArgs a) {
     const int j = c / E, e = c - j * E;
     int cnt = 0;
     for (int m = 0; m < TT; ++m) cnt += (s_sel[j * TT + m] == e);
-    s_cnt[c] = cnt;
+    a.tile_cnt[(int64_t)c * a.num_tiles + tile] = cnt;
   }
   for (int e = tid; e < E; e += 256) {
     float v = 0.f;
@@ -314,67 +300,70 @@ __global__ __launch_bounds__(256) void gate_kernel(GateArgs a) {
     a.me_tile[(int64_t)tile * E + e] = v;
   }
   __syncthreads();
-
-  // ------------------------------------------------------------ decoupled look-back
-  uint32_t* my = a.status + (int64_t)tile * KE;
-  for (int c = tid; c < KE; c += 256) st_agent(&my[c], (tile == 0 ? ST_INC : ST_AGG) | (uint32_t)s_cnt[c]);
-  for (int c = tid; c < KE; c += 256) {
-    uint32_t prefix = 0;
-    if (tile > 0) {
-      int p = tile - 1;
-      for (;;) {
-        const uint32_t v = ld_agent(&a.status[(int64_t)p * KE + c]);
-        if ((v & ~ST_VAL) == 0) {
-          __builtin_amdgcn_s_sleep(1);
-          continue;
-        }
-        prefix += v & ST_VAL;
-        if (v & ST_INC) break;
-        --p;
-      }
-      st_agent(&my[c], ST_INC | (prefix + (uint32_t)s_cnt[c]));
-    }
-    s_base[c] = (int)prefix;
-  }
-  __syncthreads();
+  // raw slot = rank inside the tile; the fix-up kernel adds the tile prefix
   for (int i = tid; i < K * TT; i += 256) {
     const int j = i / TT, nn = i - j * TT;
-    const int e = s_sel[i];
-    if (e >= 0) a.slot[(t0 + nn) * K + j] = s_base[j * E + e] + s_rnk[i];
+    if (s_sel[i] >= 0) a.slot[(t0 + nn) * K + j] = s_rnk[i];
   }
+}
 
-  // ------------------------------------------------------------ loss sums: tile -> group
-  __threadfence();
+// Exclusive prefix over tiles of one (choice, expert) column, its total
+// demand and (choice-0 columns) the expert's probability mass.
+__global__ __launch_bounds__(256) void gate_scan_kernel(GateArgs a) {
+  __shared__ int s_part[256];
+  __shared__ double s_dred[256];
+  const int tid = threadIdx.x, c = blockIdx.x;
+  const int E = a.E;
+  const int nt = a.num_tiles;
+  int32_t* col = a.tile_cnt + (int64_t)c * nt;
+  // each thread owns a contiguous run of tiles
+  const int per = (nt + 255) / 256;
+  const int lo = min(nt, tid * per), hi = min(nt, lo + per);
+  int sum = 0;
+  for (int i = lo; i < hi; ++i) sum += col[i];
+  s_part[tid] = sum;
   __syncthreads();
-  const int grp = tile / kGateGroupTiles;
-  const int g_first = grp * kGateGroupTiles;
-  const int g_last = min(g_first + kGateGroupTiles, a.num_tiles);
-  if (tid == 0) s_last = (atomicAdd(&a.counters[2 + grp], 1u) == (uint32_t)(g_last - g_first - 1));
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  for (int e = tid; e < E; e += 256) {
-    float v = 0.f;
-    for (int p = g_first; p < g_last; ++p) v += a.me_tile[(int64_t)p * E + e];
-    a.me_group[(int64_t)grp * E + e] = v;
+  // inclusive scan of the 256 partial sums (Hillis-Steele in LDS)
+  for (int off = 1; off < 256; off <<= 1) {
+    const int v = tid >= off ? s_part[tid - off] : 0;
+    __syncthreads();
+    s_part[tid] += v;
+    __syncthreads();
   }
-  // ------------------------------------------------------------ group -> all; finalize
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) s_last = (atomicAdd(&a.counters[1], 1u) == (uint32_t)(a.num_groups - 1));
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
+  int run = s_part[tid] - sum;
+  for (int i = lo; i < hi; ++i) {
+    const int v = col[i];
+    col[i] = run;
+    run += v;
+  }
+  if (tid == 255) a.demand[c] = s_part[255];
+  if (c < E) {
+    // probability mass of expert c: runs in tile order, then a fixed tree
+    double m = 0.0;
+    for (int i = lo; i < hi; ++i) m += (double)a.me_tile[(int64_t)i * E + c];
+    s_dred[tid] = m;
+    __syncthreads();
+    for (int off = 128; off > 0; off >>= 1) {
+      if (tid < off) s_dred[tid] += s_dred[tid + off];
+      __syncthreads();
+    }
+    if (tid == 0) a.me_sum[c] = s_dred[0];
+  }
+}
 
-  const uint32_t* last = a.status + (int64_t)(a.num_tiles - 1) * KE;
-  for (int c = tid; c < KE; c += 256) {
-    const int v = (int)(ld_agent(&last[c]) & ST_VAL);
-    s_cnt[c] = v;
-    a.demand[c] = v;
-  }
+// Expert counts (capacity applied per choice in order), offsets and the loss
+// from the scan's demands and probability mass, by one workgroup.
+__device__ void gate_counts_and_loss(const GateArgs& a) {
+  __shared__ int s_cnt[2 * MOE_MAX_EXPERTS_DEV];
+  __shared__ int s_base[MOE_MAX_EXPERTS_DEV];
+  __shared__ double s_dme[MOE_MAX_EXPERTS_DEV];
+  const int tid = threadIdx.x;
+  const int E = a.E, K = a.k, KE = a.k * a.E;
+  const int64_t T = a.T;
+  for (int cc = tid; cc < KE; cc += blockDim.x) s_cnt[cc] = a.demand[cc];
   __syncthreads();
   const int64_t C = a.C;
-  for (int e = tid; e < E; e += 256) {
+  for (int e = tid; e < E; e += blockDim.x) {
     const int64_t d0 = s_cnt[e];
     const int64_t d1 = (K == 2) ? s_cnt[E + e] : 0;
     int64_t kept;
@@ -389,9 +378,7 @@ __global__ __launch_bounds__(256) void gate_kernel(GateArgs a) {
     }
     a.expert_count[e] = (int32_t)kept;
     s_base[e] = (int)kept;
-    double me = 0.0;
-    for (int g = 0; g < a.num_groups; ++g) me += (double)a.me_group[(int64_t)g * E + e];
-    s_dme[e] = me;
+    s_dme[e] = a.me_sum[e];
   }
   __syncthreads();
   if (tid == 0) {
@@ -423,22 +410,26 @@ __global__ __launch_bounds__(256) void gate_kernel(GateArgs a) {
   }
 }
 
-__global__ void zero_u32_kernel(uint32_t* p, size_t n) {
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
-    p[i] = 0u;
-}
-
-// Final slots: choice 0 keeps its rank; choice 1 adds the expert's total
-// choice-0 demand; a slot at or past the capacity is dropped.
-__global__ void slot_finalize_kernel(const int32_t* __restrict__ expert_idx, int32_t* __restrict__ slot,
-                                     const int32_t* __restrict__ demand, int64_t n, int k, int64_t C) {
+// Final slots: the rank inside the tile plus the column's prefix over earlier
+// tiles; choice 1 also adds the expert's total choice-0 demand; a slot at or
+// past the capacity is dropped.  The grid's last workgroup instead forms the
+// expert counts, offsets and the loss.
+__global__ __launch_bounds__(256) void slot_finalize_kernel(GateArgs a, int tile_tokens) {
+  if (blockIdx.x == gridDim.x - 1) {
+    gate_counts_and_loss(a);
+    return;
+  }
+  const int64_t n = a.T * a.k;
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
+  const int k = a.k, E = a.E;
   const int j = (int)(i % k);
-  const int e = expert_idx[i];
-  int64_t s = slot[i];
-  if (j == 1) s += demand[e];
-  slot[i] = (C >= 0 && s >= C) ? -1 : (int32_t)s;
+  const int64_t t = i / k;
+  const int e = a.expert_idx[i];
+  const int c = j * E + e;
+  int64_t s = (int64_t)a.slot[i] + a.tile_cnt[(int64_t)c * a.num_tiles + t / tile_tokens];
+  if (j == 1) s += a.demand[e];
+  a.slot[i] = (a.C >= 0 && s >= a.C) ? -1 : (int32_t)s;
 }
 
 __global__ void gate_empty_kernel(int32_t* count, int32_t* offset, float* loss, int E) {
@@ -453,7 +444,7 @@ template <int EP, int TG, int MODE>
 size_t gate_lds_bytes() {
   constexpr int NET = EP / 16, TT = TG * 16;
   size_t red = (MODE == MODE_BF16) ? size_t(4) * TG * NET * 64 * 16 : 0;
-  return red + 4 * (2 * TT + 2 * TT + 2 * EP + 2 * EP + TG * EP) + 8 * EP;
+  return red + 4 * (2 * TT + 2 * TT + TG * EP);
 }
 
 template <int EP, int TG, int MODE>
@@ -481,34 +472,19 @@ hipError_t launch_gate_mode(const GateArgs& a, hipStream_t s) {
 
 }  // namespace
 
-size_t gate_sync_words(int64_t T, int E, int k) {
-  const int tt = gate_tile_tokens(E);
-  const int64_t tiles = (T + tt - 1) / tt;
-  const int64_t groups = (tiles + kGateGroupTiles - 1) / kGateGroupTiles;
-  return (size_t)(2 + groups) + (size_t)tiles * k * E;
-}
-
-hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t s) {
-  if (n == 0) return hipSuccess;
-  size_t blocks = (n + 255) / 256;
-  if (blocks > 1024) blocks = 1024;
-  hipLaunchKernelGGL(zero_u32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, n);
+hipError_t launch_gate(const GateArgs& a, int dtype, hipStream_t s) {
+  hipError_t e;
+  if (a.logits_in) e = launch_gate_mode<MODE_LOGITS_IN>(a, s);
+  else if (dtype == DT_BF16) e = launch_gate_mode<MODE_BF16>(a, s);
+  else e = launch_gate_mode<MODE_F32>(a, s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(gate_scan_kernel, dim3((unsigned)(a.k * a.E)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_gate(const GateArgs& a, int dtype, hipStream_t s) {
-  if (a.logits_in) return launch_gate_mode<MODE_LOGITS_IN>(a, s);
-  if (dtype == DT_BF16) return launch_gate_mode<MODE_BF16>(a, s);
-  return launch_gate_mode<MODE_F32>(a, s);
-}
-
-hipError_t launch_slot_finalize(const int32_t* expert_idx, int32_t* slot, const int32_t* demand,
-                                int64_t T, int k, int E, int64_t C, hipStream_t s) {
-  (void)E;
-  const int64_t n = T * k;
-  if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(slot_finalize_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
-                     expert_idx, slot, demand, n, k, C);
+hipError_t launch_slot_finalize(const GateArgs& a, int tile_tokens, hipStream_t s) {
+  const int64_t n = a.T * a.k;
+  hipLaunchKernelGGL(slot_finalize_kernel, dim3((unsigned)((n + 255) / 256 + 1)), dim3(256), 0, s, a, tile_tokens);
   return hipGetLastError();
 }
 

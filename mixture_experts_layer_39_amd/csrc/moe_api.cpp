@@ -60,9 +60,8 @@ int64_t max_rows_of(const moe_config* c) {
 
 struct Layout {
   int64_t T, C, rows;
-  int tiles, groups;
-  size_t sync_words;
-  size_t counters, me_tile, me_group, demand, idx, slot, weight, offset;
+  int tiles, tile_tokens;
+  size_t tile_cnt, me_tile, me_sum, demand, idx, slot, weight, offset;
   size_t x_disp, a_save, h_disp, y_disp, d_act;
   size_t total;
 };
@@ -74,9 +73,8 @@ Layout layout_of(const moe_config* c) {
   L.rows = max_rows_of(c);
   const int E = c->num_experts, k = c->k, d = c->hidden_size, h = c->ffn_hidden;
   const int tt = gate_tile_tokens(E);
+  L.tile_tokens = tt;
   L.tiles = (int)((L.T + tt - 1) / tt);
-  L.groups = (L.tiles + kGateGroupTiles - 1) / kGateGroupTiles;
-  L.sync_words = gate_sync_words(L.T, E, k);
   const size_t s = (size_t)esize(c);
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -84,9 +82,9 @@ Layout layout_of(const moe_config* c) {
     off += align_up(bytes);
     return at;
   };
-  L.counters = take(L.sync_words * 4);
+  L.tile_cnt = take((size_t)L.tiles * k * E * 4);
   L.me_tile = take((size_t)L.tiles * E * 4);
-  L.me_group = take((size_t)L.groups * E * 4);
+  L.me_sum = take((size_t)E * 8);
   L.demand = take((size_t)2 * E * 4);
   L.idx = take((size_t)L.T * k * 4);
   L.slot = take((size_t)L.T * k * 4);
@@ -131,10 +129,9 @@ moe_status run_gate(const moe_config* c, const Layout& L, const void* x, const v
   a.expert_count = expert_count;
   a.expert_offset = expert_offset;
   a.gate_loss = gate_loss;
-  a.counters = at<uint32_t>(ws, L.counters);
-  a.status = a.counters + (2 + L.groups);
+  a.tile_cnt = at<int32_t>(ws, L.tile_cnt);
   a.me_tile = at<float>(ws, L.me_tile);
-  a.me_group = at<float>(ws, L.me_group);
+  a.me_sum = at<double>(ws, L.me_sum);
   a.demand = at<int32_t>(ws, L.demand);
   a.T = L.T;
   a.C = L.C;
@@ -144,10 +141,8 @@ moe_status run_gate(const moe_config* c, const Layout& L, const void* x, const v
   a.normalize = c->normalize_topk;
   a.loss_kind = c->loss_kind;
   a.num_tiles = L.tiles;
-  a.num_groups = L.groups;
-  MOE_TRY_HIP(launch_zero_u32(a.counters, L.sync_words, s));
   MOE_TRY_HIP(launch_gate(a, c->dtype, s));
-  MOE_TRY_HIP(launch_slot_finalize(expert_idx, slot, a.demand, L.T, c->k, c->num_experts, L.C, s));
+  MOE_TRY_HIP(launch_slot_finalize(a, L.tile_tokens, s));
   return MOE_OK;
 }
 

@@ -32,8 +32,6 @@ enum { LOSS_BALANCE = 0, LOSS_USAGE_STD = 1 };
 // Tokens per gate tile: 64 (4 groups of 16) while the padded expert count is
 // at most 128, else 32, so the cross-wave logit reduction fits in LDS.
 inline int gate_tile_tokens(int E) { return E <= 128 ? 64 : 32; }
-// Tiles per group of the two-level (tile -> group -> all) loss reduction.
-constexpr int kGateGroupTiles = 32;
 
 struct GateArgs {
   const void* x;            // [T, d] dtype (router GEMM modes)
@@ -47,25 +45,20 @@ struct GateArgs {
   int32_t* expert_count;    // [E]
   int32_t* expert_offset;   // [E+1]
   float* gate_loss;         // [1]
-  uint32_t* counters;       // [2 + groups]: ticket, groups done, per-group tiles done
-  uint32_t* status;         // [tiles, k*E] look-back words
+  int32_t* tile_cnt;        // [k*E, tiles]: claims per (choice, expert) column and
+                            // tile; the scan turns it into the exclusive prefix
   float* me_tile;           // [tiles, E] per-tile sums of the softmax probabilities
-  float* me_group;          // [groups, E]
+  double* me_sum;           // [E] their totals
   int32_t* demand;          // [k, E] total claims per (choice, expert)
   int64_t T;
   int64_t C;                // capacity, < 0 = none
   int32_t d, E, k;
   int32_t normalize, loss_kind;
-  int32_t num_tiles, num_groups;
+  int32_t num_tiles;
 };
 
-// Words of (counters + status) that must be zero before the gate kernel.
-size_t gate_sync_words(int64_t T, int E, int k);
-
-hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t s);
 hipError_t launch_gate(const GateArgs& a, int dtype, hipStream_t s);
-hipError_t launch_slot_finalize(const int32_t* expert_idx, int32_t* slot, const int32_t* demand,
-                                int64_t T, int k, int E, int64_t C, hipStream_t s);
+hipError_t launch_slot_finalize(const GateArgs& a, int tile_tokens, hipStream_t s);
 hipError_t launch_gate_empty(int32_t* expert_count, int32_t* expert_offset, float* gate_loss,
                              int E, hipStream_t s);
 
