@@ -391,6 +391,10 @@ hipError_t launch_ffn_backward(const GemmBwdArgs& a, int dtype, hipStream_t s) {
   g.act = a.act;
   g.max_rows = a.max_rows;
 
+  // the large-tile kernel when the shapes fit it, else the 128 x 128 kernels below
+  err = launch_backward_big(a, s);
+  if (err != hipSuccess && err != hipErrorNotSupported) return err;
+  if (err == hipErrorNotSupported) {
   // dA = (dY · W2[e]) ⊙ act'(A): rows = h (W2[e] row-contiguous along h), K = d
   g.A = W2; g.a_estride = (int64_t)d * h; g.lda = h;
   g.B = dY; g.ldb = d;
@@ -418,6 +422,7 @@ hipError_t launch_ffn_backward(const GemmBwdArgs& a, int dtype, hipStream_t s) {
   g.Y = static_cast<bf16*>(a.dW1); g.ldy = d;
   g.nrows = d; g.ncols = h;
   if ((err = launch<L_RC, L_RC, M_WGRAD, EPI_STORE>(g, s)) != hipSuccess) return err;
+  }
 
   if (a.db2) {
     hipLaunchKernelGGL(colsum_kernel, dim3((d + 255) / 256, a.E), dim3(256), 0, s, dY, a.offset, a.db2, d);

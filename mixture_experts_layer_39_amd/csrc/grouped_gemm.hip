@@ -293,111 +293,205 @@ __global__ __launch_bounds__(WT * WF * 64) void gemm_bf16_kernel(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Large-tile bf16 kernel (K a multiple of 64): 256 tokens x 256 features per
-// tile, 4 waves each owning 128 x 128 of it (16 MFMA 32x32x16 tiles, 256
-// accumulators per lane), one persistent workgroup per CU.
+// Large-tile bf16 kernel: 256 x 256 output tiles, 4 waves each owning 128 x
+// 128 of it (16 MFMA 32x32x16 tiles, 256 accumulators per lane), one
+// persistent workgroup per CU.  It serves the forward Linears and the four
+// GEMMs of the expert backward; the output's rows are the "token side" of
+// the tile and its (memory-contiguous) columns the "feature side".
 //  * Operands go from global memory straight into LDS (buffer_load ... lds),
-//    no register staging.  Each instruction moves 8 rows x 128 bytes; the
-//    16-byte chunk c of row r lands in slot c ^ ((r >> 1) & 7), so the
-//    fragment reads of 16 consecutive rows hit 16 different bank groups.
-//    Rows past the expert's last token or past N lie outside the buffer's
-//    range and read as zero.
-//  * Double-buffered 64-wide K steps: the loads of step s+2 are issued right
-//    after the barrier of step s and land while step s+1's MFMAs run.
+//    no register staging.  An operand is either K-contiguous (its rows are
+//    tile rows or features, K along the row: the forward's X and W) or
+//    transposed (its rows are K, the tile's 256 rows/features along the row:
+//    the backward's W as [K, N] and the packed activations as [rows, ·] when
+//    the contraction runs over the rows).
+//    K-contiguous: each load instruction moves 8 rows x 128 bytes of one
+//    64-wide K step; the 16-byte chunk c of row r lands in slot
+//    c ^ ((r >> 1) & 7), so the fragment reads of 16 consecutive rows hit
+//    16 different bank groups.
+//    Transposed: each load instruction moves 2 K rows x 512 bytes; chunk c of
+//    K row r lands in slot c ^ ((r & 3) * 4); fragments are read with
+//    ds_read_b64_tr_b16 (in each group of 16 lanes, lane i receives element
+//    i % 4 of the 8-byte read of lane 4j + i / 4 as its element j), which
+//    gives every lane 4 consecutive K values of one column.
+//    Rows (or, transposed, K rows) past the valid range lie outside the
+//    buffer descriptor's range and read as zero.
+//  * Double-buffered 64-wide K steps: the loads of step s+2 are issued during
+//    the last sub-step of step s, one per MFMA, and land while step s+1's
+//    MFMAs run.
 //  * Persistent: the grid is one workgroup per CU; each workgroup walks a
 //    strided run of tiles inside its XCD's contiguous share, so the tiles
 //    running together on one XCD share operands in its L2.  The first K step
 //    of the next tile is loaded while the current tile finishes its last step
 //    and its epilogue, and the tile prefix is computed once per workgroup.
-//  * An expert's rows are split into ceil(M/256) tiles of equal size rounded
-//    up to 32; the two token-side waves take alternate 32-row blocks and skip
-//    blocks past the tile's rows, so a short tile costs proportionally less.
+//  * Token-row tiles (forward, backward data gradients): an expert's rows are
+//    split into ceil(M/256) tiles of equal size rounded up to 32; the two
+//    token-side waves take alternate 32-row blocks and skip blocks past the
+//    tile's rows, so a short tile costs proportionally less.
+//    Weight-gradient tiles: the output is [M, N] per expert and K is the
+//    expert's ragged row count (experts without rows are zero-filled apart).
 namespace big {
 constexpr int BT = 256, BF = 256, BKB = 128;  // BKB: bytes of one row's K step
-constexpr int TILE_BYTES = 256 * BKB;          // one operand tile
-constexpr int STAGE = 2 * TILE_BYTES;          // X tile + W tile
+constexpr int TILE_BYTES = 256 * BKB;          // one operand tile (both layouts)
+constexpr int STAGE = 2 * TILE_BYTES;          // token tile + feature tile
 constexpr int LDS = 2 * STAGE;                 // double buffered
+constexpr int TRB = 512;                       // bytes of one K row of a transposed tile
 }  // namespace big
+
+enum { OP_KC = 0, OP_TR = 1 };          // operand layout
+enum { BM_ROWS = 0, BM_WGRAD = 1 };     // token-row tiles / weight-gradient tiles
+enum { BE_ACT = 0, BE_DACT = 1, BE_STORE = 2 };   // epilogue
+
+struct BigArgs {
+  const bf16* tok;          // token-side operand
+  const bf16* feat;         // feature-side operand
+  const bf16* bias;         // BE_ACT: [E, N] or null
+  const bf16* S;            // BE_DACT: pre-activation [rows, N]
+  bf16* Y;                  // output
+  bf16* Apre;               // BE_ACT: pre-activation output [rows, N] or null
+  const int32_t* offset;    // [E+1]
+  int64_t max_rows;         // upper bound on offset[E]
+  int64_t tok_ld;           // elements between the token operand's memory rows
+  int64_t feat_ld;          // elements between the feature operand's memory rows
+  int64_t feat_estride;     // elements between experts' feature operands (0: packed rows)
+  int64_t y_ld, y_estride;  // output row pitch; per-expert output stride (weight gradients)
+  int32_t E, N, K, M, act;  // K: contraction (token-row tiles); M: output rows (weight gradients)
+};
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// Per-expert tile counts (exclusive prefix in s_pref[0..E]), by wavefront 0:
+// token-row tiles ceil(rows/256), or mtw weight-gradient row tiles for every
+// expert that has rows.
+template <int MODE>
+__device__ __forceinline__ void big_prefix(const int32_t* __restrict__ offset, int E, int mtw, int* s_pref) {
+  const int lane = threadIdx.x & 63;
+  if ((threadIdx.x >> 6) == 0) {
+    int c[4];
+    int s = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int e = lane * 4 + r;
+      const int rows = e < E ? offset[e + 1] - offset[e] : 0;
+      c[r] = MODE == BM_WGRAD ? (rows > 0 ? mtw : 0) : (rows + big::BT - 1) / big::BT;
+      s += c[r];
+    }
+    int incl = s;
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      const int v = __shfl_up(incl, m);
+      if (lane >= m) incl += v;
+    }
+    int excl = incl - s;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int e = lane * 4 + r;
+      if (e <= E) s_pref[e] = excl;
+      excl += c[r];
+    }
+    if (lane == 63 && E == MOE_MAX_EXPERTS_DEV) s_pref[E] = incl;
+  }
+}
+
 // One output tile as this wave sees it.
 struct BigTile {
-  int row0, mbase, mvalid, n0, e;
-  int nbw;                        // this wave's valid 32-row token blocks (0..4)
-  __amdgpu_buffer_rsrc_t lr;      // the operand rows this wave loads (X or W)
+  int e, row0;            // expert, its first packed row
+  int mbase, mvalid;      // first tile row (expert-relative, or output row) and row count
+  int n0, nk;             // first feature, 64-wide K steps
+  int nbw;                // this wave's valid 32-row token blocks (0..4)
+  __amdgpu_buffer_rsrc_t lr;   // the operand this wave loads (token or feature side)
 };
 
 // Per-workgroup constants of the big kernel.
 struct BigCtx {
   unsigned char* smem;
-  int nk, wt, wf, h, r32, wave, lds_op;
-  uint32_t vbase_e, vbase_o, sbase, row_bytes;
+  int wt, wf, h, r32, wave, lds_op;
+  bool tr;                      // this wave's operand is transposed
+  uint32_t vbase_e, vbase_o;    // per-lane load offsets for even / odd instructions
+  uint32_t sbase, ld_bytes;     // per-wave row base; bytes between operand rows
 };
 
-__device__ __forceinline__ BigTile big_tile_desc(const GemmArgs& a, const BigCtx& c, int tile, const int* s_pref,
+template <int TOK, int FEAT, int MODE>
+__device__ __forceinline__ BigTile big_tile_desc(const BigArgs& a, const BigCtx& c, int tile, const int* s_pref,
                                                  int ntf) {
   using namespace big;
   const TileCoord tc = tile_coord(tile, s_pref, a.E, ntf);
   BigTile t;
   t.e = tc.e;
   t.row0 = a.offset[tc.e];
-  const int mrows = a.offset[tc.e + 1] - t.row0;
-  const int nmt = s_pref[tc.e + 1] - s_pref[tc.e];
-  const int per = (((mrows + nmt - 1) / nmt) + 31) & ~31;   // rows per tile, balanced
-  t.mbase = tc.mt * per;
-  t.mvalid = min(per, mrows - t.mbase);
+  const int rows = a.offset[tc.e + 1] - t.row0;
   t.n0 = tc.nf * BF;
-  const int nvb = (t.mvalid + 31) >> 5;                      // valid 32-row blocks
+  if constexpr (MODE == BM_WGRAD) {
+    t.mbase = tc.mt * BT;
+    t.mvalid = min(BT, a.M - t.mbase);
+    t.nk = (rows + 63) / 64;
+  } else {
+    const int nmt = s_pref[tc.e + 1] - s_pref[tc.e];
+    const int per = (((rows + nmt - 1) / nmt) + 31) & ~31;   // rows per tile, balanced
+    t.mbase = tc.mt * per;
+    t.mvalid = min(per, rows - t.mbase);
+    t.nk = a.K / 64;
+  }
+  const int nvb = (t.mvalid + 31) >> 5;                        // valid 32-row blocks
   // this wave's token blocks are wt, wt+2, wt+4, wt+6; the valid ones are a
   // prefix of that list
   t.nbw = nvb > c.wt ? min(4, (nvb - c.wt + 1) >> 1) : 0;
   if (c.wave >= 2) {
-    const bf16* Wp = static_cast<const bf16*>(a.W) + ((int64_t)tc.e * a.N + t.n0) * a.K;
-    t.lr = make_rsrc(Wp, (uint32_t)min(BF, a.N - t.n0) * c.row_bytes);
+    const int ncols = min(BF, a.N - t.n0);
+    if constexpr (FEAT == OP_KC) {
+      const bf16* p = a.feat + (int64_t)tc.e * a.feat_estride + (int64_t)t.n0 * a.feat_ld;
+      t.lr = make_rsrc(p, (uint32_t)ncols * c.ld_bytes);
+    } else {
+      const int krows = MODE == BM_WGRAD ? rows : a.K;
+      const bf16* p = a.feat + (int64_t)tc.e * a.feat_estride + (MODE == BM_WGRAD ? (int64_t)t.row0 * a.feat_ld : 0) +
+                      t.n0;
+      t.lr = make_rsrc(p, krows > 0 ? (uint32_t)(((int64_t)(krows - 1) * a.feat_ld + ncols) * 2) : 0u);
+    }
   } else {
-    const bf16* Xp = static_cast<const bf16*>(a.X) + (int64_t)(t.row0 + t.mbase) * a.K;
-    t.lr = make_rsrc(Xp, (uint32_t)t.mvalid * c.row_bytes);
+    if constexpr (TOK == OP_KC) {
+      const bf16* p = a.tok + (int64_t)(t.row0 + t.mbase) * a.tok_ld;
+      t.lr = make_rsrc(p, (uint32_t)t.mvalid * c.ld_bytes);
+    } else {
+      const bf16* p = a.tok + (int64_t)t.row0 * a.tok_ld + t.mbase;
+      t.lr = make_rsrc(p, rows > 0 ? (uint32_t)(((int64_t)(rows - 1) * a.tok_ld + t.mvalid) * 2) : 0u);
+    }
   }
   return t;
 }
 
-// The DMA loads of one 64-wide K step (at element k0) of this wave's operand
-// rows into a stage: 16 instructions of 8 rows x 128 bytes.  Waves 0-1 fill
-// the X tile, waves 2-3 the W tile (weight rows permuted so the MFMA row
-// m = lane&31 reads feature ((m>>2)&1)*16 + (m>>3)*4 + (m&3)).
-__device__ __forceinline__ void big_issue(const BigCtx& c, __amdgpu_buffer_rsrc_t lr, int stage, int k0) {
+// Load number i (0..15) of this wave's share of one 64-wide K step (kstep)
+// into a stage.  K-contiguous: 8 rows x 128 bytes; waves 0-1 fill the token
+// tile, waves 2-3 the feature tile (feature rows permuted so the MFMA row
+// m = lane&31 reads feature ((m>>2)&1)*16 + (m>>3)*4 + (m&3)); the row goes
+// in the per-lane offset, which the buffer range check always covers, and
+// only the position along K (inside a valid row) in the scalar offset.
+// Transposed: K rows 2i, 2i+1 of this wave's 32, 512 bytes each; the K row
+// goes in the per-lane offset (K rows past the end read as zero).
+__device__ __forceinline__ void big_issue_one(const BigCtx& c, __amdgpu_buffer_rsrc_t lr, int stage, int kstep, int i) {
   using namespace big;
-  unsigned char* base = c.smem + stage * STAGE + c.lds_op + (c.wave & 1) * 128 * BKB;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const uint32_t g = c.wave >= 2 ? (uint32_t)((i >> 2) * 32 + (i & 3) * 4) : (uint32_t)(i * 8);
-    // the row part goes in the per-lane offset, which the buffer range check
-    // always covers (rows past the end read as zero); only the position
-    // along K, which stays inside a valid row, goes in the scalar offset
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(lr, (__attribute__((address_space(3))) void*)(base + i * 8 * BKB), 16,
-                                             ((i & 1) ? c.vbase_o : c.vbase_e) + c.sbase + g * c.row_bytes,
-                                             (uint32_t)k0 * 2, 0, 0);
-  }
+  // both layouts put load i of this wave at the same LDS offset: 16 KB per
+  // wave, 1 KB per instruction (8 rows x 128 B, or 2 K rows x 512 B)
+  unsigned char* dst = c.smem + stage * STAGE + c.lds_op + (c.wave & 1) * 16384 + i * 1024;
+  // wave-uniform row offset and K offset, chosen without a branch
+  const uint32_t g = c.wave >= 2 ? (uint32_t)((i >> 2) * 32 + (i & 3) * 4) : (uint32_t)(i * 8);
+  const uint32_t kc_row = c.sbase + g * c.ld_bytes;
+  const uint32_t tr_row = (uint32_t)(kstep * 64 + (c.wave & 1) * 32 + 2 * i) * c.ld_bytes;
+  const uint32_t vrow = c.tr ? tr_row : kc_row;
+  const uint32_t soff = c.tr ? 0u : (uint32_t)kstep * 128;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(lr, (__attribute__((address_space(3))) void*)dst, 16,
+                                           ((i & 1) ? c.vbase_o : c.vbase_e) + vrow, soff, 0, 0);
 }
 
-// Load number i (0..15) of big_issue alone.
-__device__ __forceinline__ void big_issue_one(const BigCtx& c, __amdgpu_buffer_rsrc_t lr, int stage, int k0, int i) {
-  using namespace big;
-  unsigned char* base = c.smem + stage * STAGE + c.lds_op + (c.wave & 1) * 128 * BKB;
-  const uint32_t g = c.wave >= 2 ? (uint32_t)((i >> 2) * 32 + (i & 3) * 4) : (uint32_t)(i * 8);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(lr, (__attribute__((address_space(3))) void*)(base + i * 8 * BKB), 16,
-                                           ((i & 1) ? c.vbase_o : c.vbase_e) + c.sbase + g * c.row_bytes,
-                                           (uint32_t)k0 * 2, 0, 0);
+__device__ __forceinline__ void big_issue(const BigCtx& c, __amdgpu_buffer_rsrc_t lr, int stage, int kstep) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) big_issue_one(c, lr, stage, kstep, i);
 }
 
 // This tile's bias (zero without one) into LDS for the epilogue.
-__device__ __forceinline__ void big_bias(const GemmArgs& a, const BigTile& t, float* s_bias) {
+__device__ __forceinline__ void big_bias(const BigArgs& a, const BigTile& t, float* s_bias) {
   const int f = t.n0 + threadIdx.x;
-  s_bias[threadIdx.x] =
-      (a.bias && f < a.N) ? static_cast<float>(static_cast<const bf16*>(a.bias)[(int64_t)t.e * a.N + f]) : 0.f;
+  s_bias[threadIdx.x] = (a.bias && f < a.N) ? static_cast<float>(a.bias[(int64_t)t.e * a.N + f]) : 0.f;
 }
 
 // Read one accumulator element out of its AGPR at the point of use.  Without
@@ -429,27 +523,95 @@ __device__ __forceinline__ void acc_block(const f32x16 (&acc)[4][4], int blk, fl
   }
 }
 
-// Epilogue of one 32x32 accumulator: this lane's 16 consecutive features f0..
-// of token row rloc (tile-relative): + bias (from LDS), optional
-// pre-activation store, activation, bf16 store (two 16-byte vectors).
+// d/dx of the activation, from the same erf as gelu_fast: for GELU
+// Phi(x) + x phi(x), with phi(x) = exp(-x^2/2) / sqrt(2 pi).
 template <int ACT>
-__device__ __forceinline__ void big_store(const GemmArgs& a, float (&v)[16], const BigTile& t, int rloc, int fl,
-                                          const float* s_bias) {
-  const int N = a.N;
-  const int f0 = t.n0 + fl;
-  const int64_t grow = (int64_t)t.row0 + t.mbase + rloc;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) v[r] += s_bias[fl + r];
-  if (a.Apre) {
-    uint4* p = reinterpret_cast<uint4*>(static_cast<bf16*>(a.Apre) + grow * N + f0);
-    p[0] = make_uint4(pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7]));
-    p[1] = make_uint4(pack2(v[8], v[9]), pack2(v[10], v[11]), pack2(v[12], v[13]), pack2(v[14], v[15]));
+__device__ __forceinline__ float act_grad_fixed(float x) {
+  if constexpr (ACT == ACT_RELU) {
+    return x > 0.f ? 1.f : 0.f;
+  } else if constexpr (ACT == ACT_GELU) {
+    const float z = fabsf(x) * 0.7071067811865476f;
+    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.f));
+    float poly = fmaf(1.061405429f, t, -1.453152027f);
+    poly = fmaf(poly, t, 1.421413741f);
+    poly = fmaf(poly, t, -0.284496736f);
+    poly = fmaf(poly, t, 0.254829592f);
+    poly *= t;
+    const float e = __builtin_amdgcn_exp2f(-z * z * 1.4426950408889634f);   // exp(-x^2/2)
+    const float erf_v = __builtin_copysignf(fmaf(-poly, e, 1.f), x);
+    return 0.5f * (1.f + erf_v) + x * e * 0.3989422804014327f;
+  } else {
+    return 1.f;
   }
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+// Epilogue of one 32x32 accumulator: this lane's 16 consecutive output
+// columns f0.. of tile row rloc, as two 16-byte vectors.
+//  BE_ACT:   + bias (from LDS), optional pre-activation store, activation.
+//  BE_DACT:  times act'(S) at the same position.
+//  BE_STORE: as is.
+template <int EPI, int ACT, int MODE>
+__device__ __forceinline__ void big_store(const BigArgs& a, float (&v)[16], const BigTile& t, int rloc, int fl,
+                                          const float* s_bias) {
+  const int f0 = t.n0 + fl;
+  int64_t off;
+  if constexpr (MODE == BM_WGRAD)
+    off = (int64_t)t.e * a.y_estride + (int64_t)(t.mbase + rloc) * a.y_ld + f0;
+  else
+    off = ((int64_t)t.row0 + t.mbase + rloc) * a.y_ld + f0;
+  if constexpr (EPI == BE_ACT) {
 #pragma unroll
-  for (int r = 0; r < 16; ++r) v[r] = act_fixed<ACT>(v[r]);
-  uint4* p = reinterpret_cast<uint4*>(static_cast<bf16*>(a.Y) + grow * N + f0);
+    for (int r = 0; r < 16; ++r) v[r] += s_bias[fl + r];
+    if (a.Apre) {
+      uint4* p = reinterpret_cast<uint4*>(a.Apre + off);
+      p[0] = make_uint4(pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7]));
+      p[1] = make_uint4(pack2(v[8], v[9]), pack2(v[10], v[11]), pack2(v[12], v[13]), pack2(v[14], v[15]));
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) v[r] = act_fixed<ACT>(v[r]);
+  } else if constexpr (EPI == BE_DACT) {
+    if constexpr (ACT != ACT_NONE) {
+      const uint4* sp = reinterpret_cast<const uint4*>(a.S + off);
+      const uint4 s0 = sp[0], s1 = sp[1];
+      const uint32_t sw[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        v[2 * q] *= act_grad_fixed<ACT>(bf16_lo(sw[q]));
+        v[2 * q + 1] *= act_grad_fixed<ACT>(bf16_hi(sw[q]));
+      }
+    }
+  }
+  uint4* p = reinterpret_cast<uint4*>(a.Y + off);
   p[0] = make_uint4(pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7]));
   p[1] = make_uint4(pack2(v[8], v[9]), pack2(v[10], v[11]), pack2(v[12], v[13]), pack2(v[14], v[15]));
+}
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+
+// One ds_read_b64_tr_b16.  The restrict-qualified pointer gives the read
+// alias-scope information; without it the compiler assumes the read may
+// alias any LDS-DMA load in flight and puts a full vmcnt(0) wait before it,
+// which serialises the load pipeline.  The kernel's own waitcnt + barrier at
+// every K step already keeps reads off a stage whose loads are in flight.
+__device__ __forceinline__ v4i16 ds_read_tr16(const __attribute__((address_space(3))) v4i16* __restrict__ p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)p);
+}
+
+// One fragment of 8 K values (sub-step i) of a transposed operand: two
+// ds_read_b64_tr_b16 of 4 K rows each.  col is this lane's source column for
+// the read (its group of 16 lanes covers 16 columns of one 32-wide block).
+__device__ __forceinline__ bf16x8 tr_frag(const unsigned char* tile, int i, int h, int lane16, int col) {
+  using namespace big;
+  const int k0 = 8 * (h * 4 + i) + (lane16 >> 2);            // K row of this lane's first read
+  const int sw = ((col >> 3) ^ ((lane16 >> 2) * 4)) * 16 + (col & 7) * 2;
+  const v4i16 lo = ds_read_tr16((const __attribute__((address_space(3))) v4i16*)(tile + k0 * TRB + sw));
+  const v4i16 hi = ds_read_tr16((const __attribute__((address_space(3))) v4i16*)(tile + (k0 + 4) * TRB + sw));
+  const v8i16 r = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, r);
 }
 
 // One wave's share of a tile with NB valid 32-row token blocks (NB in 0..4):
@@ -459,13 +621,14 @@ __device__ __forceinline__ void big_store(const GemmArgs& a, float (&v)[16], con
 // call.  If there is a next tile, its step 0 is issued into the stage this
 // tile's step nk-2 used (the other stage when nk == 1), which is stage 0 of
 // the next tile's numbering with sb' = (sb + nk) & 1.
-template <int NB, int ACT>
-__device__ __forceinline__ void big_tile(const GemmArgs& a, const BigCtx& c, const BigTile& t, int sb, bool has_next,
+template <int NB, int EPI, int ACT, int TOK, int FEAT, int MODE>
+__device__ __forceinline__ void big_tile(const BigArgs& a, const BigCtx& c, const BigTile& t, int sb, bool has_next,
                                          __amdgpu_buffer_rsrc_t next_lr, const float* s_bias) {
   using namespace big;
   unsigned char* smem = c.smem;
-  const int nk = c.nk, wt = c.wt, wf = c.wf, h = c.h, r32 = c.r32;
+  const int nk = t.nk, wt = c.wt, wf = c.wf, h = c.h, r32 = c.r32;
   const int N = a.N;
+  const int lane = threadIdx.x & 63, lane16 = lane & 15, mh = (lane >> 4) & 1, q4 = lane & 3;
   f32x16 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -475,29 +638,39 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const BigCtx& c, con
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
   // Fragment registers: two sets, so that sub-step i+1's fragments are read
   // while sub-step i's MFMAs run (sub-step i uses set i & 1).  Sub-step i of
-  // a 64-wide K step reads chunk h*4+i of each 128-byte row (slot chunk ^
-  // ((row >> 1) & 7)).
+  // a 64-wide K step covers, for lane half h, the 8 K values of chunk h*4+i
+  // (the same order on both operands, which leaves the dot product alone).
   bf16x8 fa[2][4], fb[2][NB > 0 ? NB : 1];
   constexpr int NM = 4 * NB;       // MFMAs per sub-step
   constexpr int NR = 4 + NB;       // fragment reads per sub-step
+  // transposed-read source columns of this lane within a 32-wide block: the
+  // token side reads columns in order, the feature side in the permuted order
+  // that gives each lane 16 consecutive output features
+  const int tok_col = mh * 16 + 4 * q4;
+  const int feat_col = (q4 & 1) * 16 + mh * 8 + (q4 >> 1) * 4;
   // fragment read r of sub-step i from a stage into a set, in the order the
-  // MFMAs consume them: token block 0, the four weight blocks, then the other
-  // token blocks
+  // MFMAs consume them: token block 0, the four feature blocks, then the
+  // other token blocks
   auto read1 = [&](int stage, int i, int set, int r) {
     const unsigned char* Xs = smem + stage * STAGE;
     const unsigned char* Ws = Xs + TILE_BYTES;
     const int sw = (((h * 4 + i) ^ ((r32 >> 1) & 7)) * 16);
-    if (NB > 0 && r == 0) {
-      fb[set][0] = *reinterpret_cast<const bf16x8*>(Xs + (wt * 32 + r32) * BKB + sw);
-    } else {
-      const int q = NB > 0 ? r - 1 : r;   // 0..3: weight block, 4..: token block q - 3
-      if (q < 4)
-        fa[set][q] = *reinterpret_cast<const bf16x8*>(Ws + (wf * 128 + q * 32 + r32) * BKB + sw);
+    const bool tokr = NB > 0 && (r == 0 || r >= 5);
+    const int tt = r == 0 ? 0 : r - 4;
+    const int ff = NB > 0 ? r - 1 : r;
+    if (tokr) {
+      if constexpr (TOK == OP_KC)
+        fb[set][tt] = *reinterpret_cast<const bf16x8*>(Xs + ((wt + 2 * tt) * 32 + r32) * BKB + sw);
       else
-        fb[set][q - 3] = *reinterpret_cast<const bf16x8*>(Xs + ((wt + 2 * (q - 3)) * 32 + r32) * BKB + sw);
+        fb[set][tt] = tr_frag(Xs, i, h, lane16, (wt + 2 * tt) * 32 + tok_col);
+    } else {
+      if constexpr (FEAT == OP_KC)
+        fa[set][ff] = *reinterpret_cast<const bf16x8*>(Ws + (wf * 128 + ff * 32 + r32) * BKB + sw);
+      else
+        fa[set][ff] = tr_frag(Ws, i, h, lane16, wf * 128 + ff * 32 + feat_col);
     }
   };
-  // MFMA j of a sub-step: token block j / 4 with weight block j % 4
+  // MFMA j of a sub-step: token block j / 4 with feature block j % 4
   auto mfma1 = [&](int set, int j) {
     const int tt = j >> 2, ff = j & 3;
     acc[ff][tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][ff], fb[set][tt], acc[ff][tt], 0, 0, 0);
@@ -507,7 +680,7 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const BigCtx& c, con
   // MFMAs) and, when loading, of the 16 global->LDS loads, so that the memory
   // instructions issue in the shadow of the MFMAs instead of in a bubble.
   auto substep = [&](auto loads, int mset, int rstage, int ri, int rset, __amdgpu_buffer_rsrc_t llr, int lstage,
-                     int lk0) {
+                     int lkstep) {
     constexpr bool LOADS = decltype(loads)::value;
     constexpr int NJ = NM > NR ? NM : NR;
 #pragma unroll
@@ -516,12 +689,9 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const BigCtx& c, con
       if constexpr (LOADS) {
         if constexpr (NM > 0) {
 #pragma unroll
-          for (int q = j * 16 / NM; q < (j + 1) * 16 / NM && j < NM; ++q) big_issue_one(c, llr, lstage, lk0, q);
+          for (int q = j * 16 / NM; q < (j + 1) * 16 / NM && j < NM; ++q) big_issue_one(c, llr, lstage, lkstep, q);
         } else {
-          if (j == 0) {
-#pragma unroll
-            for (int q = 0; q < 16; ++q) big_issue_one(c, llr, lstage, lk0, q);
-          }
+          if (j == 0) big_issue(c, llr, lstage, lkstep);
         }
       }
       if (j < NR && ri >= 0) read1(rstage, ri, rset, j);
@@ -530,7 +700,7 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const BigCtx& c, con
   };
   using NoLoads = std::integral_constant<bool, false>;
   using Loads = std::integral_constant<bool, true>;
-  const __amdgpu_buffer_rsrc_t no_lr = make_rsrc(a.X, 0);
+  const __amdgpu_buffer_rsrc_t no_lr = make_rsrc(a.tok, 0);
   // Stage s holds K step s (mod 2, offset by sb).  The one barrier per step
   // sits before sub-step 3: by then every wave has read all of the current
   // stage (so the loads two steps ahead may overwrite it) and the next stage
@@ -543,7 +713,7 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const BigCtx& c, con
   const __amdgpu_buffer_rsrc_t tail_lr = has_next ? next_lr : no_lr;
   __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_s_barrier();
-  if (nk > 1) big_issue(c, t.lr, (sb + 1) & 1, 64);
+  if (nk > 1) big_issue(c, t.lr, (sb + 1) & 1, 1);
   else big_issue(c, tail_lr, (sb + 1) & 1, 0);
 #pragma unroll
   for (int r = 0; r < NR; ++r) read1(sb, 0, 0, r);
@@ -556,7 +726,7 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const BigCtx& c, con
     __builtin_amdgcn_s_waitcnt(0);  // own loads of the next stage and own reads of this one
     __builtin_amdgcn_s_barrier();
     const bool more = kt + 2 < nk;
-    substep(Loads{}, 1, cur ^ 1, 0, 0, more ? t.lr : tail_lr, cur, more ? (kt + 2) * 64 : 0);
+    substep(Loads{}, 1, cur ^ 1, 0, 0, more ? t.lr : tail_lr, cur, more ? kt + 2 : 0);
   }
   {
     const int cur = (nk - 1 + sb) & 1;
@@ -572,25 +742,26 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const BigCtx& c, con
   for (int blk = 0; blk < 16; ++blk) {
     const int ff = blk >> 2, tt = blk & 3;
     const int rloc = (wt + 2 * tt) * 32 + r32;
-    const int fl = wf * 128 + ff * 32 + h * 16;   // feature offset within the tile
+    const int fl = wf * 128 + ff * 32 + h * 16;   // column offset within the tile
     if (tt >= NB || t.n0 + fl >= N) continue;
     float v[16];
     acc_block<NB>(acc, blk, v);
-    if (rloc < t.mvalid) big_store<ACT>(a, v, t, rloc, fl, s_bias);
+    if (rloc < t.mvalid) big_store<EPI, ACT, MODE>(a, v, t, rloc, fl, s_bias);
   }
 }
 
-template <int ACT>
+template <int EPI, int ACT, int TOK, int FEAT, int MODE>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
-void gemm_bf16_big_kernel(GemmArgs a) {
+void gemm_bf16_big_kernel(BigArgs a) {
   using namespace big;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __shared__ int s_pref[MOE_MAX_EXPERTS_DEV + 1];
   __shared__ float s_bias[2][BF];   // alternate tiles use alternate halves
 
-  const int E = a.E, N = a.N, K = a.K;
+  const int E = a.E, N = a.N;
   const int ntf = (N + BF - 1) / BF;
-  tile_prefix<BT>(a.offset, E, s_pref);
+  const int mtw = MODE == BM_WGRAD ? (a.M + BT - 1) / BT : 0;
+  big_prefix<MODE>(a.offset, E, mtw, s_pref);
   __syncthreads();
   const int total = s_pref[E] * ntf;
   // this XCD's contiguous share of the tiles, walked with stride L by its L
@@ -608,55 +779,75 @@ void gemm_bf16_big_kernel(GemmArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   BigCtx c;
   c.smem = smem;
-  c.nk = K / 64;
   c.wt = wave >> 1;
   c.wf = wave & 1;
   c.h = lane >> 5;
   c.r32 = lane & 31;
   c.wave = wave;
   c.lds_op = wave >= 2 ? TILE_BYTES : 0;
-  c.row_bytes = (uint32_t)K * 2;
-  // this lane's source row / chunk for each of its 16 load instructions.
-  // Chunk c of tile row r sits in slot c ^ ((r >> 1) & 7): sixteen
-  // consecutive rows read at one chunk hit sixteen different 16-byte bank
-  // groups.  For load i the rows are 8i + lrow (+ a multiple of 16 per wave),
-  // so (r >> 1) & 7 = 4 * (i & 1) + (lrow >> 1): two lane patterns, even and
-  // odd i.  Load i of this wave covers tile rows (wave&1)*128 + i*8 .. +7.
-  // For X the source row is that row; for W it is the permuted feature, which
-  // works out to a per-lane part ((lrow>>2)&1)*16 + (lrow&3) plus a
-  // wave-uniform part (i>>2)*32 + (i&3)*4, so each load needs one VGPR offset
-  // and one SGPR offset.
-  const int lrow = lane >> 3;
-  const int chunk_e = (lane & 7) ^ (lrow >> 1);
-  const int chunk_o = (lane & 7) ^ (4 + (lrow >> 1));
-  const uint32_t vrow = (uint32_t)(wave >= 2 ? (((lrow >> 2) & 1) * 16 + (lrow & 3)) : lrow) * c.row_bytes;
-  c.vbase_e = vrow + chunk_e * 16;
-  c.vbase_o = vrow + chunk_o * 16;
-  c.sbase = (uint32_t)(wave & 1) * 128 * c.row_bytes;
+  c.tr = wave >= 2 ? FEAT == OP_TR : TOK == OP_TR;
+  c.ld_bytes = (uint32_t)((wave >= 2 ? a.feat_ld : a.tok_ld) * 2);
+  if (!c.tr) {
+    // K-contiguous: this lane's source row / chunk for each of its 16 load
+    // instructions.  Chunk c of tile row r sits in slot c ^ ((r >> 1) & 7).
+    // For load i the rows are 8i + lrow (+ a multiple of 16 per wave), so
+    // (r >> 1) & 7 = 4 * (i & 1) + (lrow >> 1): two lane patterns, even and
+    // odd i.  Load i of this wave covers tile rows (wave&1)*128 + i*8 .. +7.
+    // For the token side the source row is that row; for the feature side it
+    // is the permuted feature, which works out to a per-lane part
+    // ((lrow>>2)&1)*16 + (lrow&3) plus a wave-uniform part (i>>2)*32 +
+    // (i&3)*4, so each load needs one VGPR offset and one SGPR offset.
+    const int lrow = lane >> 3;
+    const int chunk_e = (lane & 7) ^ (lrow >> 1);
+    const int chunk_o = (lane & 7) ^ (4 + (lrow >> 1));
+    const uint32_t vrow = (uint32_t)(wave >= 2 ? (((lrow >> 2) & 1) * 16 + (lrow & 3)) : lrow) * c.ld_bytes;
+    c.vbase_e = vrow + chunk_e * 16;
+    c.vbase_o = vrow + chunk_o * 16;
+    c.sbase = (uint32_t)(wave & 1) * 128 * c.ld_bytes;
+  } else {
+    // Transposed: load i moves K rows r, r+1 (r = (wave&1)*32 + 2i), lane j
+    // filling slot j % 32 of row r + j / 32; slot p of K row r holds chunk
+    // p ^ ((r & 3) * 4), and (r & 3) = 2 * (i & 1) + j / 32.
+    const int half = lane >> 5, p = lane & 31;
+    c.vbase_e = (uint32_t)half * c.ld_bytes + (uint32_t)((p ^ (half * 4)) * 16);
+    c.vbase_o = (uint32_t)half * c.ld_bytes + (uint32_t)((p ^ ((2 + half) * 4)) * 16);
+    c.sbase = 0;
+  }
 
-  BigTile cur = big_tile_desc(a, c, tile, s_pref, ntf);
+  BigTile cur = big_tile_desc<TOK, FEAT, MODE>(a, c, tile, s_pref, ntf);
   big_issue(c, cur.lr, 0, 0);
-  big_bias(a, cur, s_bias[0]);
+  if constexpr (EPI == BE_ACT) big_bias(a, cur, s_bias[0]);
   int sb = 0, par = 0;
   for (;;) {
     const int next = tile + per_xcd;
     const bool has_next = next < t_end;
     BigTile nt = cur;
-    if (has_next) nt = big_tile_desc(a, c, next, s_pref, ntf);
+    if (has_next) nt = big_tile_desc<TOK, FEAT, MODE>(a, c, next, s_pref, ntf);
     switch (cur.nbw) {
-      case 4: big_tile<4, ACT>(a, c, cur, sb, has_next, nt.lr, s_bias[par]); break;
-      case 3: big_tile<3, ACT>(a, c, cur, sb, has_next, nt.lr, s_bias[par]); break;
-      case 2: big_tile<2, ACT>(a, c, cur, sb, has_next, nt.lr, s_bias[par]); break;
-      case 1: big_tile<1, ACT>(a, c, cur, sb, has_next, nt.lr, s_bias[par]); break;
-      default: big_tile<0, ACT>(a, c, cur, sb, has_next, nt.lr, s_bias[par]); break;
+      case 4: big_tile<4, EPI, ACT, TOK, FEAT, MODE>(a, c, cur, sb, has_next, nt.lr, s_bias[par]); break;
+      case 3: big_tile<3, EPI, ACT, TOK, FEAT, MODE>(a, c, cur, sb, has_next, nt.lr, s_bias[par]); break;
+      case 2: big_tile<2, EPI, ACT, TOK, FEAT, MODE>(a, c, cur, sb, has_next, nt.lr, s_bias[par]); break;
+      case 1: big_tile<1, EPI, ACT, TOK, FEAT, MODE>(a, c, cur, sb, has_next, nt.lr, s_bias[par]); break;
+      default: big_tile<0, EPI, ACT, TOK, FEAT, MODE>(a, c, cur, sb, has_next, nt.lr, s_bias[par]); break;
     }
     if (!has_next) break;
-    sb = (sb + c.nk) & 1;
+    sb = (sb + cur.nk) & 1;
     par ^= 1;
-    big_bias(a, nt, s_bias[par]);   // visible after the next tile's first barrier
+    if constexpr (EPI == BE_ACT) big_bias(a, nt, s_bias[par]);   // visible after the next tile's first barrier
     cur = nt;
     tile = next;
   }
+}
+
+// Zero the weight gradient of every expert without rows (their tiles are not
+// in the weight-gradient schedule).
+__global__ __launch_bounds__(256) void zero_empty_experts_kernel(bf16* Y, const int32_t* offset, int64_t per_expert) {
+  const int e = blockIdx.y;
+  if (offset[e + 1] != offset[e]) return;
+  uint4* p = reinterpret_cast<uint4*>(Y + (int64_t)e * per_expert);
+  const int64_t n = per_expert / 8;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
 // fp32: one thread per output element (used for the small fp32 layers).
@@ -711,29 +902,111 @@ int device_cus() {
   return cached[dev];
 }
 
-template <int ACT>
-hipError_t launch_bf16_big_t(const GemmArgs& a, hipStream_t s) {
-  auto kern = gemm_bf16_big_kernel<ACT>;
+template <int EPI, int ACT, int TOK, int FEAT, int MODE>
+hipError_t launch_big(const BigArgs& a, hipStream_t s) {
+  auto kern = gemm_bf16_big_kernel<EPI, ACT, TOK, FEAT, MODE>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, big::LDS);
   if (e != hipSuccess) return e;
   // at most one workgroup per CU (LDS use allows no more), never more than
   // the worst-case tile count, a whole number per XCD
-  const int64_t max_mtiles = (a.max_rows + big::BT - 1) / big::BT + a.E;
   const int64_t ntf = (a.N + big::BF - 1) / big::BF;
-  int64_t grid = std::min<int64_t>(max_mtiles * ntf, device_cus());
+  const int64_t mtiles = MODE == BM_WGRAD ? (int64_t)a.E * ((a.M + big::BT - 1) / big::BT)
+                                          : (a.max_rows + big::BT - 1) / big::BT + a.E;
+  int64_t grid = std::min<int64_t>(mtiles * ntf, device_cus());
   grid = std::max<int64_t>(kXcds, grid / kXcds * kXcds);
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), big::LDS, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_bf16_big(const GemmArgs& a, hipStream_t s) {
-  if (a.act == ACT_GELU) return launch_bf16_big_t<ACT_GELU>(a, s);
-  if (a.act == ACT_RELU) return launch_bf16_big_t<ACT_RELU>(a, s);
-  return launch_bf16_big_t<ACT_NONE>(a, s);
+template <int EPI, int TOK, int FEAT, int MODE>
+hipError_t launch_big_act(const BigArgs& a, hipStream_t s) {
+  if (a.act == ACT_GELU) return launch_big<EPI, ACT_GELU, TOK, FEAT, MODE>(a, s);
+  if (a.act == ACT_RELU) return launch_big<EPI, ACT_RELU, TOK, FEAT, MODE>(a, s);
+  return launch_big<EPI, ACT_NONE, TOK, FEAT, MODE>(a, s);
+}
+
+hipError_t launch_bf16_big(const GemmArgs& g, hipStream_t s) {
+  BigArgs a{};
+  a.tok = static_cast<const bf16*>(g.X);
+  a.feat = static_cast<const bf16*>(g.W);
+  a.bias = static_cast<const bf16*>(g.bias);
+  a.S = nullptr;
+  a.Y = static_cast<bf16*>(g.Y);
+  a.Apre = static_cast<bf16*>(g.Apre);
+  a.offset = g.offset;
+  a.max_rows = g.max_rows;
+  a.tok_ld = g.K;
+  a.feat_ld = g.K;
+  a.feat_estride = (int64_t)g.N * g.K;
+  a.y_ld = g.N;
+  a.y_estride = 0;
+  a.E = g.E;
+  a.N = g.N;
+  a.K = g.K;
+  a.M = 0;
+  a.act = g.act;
+  return launch_big_act<BE_ACT, OP_KC, OP_KC, BM_ROWS>(a, s);
 }
 
 }  // namespace
+
+// The four GEMMs of the expert backward on the large-tile kernel (transposed
+// operands read with ds_read_b64_tr_b16), or hipErrorNotSupported when the
+// shapes do not fit it: both dims multiples of 64, every per-launch byte
+// offset below 2^31.
+hipError_t launch_backward_big(const GemmBwdArgs& g, hipStream_t s) {
+  const int64_t d = g.d, h = g.h;
+  if (d % 64 != 0 || h % 64 != 0) return hipErrorNotSupported;
+  const int64_t lim = int64_t(1) << 31;
+  if (d * h * 2 >= lim || (g.max_rows + 64) * std::max(d, h) * 2 >= lim || 256 * std::max(d, h) * 2 >= lim)
+    return hipErrorNotSupported;
+  if (g.max_rows <= 0) return hipSuccess;
+  hipError_t e;
+  const bf16* X = static_cast<const bf16*>(g.X);
+  const bf16* dY = static_cast<const bf16*>(g.dY);
+  bf16* dA = static_cast<bf16*>(g.dA);
+  BigArgs a{};
+  a.offset = g.offset;
+  a.max_rows = g.max_rows;
+  a.E = g.E;
+  a.bias = nullptr;
+  a.Apre = nullptr;
+
+  // dA = (dY · W2[e]) ⊙ act'(A): token rows, K = d; W2[e] is [d, h] = [K, N]
+  a.tok = dY; a.tok_ld = d;
+  a.feat = static_cast<const bf16*>(g.W2); a.feat_ld = h; a.feat_estride = d * h;
+  a.S = static_cast<const bf16*>(g.A);
+  a.Y = dA; a.y_ld = h; a.y_estride = 0;
+  a.N = (int)h; a.K = (int)d; a.M = 0; a.act = g.act;
+  if ((e = launch_big_act<BE_DACT, OP_KC, OP_TR, BM_ROWS>(a, s)) != hipSuccess) return e;
+
+  // dX = dA · W1[e]: token rows, K = h; W1[e] is [h, d] = [K, N]
+  a.tok = dA; a.tok_ld = h;
+  a.feat = static_cast<const bf16*>(g.W1); a.feat_ld = d; a.feat_estride = h * d;
+  a.S = nullptr;
+  a.Y = static_cast<bf16*>(g.dX); a.y_ld = d;
+  a.N = (int)d; a.K = (int)h; a.act = ACT_NONE;
+  if ((e = launch_big<BE_STORE, ACT_NONE, OP_KC, OP_TR, BM_ROWS>(a, s)) != hipSuccess) return e;
+
+  // dW2[e] = dY^T · H, [d, h]: K = the expert's rows
+  a.tok = dY; a.tok_ld = d;
+  a.feat = static_cast<const bf16*>(g.H); a.feat_ld = h; a.feat_estride = 0;
+  a.Y = static_cast<bf16*>(g.dW2); a.y_ld = h; a.y_estride = d * h;
+  a.N = (int)h; a.M = (int)d; a.K = 0;
+  if ((e = launch_big<BE_STORE, ACT_NONE, OP_TR, OP_TR, BM_WGRAD>(a, s)) != hipSuccess) return e;
+  hipLaunchKernelGGL(zero_empty_experts_kernel, dim3(64, g.E), dim3(256), 0, s, a.Y, g.offset, d * h);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+
+  // dW1[e] = dA^T · X, [h, d]
+  a.tok = dA; a.tok_ld = h;
+  a.feat = X; a.feat_ld = d;
+  a.Y = static_cast<bf16*>(g.dW1); a.y_ld = d; a.y_estride = h * d;
+  a.N = (int)d; a.M = (int)h;
+  if ((e = launch_big<BE_STORE, ACT_NONE, OP_TR, OP_TR, BM_WGRAD>(a, s)) != hipSuccess) return e;
+  hipLaunchKernelGGL(zero_empty_experts_kernel, dim3(64, g.E), dim3(256), 0, s, a.Y, g.offset, h * d);
+  return hipGetLastError();
+}
 
 hipError_t launch_grouped_gemm(const GemmArgs& a, int dtype, hipStream_t s) {
   if (a.max_rows <= 0) return hipSuccess;

@@ -103,5 +103,7 @@ struct GemmBwdArgs {
   int32_t E, d, h, act;
 };
 hipError_t launch_ffn_backward(const GemmBwdArgs& a, int dtype, hipStream_t s);
+// The four backward GEMMs on the large-tile kernel, or hipErrorNotSupported.
+hipError_t launch_backward_big(const GemmBwdArgs& a, hipStream_t s);
 
 }  // namespace moe
