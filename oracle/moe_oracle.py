@@ -368,7 +368,8 @@ def expert_ffn_backward(x_disp, offset, w1, w2, a_save, h, dy, act, dtype):
     Per expert, with rows X, saved pre-activation A and H = act(A):
       dH = dY W2;  dA = dH * act'(A) (stored as ``dtype``);  dX = dA W1;
       dW2 = dY^T H;  dW1 = dA^T X;  db2 = colsum dY;  db1 = colsum dA.
-    Returns (dx, dw1, db1, dw2, db2); dx/dW stored as ``dtype``, biases f32.
+    Returns (dx, dw1, db1, dw2, db2); dx/dW stored as ``dtype``, biases f32
+    (unrounded in the float64 mode).
     """
     x_disp = np.asarray(x_disp, np.float64)
     dy = np.asarray(dy, np.float64)
@@ -400,6 +401,130 @@ def expert_ffn_backward(x_disp, offset, w1, w2, a_save, h, dy, act, dtype):
         dx[r0:r1] = store(dA @ W1, dtype)
         dw2[e] = store(dY.T @ H, dtype)
         dw1[e] = store(dA.T @ X, dtype)
-        db2[e] = store(dY.sum(axis=0), "f32")
-        db1[e] = store(dA.sum(axis=0), "f32")
+        db2[e] = store(dY.sum(axis=0), _f32_or_f64(dtype))
+        db1[e] = store(dA.sum(axis=0), _f32_or_f64(dtype))
     return dx, dw1, db1, dw2, db2
+
+
+# --------------------------------------------------------------------------
+# backward of the whole layer (chain rule through combine, the expert FFNs,
+# dispatch, the gate weights, softmax and the router Linear)
+#
+# Reading R13: the top-k choice and the capacity slots are piecewise constant
+# in the inputs, so they pass no gradient: the top-k operation passes its
+# gradient only to the chosen positions ([DS-MoE-traps] ch.3 §3.1, the
+# TopKRouter backward) and experts without tokens get none (ch.2 §2.1, the
+# gradient mask); the chosen values then reach all logits through the
+# softmax over the experts (R1).  The gradient of gate_loss is taken through
+# its probability term only (the counts are integers).  Precisions as the HIP
+# path stores them: dY_disp (= w * dOut) as ``dtype``, the per-choice weight
+# gradients and logit gradients in f32, dX stored once as ``dtype`` after
+# summing the expert rows and the router term, router weight and bias
+# gradients in f32 (nothing is rounded in the float64 mode, dtype "f64").
+# --------------------------------------------------------------------------
+def combine_backward(dout, y_disp, idx, slot, weight, offset, dtype):
+    """Backward of ``combine``: for each kept claim (t, j) at packed row r,
+    dY_disp[r] = w[t,j] * dOut[t] and dw[t,j] = <dOut[t], y_disp[r]>;
+    dropped claims get dw = 0 and own no row."""
+    dout = np.asarray(dout, np.float64)
+    y_disp = np.asarray(y_disp, np.float64)
+    T, k = idx.shape
+    dy = np.zeros_like(y_disp)
+    dw = np.zeros((T, k))
+    for t in range(T):
+        for j in range(k):
+            s = slot[t, j]
+            if s >= 0:
+                r = offset[idx[t, j]] + s
+                dy[r] = weight[t, j] * dout[t]
+                dw[t, j] = float(dout[t] @ y_disp[r])
+    return store(dy, dtype), store(dw, _f32_or_f64(dtype))
+
+
+def _f32_or_f64(dtype):
+    """The f32 intermediates of the backward, left unrounded in the pure
+    float64 mode (dtype "f64") used by the mathematical pins."""
+    return "f64" if dtype == "f64" else "f32"
+
+
+def dispatch_backward(dx_disp, idx, slot, offset, num_tokens):
+    """Backward of ``dispatch``: token t's input gradient is the sum over its
+    kept claims (in choice order) of the rows they were copied to."""
+    dx_disp = np.asarray(dx_disp, np.float64)
+    dx = np.zeros((num_tokens, dx_disp.shape[1]))
+    T, k = idx.shape
+    for t in range(T):
+        for j in range(k):
+            s = slot[t, j]
+            if s >= 0:
+                dx[t] += dx_disp[offset[idx[t, j]] + s]
+    return dx
+
+
+def gate_backward(probs, idx, dw, normalize_topk, loss_kind, dloss, dtype="f32"):
+    """Gradient of the router logits from the weight gradients dw [T, k] and
+    the upstream gradient dloss of gate_loss.
+
+    Weights: w_j = p[t, e_j], or w_j = p_j / S with S = sum_j p[t, e_j]
+    (normalize_topk), whose derivative gives dp[t, e_i] += (dw_i - sum_j
+    dw_j w_j) / S.  BALANCE loss E * sum_e mean_t(p[t,e]) * ce_e adds
+    dloss * E * ce_e / T to every dp[t, e] (ce_e = share of top-1 choices);
+    USAGE_STD depends on counts only.  Then the softmax backward
+    dlogits = p * (dp - <p, dp>) per token.
+    """
+    p = np.asarray(probs, np.float64)
+    T, E = p.shape
+    k = idx.shape[1]
+    dw = np.asarray(dw, np.float64)
+    dp = np.zeros((T, E))
+    for t in range(T):
+        pe = [p[t, idx[t, j]] for j in range(k)]
+        if normalize_topk:
+            S = sum(pe)
+            w = [v / S for v in pe]
+            corr = sum(dw[t, j] * w[j] for j in range(k))
+            for i in range(k):
+                dp[t, idx[t, i]] += (dw[t, i] - corr) / S
+        else:
+            for j in range(k):
+                dp[t, idx[t, j]] += dw[t, j]
+    if T > 0 and loss_kind == LOSS_BALANCE:
+        ce = np.bincount(idx[:, 0], minlength=E) / T
+        dp += dloss * E * ce[None, :] / T
+    dl = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+    return store(dl, _f32_or_f64(dtype))
+
+
+def router_backward(x, w_router, dlogits):
+    """Backward of ``router_logits``: dx = dlogits W_r, dW_r = dlogits^T x,
+    db_r = column sums of dlogits (all float64)."""
+    x = np.asarray(x, np.float64)
+    dl = np.asarray(dlogits, np.float64)
+    wr = np.asarray(w_router, np.float64)
+    return dl @ wr, dl.T @ x, dl.sum(axis=0)
+
+
+def layer_backward(x, w_router, r, w1, w2, dout, dloss, *, act, dtype,
+                   normalize_topk=False, loss_kind=LOSS_BALANCE):
+    """Gradients of <dOut, out> + dloss * gate_loss for the layer whose
+    forward ``r`` is (``layer_forward``'s result, with ``probs`` from the
+    same logits).  ``w_router`` None means the logits were inputs: the
+    logit gradient is returned instead of router gradients.
+
+    Returns a dict: dx (stored ``dtype``), dlogits (f32), dw_router, db_router
+    (f32, or None), dw1, db1, dw2, db2 (as ``expert_ffn_backward``), and the
+    intermediates dy_disp, dw_gate, dx_disp.
+    """
+    T = np.asarray(x).shape[0]
+    idx, slot, off = r["expert_idx"], r["slot"], r["expert_offset"]
+    dy, dwg = combine_backward(dout, r["y_disp"], idx, slot, r["weight"], off, dtype)
+    dxd, dw1, db1, dw2, db2 = expert_ffn_backward(r["x_disp"], off, w1, w2, r["a"], r["h"], dy, act, dtype)
+    dx = dispatch_backward(dxd, idx, slot, off, T)
+    dl = gate_backward(r["probs"], idx, dwg, normalize_topk, loss_kind, dloss, dtype)
+    dwr = dbr = None
+    if w_router is not None:
+        dxr, dwr, dbr = router_backward(x, w_router, dl)
+        dx = dx + dxr
+        dwr, dbr = store(dwr, _f32_or_f64(dtype)), store(dbr, _f32_or_f64(dtype))
+    return dict(dx=store(dx, dtype), dlogits=dl, dw_router=dwr, db_router=dbr,
+                dw1=dw1, db1=db1, dw2=dw2, db2=db2, dy_disp=dy, dw_gate=dwg, dx_disp=dxd)
