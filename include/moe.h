@@ -1,7 +1,7 @@
 /*
  * moe.h - C ABI of a top-k gated Mixture-of-Experts layer for one MI355X
  * (gfx950) GPU: gate, dispatch, expert FFNs, combine, the fused layer
- * forward, and the backward of the expert FFNs.
+ * forward, and the backward of every step and of the whole layer.
  *
  * What the calls compute follows these pages (cited by title and section):
  *   [ds.moe]     "deepspeed.moe 模块" overview (adg.csdn.net): §2.1 the MoE
@@ -15,7 +15,10 @@
  *                gather and weighted sum) and the capacity / drop-tokens items.
  *   [DS-MoE-traps] DeepSeek-MoE fine-tuning article (lnwmold.com), ch.1:
  *                softmax over the router logits, top-2 on it, weighted sum;
- *                the capacity formula and the usage-std balance loss.
+ *                the capacity formula and the usage-std balance loss;
+ *                ch.2 §2.1 the gradient mask (experts without tokens get no
+ *                gradient) and ch.3 §3.1 the TopKRouter backward (the top-k
+ *                selection passes gradient only to the chosen positions).
  *
  * Conventions for every call
  *  - Pointers named as device pointers must point to GPU memory of the
@@ -93,9 +96,11 @@ typedef struct moe_config {
                               softmax over the top-k logits ([MoE-sched] §3.1
                               Step 2).  Computed before any drop.              */
   int32_t loss_kind;       /* moe_loss_kind                                     */
-  int32_t save_preact;     /* 1: moe_layer_forward keeps the pre-activation
-                              of the first Linear in the workspace for
-                              moe_expert_ffn_backward                          */
+  int32_t save_preact;     /* 1 (training): moe_layer_forward keeps in the
+                              workspace what the backward needs (the first
+                              Linear's pre-activation, and the logits when
+                              logits_out is NULL), and the workspace has the
+                              regions the *_backward calls below use          */
 } moe_config;
 
 /* Static text for a status code. */
@@ -163,6 +168,8 @@ moe_status moe_expert_ffn(const moe_config* cfg, const void* x_disp, const int32
                           void* ws, size_t ws_bytes, void* stream);
 
 /* Backward of the expert FFNs for an upstream gradient dy_disp [rows, d]
+ * (dx_disp may be the same buffer as dy_disp: dY's last read precedes the
+ * first write of dX)
  * (chain rule of Linear-act-Linear, per expert e on its packed rows):
  *   dh = dy·w2[e];  da = dh ⊙ act'(a_save)  (stored as dtype);
  *   dx = da·w1[e];  dw2[e] = dy^T·h;  dw1[e] = da^T·x;
@@ -200,6 +207,89 @@ moe_status moe_layer_forward(const moe_config* cfg, const void* x, const void* w
                              void* out, float* gate_loss, int32_t* expert_count,
                              float* logits_out, int32_t* expert_idx, int32_t* slot,
                              float* weight, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Backward of the layer.  Gradients follow the chain rule through the
+ * forward above; the top-k choice and the capacity slots are piecewise
+ * constant and pass no gradient ([DS-MoE-traps] ch.3 §3.1 TopKRouter
+ * backward, ch.2 §2.1 gradient mask); the chosen probabilities reach every
+ * logit through the softmax.  bf16 only for the calls that run GEMMs.
+ * Those that take ws need a config with save_preact = 1 (else
+ * MOE_ERR_INVALID_ARG) and ws of moe_workspace_size() bytes.
+ * ------------------------------------------------------------------------ */
+
+/* Backward of moe_combine: for every kept claim (t, j) at packed row
+ * r = expert_offset[e] + slot[t,j]:
+ *   dy_disp[r]    = weight[t,j] * dout[t]   (fp32 product, stored as dtype)
+ *   dweight[t,j]  = <dout[t], y_disp[r]>    (fp32 accumulation)
+ * and dweight = 0 for dropped claims.  dout device [T, d] dtype; y_disp and
+ * dy_disp device [rows, d] dtype and MAY BE THE SAME BUFFER (each row is
+ * read, then overwritten, by the one wavefront that owns its claim);
+ * dweight device [T, k] fp32. */
+moe_status moe_combine_backward(const moe_config* cfg, const void* dout, const void* y_disp,
+                                const int32_t* expert_idx, const int32_t* slot, const float* weight,
+                                const int32_t* expert_offset, void* dy_disp, float* dweight, void* stream);
+
+/* Logit gradient of the gate ([MoE-sched] §3.1 Step 2; [ds.moe] §3.1 step 5):
+ * p = softmax(logits[t]);  dp[e_j] += dweight[t,j] (when normalize_topk,
+ * w_j = p_j / S with S the sum of the k chosen p, so dp[e_i] +=
+ * (dweight_i - sum_j dweight_j w_j) / S);  BALANCE loss: dp[e] +=
+ * dloss * E * ce_e / T, ce_e the share of tokens whose top-1 is e
+ * (USAGE_STD depends on counts only and adds nothing);
+ * dlogits[t] = p * (dp - <p, dp>), all fp32.
+ *   logits   device [T, E] fp32: the logits the forward used
+ *   dweight  device [T, k] fp32 (from moe_combine_backward)
+ *   dloss    device [1] fp32, the upstream gradient of gate_loss; NULL = 0
+ *   dlogits  device [T, E] fp32 out */
+moe_status moe_gate_backward(const moe_config* cfg, const float* logits, const int32_t* expert_idx,
+                             const float* dweight, const float* dloss, float* dlogits, void* ws,
+                             size_t ws_bytes, void* stream);
+
+/* Backward of moe_dispatch plus, when w_router is non-NULL, the router
+ * Linear's input gradient ([MoE-sched] §3.1 Steps 1 and 3):
+ *   dx[t] = sum over kept j (choice order) of dx_disp[row(t,j)]
+ *           + dlogits[t] · w_router            (fp32, one rounding to bf16)
+ * The router product runs on bf16 matrix cores with dlogits split into two
+ * bf16 terms (|error| <= 2^-16 |dlogits| per element before the fp32 sum).
+ * A token with every claim dropped gets the router term only.
+ *   dx_disp device [rows, d] bf16;  w_router device [E, d] bf16, nullable;
+ *   dlogits device [T, E] fp32 (needed with w_router);  dx device [T, d] bf16.
+ * MOE_ERR_UNSUPPORTED unless bf16 and d % 32 == 0. */
+moe_status moe_dispatch_backward(const moe_config* cfg, const void* dx_disp, const int32_t* expert_idx,
+                                 const int32_t* slot, const int32_t* expert_offset, const void* w_router,
+                                 const float* dlogits, void* dx, void* ws, size_t ws_bytes, void* stream);
+
+/* Router weight gradients ([MoE-sched] §3.1 Step 1, the router Linear):
+ *   dw_router[e, :] = sum_t dlogits[t, e] * x[t, :]   fp32 [E, d], nullable
+ *   db_router[e]    = sum_t dlogits[t, e]              fp32 [E], nullable
+ * (at least one non-NULL).  x device [T, d] bf16.  Token chunks are summed
+ * in a fixed order, so results are bit-identical run to run.
+ * MOE_ERR_UNSUPPORTED unless bf16 and d % 64 == 0 (for dw_router). */
+moe_status moe_router_backward(const moe_config* cfg, const void* x, const float* dlogits,
+                               float* dw_router, float* db_router, void* ws, size_t ws_bytes,
+                               void* stream);
+
+/* The whole layer backward on one stream, after moe_layer_forward with the
+ * same cfg (save_preact = 1, ffn_hidden > 0, bf16) and the same ws, whose
+ * intermediates it consumes (afterwards ws's y_disp region holds dX_disp):
+ *   moe_combine_backward -> moe_expert_ffn_backward -> moe_gate_backward ->
+ *   moe_dispatch_backward (with the router input term) -> moe_router_backward.
+ * Gradients of <dout, out> + dloss * gate_loss with respect to:
+ *   dx [T, d] bf16;  dlogits [T, E] fp32 (nullable when w_router is given;
+ *   required when the forward took logits_in, i.e. w_router == NULL);
+ *   dw_router [E, d] fp32, db_router [E] fp32 (nullable; need w_router);
+ *   dw1 [E, h, d], dw2 [E, d, h] bf16; db1 [E, h], db2 [E, d] fp32 (nullable).
+ * logits, expert_idx, slot, weight: what the forward wrote, or NULL if the
+ * forward kept them in ws (logits_out / expert_idx / slot / weight NULL).
+ * x, w_router, w1, w2 as in moe_layer_forward; dout device [T, d] bf16;
+ * dloss device [1] fp32 or NULL (= 0).  MOE_ERR_UNSUPPORTED unless d is a
+ * multiple of 32 (64 with dw_router) and h of 16. */
+moe_status moe_layer_backward(const moe_config* cfg, const void* x, const void* w_router, const void* w1,
+                              const void* w2, const float* logits, const int32_t* expert_idx,
+                              const int32_t* slot, const float* weight, const void* dout,
+                              const float* dloss, void* dx, float* dlogits, float* dw_router,
+                              float* db_router, void* dw1, float* db1, void* dw2, float* db2, void* ws,
+                              size_t ws_bytes, void* stream);
 
 /* Device addresses, inside a workspace ws, of the intermediates that
  * moe_layer_forward leaves there (valid until the next call that uses ws):

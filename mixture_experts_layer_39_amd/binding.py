@@ -22,7 +22,8 @@ MOE_MAX_EXPERTS = 256
 
 EXPORTED = ("moe_status_string", "moe_capacity", "moe_max_rows", "moe_workspace_size", "moe_gate",
             "moe_dispatch", "moe_expert_ffn", "moe_expert_ffn_backward", "moe_combine",
-            "moe_layer_forward", "moe_workspace_views")
+            "moe_layer_forward", "moe_workspace_views", "moe_combine_backward", "moe_gate_backward",
+            "moe_dispatch_backward", "moe_router_backward", "moe_layer_backward")
 
 
 class MoeConfig(ctypes.Structure):
@@ -81,6 +82,11 @@ def lib():
         L.moe_combine.argtypes = [CFG] + [P] * 6 + [P]
         L.moe_layer_forward.argtypes = [CFG] + [P] * 15 + [P, S, P]
         L.moe_workspace_views.argtypes = [CFG, P] + [ctypes.POINTER(P)] * 5
+        L.moe_combine_backward.argtypes = [CFG] + [P] * 8 + [P]
+        L.moe_gate_backward.argtypes = [CFG] + [P] * 5 + [P, S, P]
+        L.moe_dispatch_backward.argtypes = [CFG] + [P] * 7 + [P, S, P]
+        L.moe_router_backward.argtypes = [CFG] + [P] * 4 + [P, S, P]
+        L.moe_layer_backward.argtypes = [CFG] + [P] * 18 + [P, S, P]
         for name in EXPORTED:
             if name != "moe_status_string":
                 getattr(L, name).restype = ctypes.c_int
@@ -180,3 +186,38 @@ def moe_layer_forward(cfg, x, w_router, b_router, logits_in, w1, b1, w2, b2, out
                                    _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2), _ptr(out), _ptr(gate_loss),
                                    _ptr(expert_count), _ptr(logits_out), _ptr(expert_idx), _ptr(slot),
                                    _ptr(weight), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def _nbytes(ws):
+    return 0 if ws is None else ws.numel() * ws.element_size()
+
+
+def moe_combine_backward(cfg, dout, y_disp, expert_idx, slot, weight, expert_offset, dy_disp, dweight, stream=None):
+    _check(lib().moe_combine_backward(ctypes.byref(cfg), _ptr(dout), _ptr(y_disp), _ptr(expert_idx), _ptr(slot),
+                                      _ptr(weight), _ptr(expert_offset), _ptr(dy_disp), _ptr(dweight),
+                                      _stream(stream)))
+
+
+def moe_gate_backward(cfg, logits, expert_idx, dweight, dloss, dlogits, ws, stream=None):
+    _check(lib().moe_gate_backward(ctypes.byref(cfg), _ptr(logits), _ptr(expert_idx), _ptr(dweight), _ptr(dloss),
+                                   _ptr(dlogits), _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def moe_dispatch_backward(cfg, dx_disp, expert_idx, slot, expert_offset, w_router, dlogits, dx, ws, stream=None):
+    _check(lib().moe_dispatch_backward(ctypes.byref(cfg), _ptr(dx_disp), _ptr(expert_idx), _ptr(slot),
+                                       _ptr(expert_offset), _ptr(w_router), _ptr(dlogits), _ptr(dx), _ptr(ws),
+                                       _nbytes(ws), _stream(stream)))
+
+
+def moe_router_backward(cfg, x, dlogits, dw_router, db_router, ws, stream=None):
+    _check(lib().moe_router_backward(ctypes.byref(cfg), _ptr(x), _ptr(dlogits), _ptr(dw_router), _ptr(db_router),
+                                     _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def moe_layer_backward(cfg, x, w_router, w1, w2, dout, dloss, dx, dw1, dw2, *, logits=None, expert_idx=None,
+                       slot=None, weight=None, dlogits=None, dw_router=None, db_router=None, db1=None, db2=None,
+                       ws=None, stream=None):
+    _check(lib().moe_layer_backward(ctypes.byref(cfg), _ptr(x), _ptr(w_router), _ptr(w1), _ptr(w2), _ptr(logits),
+                                    _ptr(expert_idx), _ptr(slot), _ptr(weight), _ptr(dout), _ptr(dloss), _ptr(dx),
+                                    _ptr(dlogits), _ptr(dw_router), _ptr(db_router), _ptr(dw1), _ptr(db1),
+                                    _ptr(dw2), _ptr(db2), _ptr(ws), _nbytes(ws), _stream(stream)))

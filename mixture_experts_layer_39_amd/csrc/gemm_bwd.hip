@@ -375,7 +375,6 @@ hipError_t launch(const BwdGemm& g, hipStream_t s) {
 
 hipError_t launch_ffn_backward(const GemmBwdArgs& a, int dtype, hipStream_t s) {
   if (dtype != DT_BF16) return hipErrorNotSupported;
-  if (a.max_rows <= 0) return hipSuccess;
   const bf16* X = static_cast<const bf16*>(a.X);
   const bf16* W1 = static_cast<const bf16*>(a.W1);
   const bf16* W2 = static_cast<const bf16*>(a.W2);
@@ -385,6 +384,20 @@ hipError_t launch_ffn_backward(const GemmBwdArgs& a, int dtype, hipStream_t s) {
   bf16* dA = static_cast<bf16*>(a.dA);
   const int d = a.d, h = a.h;
   hipError_t err;
+  if (a.max_rows <= 0) {
+    // no rows at all: every gradient is zero
+    if ((err = launch_zero_bytes(a.dW1, (size_t)a.E * h * d * 2, s)) != hipSuccess) return err;
+    if ((err = launch_zero_bytes(a.dW2, (size_t)a.E * d * h * 2, s)) != hipSuccess) return err;
+    if (a.db1 && (err = launch_zero_bytes(a.db1, (size_t)a.E * h * 4, s)) != hipSuccess) return err;
+    if (a.db2 && (err = launch_zero_bytes(a.db2, (size_t)a.E * d * 4, s)) != hipSuccess) return err;
+    return hipSuccess;
+  }
+  // Order: db2 and dW2 are the last reads of dY, before dX is written, so
+  // that dX may take dY's memory.
+  if (a.db2) {
+    hipLaunchKernelGGL(colsum_kernel, dim3((d + 255) / 256, a.E), dim3(256), 0, s, dY, a.offset, a.db2, d);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
   BwdGemm g{};
   g.offset = a.offset;
   g.E = a.E;
@@ -402,32 +415,28 @@ hipError_t launch_ffn_backward(const GemmBwdArgs& a, int dtype, hipStream_t s) {
   g.nrows = h; g.kdim = d;
   if ((err = launch<L_RC, L_KC, M_ROWS, EPI_DACT>(g, s)) != hipSuccess) return err;
 
-  // dX = dA · W1[e]: rows = d (W1[e] row-contiguous along d), K = h
-  g.A = W1; g.a_estride = (int64_t)h * d; g.lda = d;
-  g.B = dA; g.ldb = h;
-  g.Y = static_cast<bf16*>(a.dX); g.S = nullptr; g.ldy = d;
-  g.nrows = d; g.kdim = h;
-  if ((err = launch<L_RC, L_KC, M_ROWS, EPI_STORE>(g, s)) != hipSuccess) return err;
-
   // dW2[e][d][h] = dY^T · H: rows = h (from H), columns = d (from dY), K = rows of e
   g.A = H; g.a_estride = 0; g.lda = h;
   g.B = dY; g.ldb = d;
-  g.Y = static_cast<bf16*>(a.dW2); g.ldy = h;
+  g.Y = static_cast<bf16*>(a.dW2); g.S = nullptr; g.ldy = h;
   g.nrows = h; g.ncols = d;
   if ((err = launch<L_RC, L_RC, M_WGRAD, EPI_STORE>(g, s)) != hipSuccess) return err;
 
+  // dX = dA · W1[e]: rows = d (W1[e] row-contiguous along d), K = h
+  g.A = W1; g.a_estride = (int64_t)h * d; g.lda = d;
+  g.B = dA; g.ldb = h;
+  g.Y = static_cast<bf16*>(a.dX); g.ldy = d;
+  g.nrows = d; g.kdim = h;
+  if ((err = launch<L_RC, L_KC, M_ROWS, EPI_STORE>(g, s)) != hipSuccess) return err;
+
   // dW1[e][h][d] = dA^T · X: rows = d (from X), columns = h (from dA)
-  g.A = X; g.lda = d;
+  g.A = X; g.a_estride = 0; g.lda = d;
   g.B = dA; g.ldb = h;
   g.Y = static_cast<bf16*>(a.dW1); g.ldy = d;
   g.nrows = d; g.ncols = h;
   if ((err = launch<L_RC, L_RC, M_WGRAD, EPI_STORE>(g, s)) != hipSuccess) return err;
   }
 
-  if (a.db2) {
-    hipLaunchKernelGGL(colsum_kernel, dim3((d + 255) / 256, a.E), dim3(256), 0, s, dY, a.offset, a.db2, d);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-  }
   if (a.db1) {
     hipLaunchKernelGGL(colsum_kernel, dim3((h + 255) / 256, a.E), dim3(256), 0, s, (const bf16*)dA, a.offset, a.db1, h);
     if ((err = hipGetLastError()) != hipSuccess) return err;

@@ -339,7 +339,7 @@ constexpr int TRB = 512;                       // bytes of one K row of a transp
 
 enum { OP_KC = 0, OP_TR = 1 };          // operand layout
 enum { BM_ROWS = 0, BM_WGRAD = 1 };     // token-row tiles / weight-gradient tiles
-enum { BE_ACT = 0, BE_DACT = 1, BE_STORE = 2 };   // epilogue
+enum { BE_ACT = 0, BE_DACT = 1, BE_STORE = 2, BE_F32 = 3 };   // epilogue
 
 struct BigArgs {
   const bf16* tok;          // token-side operand
@@ -347,6 +347,7 @@ struct BigArgs {
   const bf16* bias;         // BE_ACT: [E, N] or null
   const bf16* S;            // BE_DACT: pre-activation [rows, N]
   bf16* Y;                  // output
+  float* Yf;                // BE_F32: fp32 output
   bf16* Apre;               // BE_ACT: pre-activation output [rows, N] or null
   const int32_t* offset;    // [E+1]
   int64_t max_rows;         // upper bound on offset[E]
@@ -553,6 +554,7 @@ __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u 
 //  BE_ACT:   + bias (from LDS), optional pre-activation store, activation.
 //  BE_DACT:  times act'(S) at the same position.
 //  BE_STORE: as is.
+//  BE_F32:   as is, in fp32 (four 16-byte vectors).
 template <int EPI, int ACT, int MODE>
 __device__ __forceinline__ void big_store(const BigArgs& a, float (&v)[16], const BigTile& t, int rloc, int fl,
                                           const float* s_bias) {
@@ -583,6 +585,12 @@ __device__ __forceinline__ void big_store(const BigArgs& a, float (&v)[16], cons
         v[2 * q + 1] *= act_grad_fixed<ACT>(bf16_hi(sw[q]));
       }
     }
+  }
+  if constexpr (EPI == BE_F32) {
+    float4* q = reinterpret_cast<float4*>(a.Yf + off);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) q[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+    return;
   }
   uint4* p = reinterpret_cast<uint4*>(a.Y + off);
   p[0] = make_uint4(pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7]));
@@ -981,31 +989,56 @@ hipError_t launch_backward_big(const GemmBwdArgs& g, hipStream_t s) {
   a.N = (int)h; a.K = (int)d; a.M = 0; a.act = g.act;
   if ((e = launch_big_act<BE_DACT, OP_KC, OP_TR, BM_ROWS>(a, s)) != hipSuccess) return e;
 
-  // dX = dA · W1[e]: token rows, K = h; W1[e] is [h, d] = [K, N]
-  a.tok = dA; a.tok_ld = h;
-  a.feat = static_cast<const bf16*>(g.W1); a.feat_ld = d; a.feat_estride = h * d;
-  a.S = nullptr;
-  a.Y = static_cast<bf16*>(g.dX); a.y_ld = d;
-  a.N = (int)d; a.K = (int)h; a.act = ACT_NONE;
-  if ((e = launch_big<BE_STORE, ACT_NONE, OP_KC, OP_TR, BM_ROWS>(a, s)) != hipSuccess) return e;
-
-  // dW2[e] = dY^T · H, [d, h]: K = the expert's rows
+  // dW2[e] = dY^T · H, [d, h]: K = the expert's rows (the last use of dY)
   a.tok = dY; a.tok_ld = d;
   a.feat = static_cast<const bf16*>(g.H); a.feat_ld = h; a.feat_estride = 0;
+  a.S = nullptr;
   a.Y = static_cast<bf16*>(g.dW2); a.y_ld = h; a.y_estride = d * h;
-  a.N = (int)h; a.M = (int)d; a.K = 0;
+  a.N = (int)h; a.M = (int)d; a.K = 0; a.act = ACT_NONE;
   if ((e = launch_big<BE_STORE, ACT_NONE, OP_TR, OP_TR, BM_WGRAD>(a, s)) != hipSuccess) return e;
   hipLaunchKernelGGL(zero_empty_experts_kernel, dim3(64, g.E), dim3(256), 0, s, a.Y, g.offset, d * h);
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
+  // dX = dA · W1[e]: token rows, K = h; W1[e] is [h, d] = [K, N] (dX may overwrite dY)
+  a.tok = dA; a.tok_ld = h;
+  a.feat = static_cast<const bf16*>(g.W1); a.feat_ld = d; a.feat_estride = h * d;
+  a.Y = static_cast<bf16*>(g.dX); a.y_ld = d; a.y_estride = 0;
+  a.N = (int)d; a.K = (int)h; a.M = 0;
+  if ((e = launch_big<BE_STORE, ACT_NONE, OP_KC, OP_TR, BM_ROWS>(a, s)) != hipSuccess) return e;
+
   // dW1[e] = dA^T · X, [h, d]
   a.tok = dA; a.tok_ld = h;
-  a.feat = X; a.feat_ld = d;
+  a.feat = X; a.feat_ld = d; a.feat_estride = 0;
   a.Y = static_cast<bf16*>(g.dW1); a.y_ld = d; a.y_estride = h * d;
-  a.N = (int)d; a.M = (int)h;
+  a.N = (int)d; a.M = (int)h; a.K = 0;
   if ((e = launch_big<BE_STORE, ACT_NONE, OP_TR, OP_TR, BM_WGRAD>(a, s)) != hipSuccess) return e;
   hipLaunchKernelGGL(zero_empty_experts_kernel, dim3(64, g.E), dim3(256), 0, s, a.Y, g.offset, h * d);
   return hipGetLastError();
+}
+
+// Chunked router weight gradient: part[c] = dl_hl[rows of chunk c]^T x[rows
+// of chunk c], [2*Ep, d] fp32 per chunk, on the weight-gradient tiles with
+// the chunks in the role of experts (choff holds their row offsets).
+hipError_t launch_router_partials(const uint16_t* dl_hl, const void* x, const int32_t* choff, float* part,
+                                  int64_t T, int S, int d, int Ep, hipStream_t s) {
+  if (d % 64 != 0 || S < 1 || S > MOE_MAX_EXPERTS_DEV) return hipErrorNotSupported;
+  BigArgs a{};
+  a.tok = reinterpret_cast<const bf16*>(dl_hl);
+  a.tok_ld = 2 * Ep;
+  a.feat = static_cast<const bf16*>(x);
+  a.feat_ld = d;
+  a.feat_estride = 0;
+  a.Yf = part;
+  a.y_ld = d;
+  a.y_estride = (int64_t)2 * Ep * d;
+  a.offset = choff;
+  a.max_rows = T;
+  a.E = S;
+  a.N = d;
+  a.M = 2 * Ep;
+  a.K = 0;
+  a.act = ACT_NONE;
+  return launch_big<BE_F32, ACT_NONE, OP_TR, OP_TR, BM_WGRAD>(a, s);
 }
 
 hipError_t launch_grouped_gemm(const GemmArgs& a, int dtype, hipStream_t s) {

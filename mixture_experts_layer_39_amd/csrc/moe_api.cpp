@@ -63,6 +63,10 @@ struct Layout {
   int tiles, tile_tokens;
   size_t tile_cnt, me_tile, me_sum, demand, idx, slot, weight, offset;
   size_t x_disp, a_save, h_disp, y_disp, d_act;
+  // backward regions (save_preact == 1 only)
+  int Ep;
+  RouterChunks rc;
+  size_t logits, dwg, dlg, dl_hl, wrT, top1, coef, dbpart, choff, wpart;
   size_t total;
 };
 
@@ -95,6 +99,20 @@ Layout layout_of(const moe_config* c) {
   L.h_disp = take(h > 0 ? (size_t)L.rows * h * s : 0);
   L.y_disp = take((size_t)L.rows * d * s);
   L.d_act = take(h > 0 ? (size_t)L.rows * h * s : 0);
+  const bool train = c->save_preact != 0;
+  L.Ep = router_ep(E);
+  L.rc = train ? router_chunks(L.T, d, E) : RouterChunks{0, 0};
+  const size_t nbt = (size_t)((L.T + kGateBwdTokens - 1) / kGateBwdTokens);
+  L.logits = take(train ? (size_t)L.T * E * 4 : 0);
+  L.dwg = take(train ? (size_t)L.T * k * 4 : 0);
+  L.dlg = take(train ? (size_t)L.T * E * 4 : 0);
+  L.dl_hl = take(train ? (size_t)L.T * 2 * L.Ep * 2 : 0);
+  L.wrT = take(train ? (size_t)d * L.Ep * 2 : 0);
+  L.top1 = take(train ? (size_t)kTop1Parts * E * 4 : 0);
+  L.coef = take(train ? (size_t)E * 4 : 0);
+  L.dbpart = take(train ? nbt * E * 4 : 0);
+  L.choff = take(train ? (size_t)(kRouterMaxChunks + 1) * 4 : 0);
+  L.wpart = take(train ? (size_t)L.rc.S * 2 * L.Ep * d * 4 : 0);
   L.total = off;
   return L;
 }
@@ -347,8 +365,9 @@ moe_status moe_layer_forward(const moe_config* cfg, const void* x, const void* w
   int32_t* sl = slot ? slot : at<int32_t>(ws, L.slot);
   float* wt = weight ? weight : at<float>(ws, L.weight);
   int32_t* off = at<int32_t>(ws, L.offset);
-  st = run_gate(cfg, L, x, w_router, b_router, logits_in, logits_out, idx, sl, wt, expert_count, off, gate_loss, ws,
-                s);
+  // training: the backward needs the logits, so keep them when the caller does not
+  float* lg = (logits_out || !cfg->save_preact) ? logits_out : at<float>(ws, L.logits);
+  st = run_gate(cfg, L, x, w_router, b_router, logits_in, lg, idx, sl, wt, expert_count, off, gate_loss, ws, s);
   if (st != MOE_OK || L.T == 0) return st;
   void* xd = at<void>(ws, L.x_disp);
   void* hd = cfg->ffn_hidden > 0 ? at<void>(ws, L.h_disp) : nullptr;
@@ -358,6 +377,220 @@ moe_status moe_layer_forward(const moe_config* cfg, const void* x, const void* w
   st = run_ffn(cfg, L, xd, off, w1, b1, w2, b2, as, hd, yd, s);
   if (st != MOE_OK) return st;
   MOE_TRY_HIP(launch_combine(yd, idx, sl, wt, off, out, L.T, cfg->k, cfg->hidden_size, cfg->dtype, s));
+  return MOE_OK;
+}
+
+moe_status moe_combine_backward(const moe_config* cfg, const void* dout, const void* y_disp,
+                                const int32_t* expert_idx, const int32_t* slot, const float* weight,
+                                const int32_t* expert_offset, void* dy_disp, float* dweight, void* stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (cfg->num_tokens == 0) return MOE_OK;
+  if (!dout || !y_disp || !expert_idx || !slot || !weight || !expert_offset || !dy_disp || !dweight)
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_combine_backward(dout, y_disp, expert_idx, slot, weight, expert_offset, dy_disp, dweight,
+                                            cfg->num_tokens, cfg->k, cfg->hidden_size, cfg->dtype,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+namespace {
+
+// The logit gradient from the gate-weight gradient (and dloss for BALANCE);
+// optionally also its hi/lo split and column partial sums in the workspace.
+moe_status run_gate_backward(const moe_config* c, const Layout& L, const float* logits, const int32_t* idx,
+                             const float* dw, const float* dloss, float* dlogits, bool split, void* ws,
+                             hipStream_t s) {
+  GateBwdArgs g{};
+  g.logits = logits;
+  g.idx = idx;
+  g.dw = dw;
+  g.coef = nullptr;
+  if (c->loss_kind == MOE_LOSS_BALANCE && dloss) {
+    MOE_TRY_HIP(launch_top1_coef(idx, c->k, L.T, c->num_experts, dloss, at<int32_t>(ws, L.top1),
+                                 at<float>(ws, L.coef), s));
+    g.coef = at<float>(ws, L.coef);
+  }
+  g.dlogits = dlogits;
+  g.dl_hl = split ? at<uint16_t>(ws, L.dl_hl) : nullptr;
+  g.dbpart = split ? at<float>(ws, L.dbpart) : nullptr;
+  g.T = L.T;
+  g.E = c->num_experts;
+  g.k = c->k;
+  g.Ep = L.Ep;
+  g.normalize = c->normalize_topk;
+  MOE_TRY_HIP(launch_gate_backward(g, s));
+  return MOE_OK;
+}
+
+// The hi/lo split and column partial sums of a given logit gradient.
+moe_status run_split(const moe_config* c, const Layout& L, const float* dlogits, void* ws, hipStream_t s) {
+  GateBwdArgs g{};
+  g.dlogits = const_cast<float*>(dlogits);   // read only without logits
+  g.dl_hl = at<uint16_t>(ws, L.dl_hl);
+  g.dbpart = at<float>(ws, L.dbpart);
+  g.T = L.T;
+  g.E = c->num_experts;
+  g.k = c->k;
+  g.Ep = L.Ep;
+  MOE_TRY_HIP(launch_gate_backward(g, s));
+  return MOE_OK;
+}
+
+moe_status run_input_grad(const moe_config* c, const Layout& L, const void* dx_disp, const int32_t* idx,
+                          const int32_t* slot, const int32_t* offset, const void* w_router, void* dx, void* ws,
+                          hipStream_t s) {
+  InputGradArgs g{};
+  g.dx_disp = static_cast<const bf16*>(dx_disp);
+  g.idx = idx;
+  g.slot = slot;
+  g.offset = offset;
+  g.dl_hl = w_router ? at<uint16_t>(ws, L.dl_hl) : nullptr;
+  g.wrT = at<uint16_t>(ws, L.wrT);
+  g.dx = static_cast<bf16*>(dx);
+  g.T = L.T;
+  g.d = c->hidden_size;
+  g.k = c->k;
+  g.Ep = L.Ep;
+  if (w_router)
+    MOE_TRY_HIP(launch_router_transpose(w_router, at<uint16_t>(ws, L.wrT), c->num_experts, c->hidden_size, L.Ep, s));
+  MOE_TRY_HIP(launch_input_grad(g, s));
+  return MOE_OK;
+}
+
+moe_status run_router_wgrad(const moe_config* c, const Layout& L, const void* x, float* dw_router, float* db_router,
+                            void* ws, hipStream_t s) {
+  RouterWgradArgs r{};
+  r.x = x;
+  r.dl_hl = at<uint16_t>(ws, L.dl_hl);
+  r.dbpart = at<float>(ws, L.dbpart);
+  r.choff = at<int32_t>(ws, L.choff);
+  r.part = at<float>(ws, L.wpart);
+  r.dw_router = dw_router;
+  r.db_router = db_router;
+  r.T = L.T;
+  r.d = c->hidden_size;
+  r.E = c->num_experts;
+  r.Ep = L.Ep;
+  const hipError_t e = launch_router_wgrad(r, s);
+  if (e == hipErrorNotSupported) return MOE_ERR_UNSUPPORTED;
+  return hip_status(e);
+}
+
+// Shapes the router and dispatch backward kernels take: bf16, d a multiple
+// of 32 (64 for the router weight gradient), the backward workspace regions.
+moe_status check_backward(const moe_config* c, bool router_weights) {
+  if (!c->save_preact) return MOE_ERR_INVALID_ARG;
+  if (c->dtype != MOE_BF16 || c->hidden_size % 32) return MOE_ERR_UNSUPPORTED;
+  if (router_weights && c->hidden_size % 64) return MOE_ERR_UNSUPPORTED;
+  const Layout L = layout_of(c);
+  if (router_weights && L.rc.S > kRouterMaxChunks) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+}  // namespace
+
+moe_status moe_gate_backward(const moe_config* cfg, const float* logits, const int32_t* expert_idx,
+                             const float* dweight, const float* dloss, float* dlogits, void* ws, size_t ws_bytes,
+                             void* stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (!cfg->save_preact || !ws) return MOE_ERR_INVALID_ARG;
+  if (cfg->num_tokens == 0) return MOE_OK;
+  if (!logits || !expert_idx || !dweight || !dlogits) return MOE_ERR_INVALID_ARG;
+  const Layout L = layout_of(cfg);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  return run_gate_backward(cfg, L, logits, expert_idx, dweight, dloss, dlogits, false, ws,
+                           static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_dispatch_backward(const moe_config* cfg, const void* dx_disp, const int32_t* expert_idx,
+                                 const int32_t* slot, const int32_t* expert_offset, const void* w_router,
+                                 const float* dlogits, void* dx, void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (!ws) return MOE_ERR_INVALID_ARG;
+  if ((st = check_backward(cfg, false)) != MOE_OK) return st;
+  if (cfg->num_tokens == 0) return MOE_OK;
+  if (!dx_disp || !expert_idx || !slot || !expert_offset || !dx || (w_router && !dlogits)) return MOE_ERR_INVALID_ARG;
+  const Layout L = layout_of(cfg);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (w_router && (st = run_split(cfg, L, dlogits, ws, s)) != MOE_OK) return st;
+  return run_input_grad(cfg, L, dx_disp, expert_idx, slot, expert_offset, w_router, dx, ws, s);
+}
+
+moe_status moe_router_backward(const moe_config* cfg, const void* x, const float* dlogits, float* dw_router,
+                               float* db_router, void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (!ws || (!dw_router && !db_router)) return MOE_ERR_INVALID_ARG;
+  if ((st = check_backward(cfg, dw_router != nullptr)) != MOE_OK) return st;
+  const bool tok = cfg->num_tokens > 0;
+  if (tok && (!dlogits || (dw_router && !x))) return MOE_ERR_INVALID_ARG;
+  const Layout L = layout_of(cfg);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (tok && (st = run_split(cfg, L, dlogits, ws, s)) != MOE_OK) return st;
+  return run_router_wgrad(cfg, L, x, dw_router, db_router, ws, s);
+}
+
+moe_status moe_layer_backward(const moe_config* cfg, const void* x, const void* w_router, const void* w1,
+                              const void* w2, const float* logits, const int32_t* expert_idx, const int32_t* slot,
+                              const float* weight, const void* dout, const float* dloss, void* dx, float* dlogits,
+                              float* dw_router, float* db_router, void* dw1, float* db1, void* dw2, float* db2,
+                              void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (cfg->ffn_hidden <= 0 || !ws || !w1 || !w2 || !dw1 || !dw2) return MOE_ERR_INVALID_ARG;
+  if (!w_router && (dw_router || db_router)) return MOE_ERR_INVALID_ARG;
+  const bool router_w = w_router && dw_router;
+  if ((st = check_backward(cfg, router_w)) != MOE_OK) return st;
+  if (cfg->ffn_hidden % 16) return MOE_ERR_UNSUPPORTED;
+  const bool tok = cfg->num_tokens > 0;
+  if (tok && (!dout || !dx || (!w_router && !dlogits) || (router_w && !x))) return MOE_ERR_INVALID_ARG;
+  const Layout L = layout_of(cfg);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int32_t* idx = expert_idx ? expert_idx : at<int32_t>(ws, L.idx);
+  const int32_t* sl = slot ? slot : at<int32_t>(ws, L.slot);
+  const float* wt = weight ? weight : at<float>(ws, L.weight);
+  const float* lg = logits ? logits : at<float>(ws, L.logits);
+  float* dl = dlogits ? dlogits : at<float>(ws, L.dlg);
+  const int32_t* off = at<int32_t>(ws, L.offset);
+  void* yd = at<void>(ws, L.y_disp);   // y_disp, then dY_disp, then dX_disp
+
+  // combine backward: dY_disp over y_disp, gate-weight gradient
+  MOE_TRY_HIP(launch_combine_backward(dout, yd, idx, sl, wt, off, yd, at<float>(ws, L.dwg), L.T, cfg->k,
+                                      cfg->hidden_size, cfg->dtype, s));
+  // expert FFNs: dX_disp over dY_disp
+  GemmBwdArgs b;
+  b.X = at<void>(ws, L.x_disp);
+  b.W1 = w1;
+  b.W2 = w2;
+  b.A = at<void>(ws, L.a_save);
+  b.H = at<void>(ws, L.h_disp);
+  b.dY = yd;
+  b.dA = at<void>(ws, L.d_act);
+  b.dX = yd;
+  b.dW1 = dw1;
+  b.dW2 = dw2;
+  b.db1 = db1;
+  b.db2 = db2;
+  b.offset = off;
+  b.max_rows = L.T > 0 ? L.rows : 0;
+  b.E = cfg->num_experts;
+  b.d = cfg->hidden_size;
+  b.h = cfg->ffn_hidden;
+  b.act = cfg->activation;
+  MOE_TRY_HIP(launch_ffn_backward(b, cfg->dtype, s));
+  if (!tok) return run_router_wgrad(cfg, L, x, dw_router, db_router, ws, s);
+  // gate: logit gradient (and its split for the router products)
+  st = run_gate_backward(cfg, L, lg, idx, at<float>(ws, L.dwg), dloss, dl, w_router != nullptr, ws, s);
+  if (st != MOE_OK) return st;
+  // dispatch backward plus the router input gradient
+  st = run_input_grad(cfg, L, yd, idx, sl, off, w_router, dx, ws, s);
+  if (st != MOE_OK) return st;
+  if (dw_router || db_router) return run_router_wgrad(cfg, L, x, dw_router, db_router, ws, s);
   return MOE_OK;
 }
 

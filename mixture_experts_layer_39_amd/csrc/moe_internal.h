@@ -106,4 +106,95 @@ hipError_t launch_ffn_backward(const GemmBwdArgs& a, int dtype, hipStream_t s);
 // The four backward GEMMs on the large-tile kernel, or hipErrorNotSupported.
 hipError_t launch_backward_big(const GemmBwdArgs& a, hipStream_t s);
 
+// ---------------------------------------------------------------- layer backward
+// Router-gradient layout: the logit gradient is carried as two bf16 arrays
+// (hi = bf16(g), lo = bf16(g - hi), |g - hi - lo| <= 2^-16 |g|) side by
+// side in rows of 2*Ep, Ep = E rounded up to 32 (zero padded), so that the
+// router products run on bf16 MFMA at nearly fp32 accuracy.
+inline int router_ep(int E) { return (E + 31) / 32 * 32; }
+
+// Token chunks of the router weight gradient dW_r = dlogits^T x: the token
+// range is cut into S chunks (a multiple of 64 tokens each, at least 1024
+// unless T is smaller) so that S x (feature tiles) fills the chip; each chunk
+// yields an fp32 partial [2*Ep, d] that a second kernel sums in chunk order.
+struct RouterChunks {
+  int S, chunk;
+};
+inline RouterChunks router_chunks(int64_t T, int d, int E) {
+  RouterChunks r{0, 0};
+  if (T <= 0) return r;
+  const int64_t ep2 = 2 * (int64_t)router_ep(E);
+  const int64_t tiles = ((ep2 + 255) / 256) * ((d + 255) / 256);
+  int64_t S = (256 + tiles - 1) / tiles;
+  const int64_t smax = (T + 1023) / 1024;
+  if (S > smax) S = smax;
+  // a chunk's operand bytes must stay below 2^31 (32-bit buffer offsets)
+  const int64_t wmax = (d > ep2 ? d : ep2) * 2;
+  const int64_t smin = (T * wmax + (int64_t(1) << 30) - 1) >> 30;
+  if (S < smin) S = smin;
+  if (S < 1) S = 1;
+  int64_t chunk = ((T + S - 1) / S + 63) / 64 * 64;
+  r.chunk = (int)chunk;
+  r.S = (int)((T + chunk - 1) / chunk);
+  return r;
+}
+constexpr int kRouterMaxChunks = 256;
+constexpr int kTop1Parts = 64;          // workgroups of the top-1 histogram
+constexpr int kGateBwdTokens = 128;     // tokens per gate-backward workgroup
+
+hipError_t launch_combine_backward(const void* dout, const void* y_disp, const int32_t* expert_idx,
+                                   const int32_t* slot, const float* weight, const int32_t* expert_offset,
+                                   void* dy_disp, float* dweight, int64_t T, int k, int d, int dtype,
+                                   hipStream_t s);
+
+struct GateBwdArgs {
+  const float* logits;      // [T, E] (the logits of the forward); null = dlogits is an input
+  const int32_t* idx;       // [T, k]
+  const float* dw;          // [T, k] gradient of the gate weights
+  const float* coef;        // [E] dloss*E*ce_e/T (BALANCE), or null
+  float* dlogits;           // [T, E]: output (from logits) or input
+  uint16_t* dl_hl;          // [T, 2*Ep] bf16 hi/lo split, or null
+  float* dbpart;            // [ceil(T/kGateBwdTokens), E] column partial sums, or null
+  int64_t T;
+  int32_t E, k, Ep, normalize;
+};
+hipError_t launch_top1_coef(const int32_t* idx, int k, int64_t T, int E, const float* dloss, int32_t* part,
+                            float* coef, hipStream_t s);
+hipError_t launch_gate_backward(const GateBwdArgs& a, hipStream_t s);
+
+struct InputGradArgs {
+  const bf16* dx_disp;      // [rows, d]
+  const int32_t* idx;       // [T, k]
+  const int32_t* slot;      // [T, k]
+  const int32_t* offset;    // [E+1]
+  const uint16_t* dl_hl;    // [T, 2*Ep] or null (no router term)
+  const uint16_t* wrT;      // [d, Ep] router weight, transposed and padded
+  bf16* dx;                 // [T, d]
+  int64_t T;
+  int32_t d, k, Ep;
+};
+hipError_t launch_router_transpose(const void* w_router, uint16_t* wrT, int E, int d, int Ep, hipStream_t s);
+hipError_t launch_input_grad(const InputGradArgs& a, hipStream_t s);
+
+// dW_r (fp32 [E, d], nullable) and db_r (fp32 [E], nullable) from the split
+// logit gradient and x; part: [S, 2*Ep, d] fp32, choff: [S+1] int32.
+struct RouterWgradArgs {
+  const void* x;            // [T, d] bf16
+  const uint16_t* dl_hl;    // [T, 2*Ep]
+  const float* dbpart;      // [ceil(T/kGateBwdTokens), E]
+  int32_t* choff;
+  float* part;
+  float* dw_router;
+  float* db_router;
+  int64_t T;
+  int32_t d, E, Ep;
+};
+hipError_t launch_router_wgrad(const RouterWgradArgs& a, hipStream_t s);
+// The chunked product on the large-tile GEMM: part[c] = dl_hl[chunk c]^T x[chunk c].
+hipError_t launch_router_partials(const uint16_t* dl_hl, const void* x, const int32_t* choff, float* part,
+                                  int64_t T, int S, int d, int Ep, hipStream_t s);
+
+// Zero fill of n bytes (a kernel, so that it can sit in a captured graph).
+hipError_t launch_zero_bytes(void* p, size_t n, hipStream_t s);
+
 }  // namespace moe

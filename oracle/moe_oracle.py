@@ -461,9 +461,12 @@ def dispatch_backward(dx_disp, idx, slot, offset, num_tokens):
     return dx
 
 
-def gate_backward(probs, idx, dw, normalize_topk, loss_kind, dloss, dtype="f32"):
+def gate_backward(probs, idx, dw, normalize_topk, loss_kind, dloss, dtype="f32", top1_count=None,
+                  num_tokens=None):
     """Gradient of the router logits from the weight gradients dw [T, k] and
-    the upstream gradient dloss of gate_loss.
+    the upstream gradient dloss of gate_loss.  ``top1_count`` [E] and
+    ``num_tokens`` describe the whole batch when ``probs`` holds only some of
+    its tokens (default: the rows given are the batch).
 
     Weights: w_j = p[t, e_j], or w_j = p_j / S with S = sum_j p[t, e_j]
     (normalize_topk), whose derivative gives dp[t, e_i] += (dw_i - sum_j
@@ -489,8 +492,10 @@ def gate_backward(probs, idx, dw, normalize_topk, loss_kind, dloss, dtype="f32")
             for j in range(k):
                 dp[t, idx[t, j]] += dw[t, j]
     if T > 0 and loss_kind == LOSS_BALANCE:
-        ce = np.bincount(idx[:, 0], minlength=E) / T
-        dp += dloss * E * ce[None, :] / T
+        n = T if num_tokens is None else num_tokens
+        cnt = np.bincount(idx[:, 0], minlength=E) if top1_count is None else np.asarray(top1_count)
+        ce = cnt / n
+        dp += dloss * E * ce[None, :] / n
     dl = p * (dp - (p * dp).sum(axis=1, keepdims=True))
     return store(dl, _f32_or_f64(dtype))
 

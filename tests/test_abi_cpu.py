@@ -197,6 +197,45 @@ def test_device_entry_points_validate_before_launch():
                                None, None, FAKE, ws_need, None) == B.MOE_ERR_INVALID_ARG
 
 
+def test_backward_entry_points_validate_before_launch():
+    L = B.lib()
+    tr = _cfg(hidden_size=256, ffn_hidden=512, activation=B.MOE_ACT_GELU, save_preact=True)
+    ws = B.moe_workspace_size(tr)
+    c = ctypes.byref(tr)
+    inf = _cfg(hidden_size=256, ffn_hidden=512, activation=B.MOE_ACT_GELU)
+    ci = ctypes.byref(inf)
+    # training workspace is larger (it holds the logits and the backward regions)
+    assert ws > B.moe_workspace_size(inf)
+    # combine backward: every pointer needed
+    assert L.moe_combine_backward(c, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == B.MOE_ERR_INVALID_ARG
+    # gate backward: training config, outputs, workspace size
+    assert L.moe_gate_backward(ci, FAKE, FAKE, FAKE, None, FAKE, FAKE, 1 << 40, None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_gate_backward(c, FAKE, FAKE, FAKE, None, None, FAKE, ws, None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_gate_backward(c, FAKE, FAKE, FAKE, None, FAKE, FAKE, ws - 1, None) == B.MOE_ERR_WORKSPACE
+    # dispatch backward: dlogits needed with the router weight; bf16 and d % 32
+    assert L.moe_dispatch_backward(c, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, ws, None) \
+        == B.MOE_ERR_INVALID_ARG
+    assert L.moe_dispatch_backward(c, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, ws - 1, None) \
+        == B.MOE_ERR_WORKSPACE
+    f32 = _cfg(hidden_size=256, ffn_hidden=512, activation=B.MOE_ACT_GELU, save_preact=True, dtype=B.MOE_F32)
+    assert L.moe_dispatch_backward(ctypes.byref(f32), FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, 1 << 40,
+                                   None) == B.MOE_ERR_UNSUPPORTED
+    # router backward: some output; d % 64 for the weight gradient
+    assert L.moe_router_backward(c, FAKE, FAKE, None, None, FAKE, ws, None) == B.MOE_ERR_INVALID_ARG
+    d96 = _cfg(hidden_size=96, ffn_hidden=64, activation=B.MOE_ACT_GELU, save_preact=True)
+    assert L.moe_router_backward(ctypes.byref(d96), FAKE, FAKE, FAKE, None, FAKE, 1 << 40, None) \
+        == B.MOE_ERR_UNSUPPORTED
+    # layer backward: training config with a hidden layer; router gradients need the router weight
+    args = [FAKE] * 18
+    assert L.moe_layer_backward(ci, *args, FAKE, 1 << 40, None) == B.MOE_ERR_INVALID_ARG
+    no_router = list(args)
+    no_router[1] = None
+    assert L.moe_layer_backward(c, *no_router, FAKE, ws, None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_layer_backward(c, *args, FAKE, ws - 1, None) == B.MOE_ERR_WORKSPACE
+    one = _cfg(hidden_size=256, ffn_hidden=0, save_preact=True)
+    assert L.moe_layer_backward(ctypes.byref(one), *args, FAKE, 1 << 40, None) == B.MOE_ERR_INVALID_ARG
+
+
 def test_workspace_views_are_inside_workspace():
     cfg = _cfg(ffn_hidden=1024, activation=B.MOE_ACT_GELU, save_preact=True)
     n = B.moe_workspace_size(cfg)

@@ -1,0 +1,340 @@
+"""GPU parity of the layer backward around the expert FFNs, through the C ABI:
+moe_combine_backward, moe_gate_backward, moe_dispatch_backward,
+moe_router_backward and the fused moe_layer_backward, against the CPU
+oracle's combine_backward / gate_backward / dispatch_backward /
+router_backward / layer_backward.
+
+Every input is drawn by seeded generators (the routing of the standalone
+cases is the oracle's own, on drawn logits; the fused cases give both sides
+the same drawn logits, so their routing is identical by construction).
+
+Bars: bf16 outputs |g-o| <= 2e-2*|o| + 2e-2*rms(o); fp32 outputs computed
+from exact inputs (gate-weight and logit gradients, router weight
+gradients) 1e-5 in the same form; gradients downstream of bf16 storage in
+the fused backward 2e-2."""
+import numpy as np
+import pytest
+import torch
+
+from mixture_experts_layer_39_amd import binding as B
+from mixture_experts_layer_39_amd.synthetic import make_inputs, spec
+from oracle import moe_oracle as O
+from tests.gpu_util import close, experts, f64, i64, workspace
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _gen(seed):
+    g = torch.Generator(device=DEV)
+    g.manual_seed(seed)
+    return g
+
+
+def _draw(g, shape, std=1.0, dtype=torch.float32):
+    return (torch.randn(*shape, generator=g, device=DEV, dtype=torch.float32) * std).to(dtype)
+
+
+def _routing(logits, k, cf, min_cap, drop, normalize=False):
+    """The oracle's routing of drawn logits, as device int32/fp32 tensors."""
+    r = O.route(f64(logits), k, cf, min_cap, drop, normalize_topk=normalize)
+    dev = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a)).to(dt).to(DEV)
+    return r, dict(idx=dev(r["expert_idx"], torch.int32), slot=dev(r["slot"], torch.int32),
+                   weight=dev(r["weight"], torch.float32), offset=dev(r["expert_offset"], torch.int32))
+
+
+CB_CASES = [  # T, d, E, k, cf, dtype
+    (700, 512, 8, 2, 0.8, "bf16"),
+    (333, 256, 5, 1, 0.7, "bf16"),
+    (260, 128, 4, 2, 1.0, "f32"),
+    (1, 64, 3, 2, 1.0, "bf16"),
+]
+
+
+@pytest.mark.parametrize("T,d,E,k,cf,dt", CB_CASES)
+@pytest.mark.parametrize("in_place", [False, True])
+def test_combine_backward(T, d, E, k, cf, dt, in_place):
+    g = _gen(11 + T + d)
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    L = _draw(g, (T, E))
+    r, rt = _routing(L, k, cf, 1, True)
+    rows = max(int(r["expert_offset"][-1]), 1)
+    y = _draw(g, (rows, d), 1.0, tdt)
+    dout = _draw(g, (T, d), 1.0, tdt)
+    cfg = B.make_config(T, d, E, k, cf, 1, True, 16, B.MOE_ACT_GELU, B.MOE_BF16 if dt == "bf16" else B.MOE_F32)
+    want_dy, want_dw = O.combine_backward(f64(dout), f64(y), r["expert_idx"], r["slot"], r["weight"],
+                                          r["expert_offset"], dt)
+    y_np = f64(y)
+    dy = y if in_place else torch.full_like(y, 7.0)
+    dw = torch.full((T, k), 7.0, dtype=torch.float32, device=DEV)
+    B.moe_combine_backward(cfg, dout, y, rt["idx"], rt["slot"], rt["weight"], rt["offset"], dy, dw)
+    torch.cuda.synchronize()
+    n = int(r["expert_offset"][-1])
+    close(f64(dy)[:n], want_dy[:n], 2e-2 if dt == "bf16" else 1e-5)
+    close(f64(dw), want_dw, 1e-5)
+    assert (f64(dw)[r["slot"] < 0] == 0).all()
+    if not in_place:
+        np.testing.assert_array_equal(f64(y), y_np)
+
+
+GB_CASES = [  # T, E, k, normalize, loss, dloss
+    (500, 8, 2, False, O.LOSS_BALANCE, 0.7),
+    (500, 8, 2, True, O.LOSS_BALANCE, -1.3),
+    (300, 64, 2, False, O.LOSS_USAGE_STD, 0.5),
+    (300, 128, 2, True, O.LOSS_BALANCE, 2.0),
+    (200, 256, 1, False, O.LOSS_BALANCE, 1.0),
+    (200, 100, 2, True, O.LOSS_USAGE_STD, 0.0),
+    (129, 4, 1, True, O.LOSS_BALANCE, None),
+    (77, 37, 2, False, O.LOSS_BALANCE, 0.25),
+]
+
+
+@pytest.mark.parametrize("T,E,k,norm,loss,dloss", GB_CASES)
+def test_gate_backward(T, E, k, norm, loss, dloss):
+    g = _gen(23 + T + E)
+    L = _draw(g, (T, E), 1.5)
+    dw = _draw(g, (T, k))
+    r = O.route(f64(L), k, 1.0, 1, True, normalize_topk=norm)
+    idx = torch.from_numpy(r["expert_idx"]).to(torch.int32).to(DEV)
+    cfg = B.make_config(T, 64, E, k, 1.0, 1, True, 64, B.MOE_ACT_GELU, B.MOE_BF16, normalize_topk=norm,
+                        loss_kind=loss, save_preact=True)
+    ws = workspace(cfg, DEV)
+    dl = torch.full((T, E), 7.0, dtype=torch.float32, device=DEV)
+    dls = None if dloss is None else torch.tensor([dloss], dtype=torch.float32, device=DEV)
+    B.moe_gate_backward(cfg, L, idx, dw, dls, dl, ws)
+    torch.cuda.synchronize()
+    want = O.gate_backward(r["probs"], r["expert_idx"], f64(dw), norm, loss, 0.0 if dloss is None else dloss)
+    close(f64(dl), want, 1e-5)
+    if norm and loss == O.LOSS_USAGE_STD:
+        # renormalised weights and a count-only loss: no gradient off the top k
+        # (zero up to the rounding of <p, dp>, which is exactly 0 in real arithmetic)
+        chosen = np.zeros((T, E), bool)
+        np.put_along_axis(chosen, r["expert_idx"], True, axis=1)
+        got = f64(dl)
+        assert np.abs(got[~chosen]).max() <= 1e-6 * np.abs(got[chosen]).max()
+
+
+DB_CASES = [  # T, d, E, k, cf, router
+    (600, 512, 8, 2, 0.8, True),
+    (600, 512, 8, 2, 0.8, False),
+    (257, 256, 64, 2, 1.0, True),
+    (130, 96, 5, 1, 0.6, True),
+    (70, 2048, 256, 2, 1.0, True),
+]
+
+
+@pytest.mark.parametrize("T,d,E,k,cf,router", DB_CASES)
+def test_dispatch_backward(T, d, E, k, cf, router):
+    g = _gen(31 + T + d + E)
+    L = _draw(g, (T, E))
+    r, rt = _routing(L, k, cf, 1, True)
+    rows = max(int(r["expert_offset"][-1]), 1)
+    dxd = _draw(g, (rows, d), 1.0, torch.bfloat16)
+    wr = _draw(g, (E, d), 0.02, torch.bfloat16) if router else None
+    dl = _draw(g, (T, E), 0.05) if router else None
+    cfg = B.make_config(T, d, E, k, cf, 1, True, 64, B.MOE_ACT_GELU, B.MOE_BF16, save_preact=True)
+    ws = workspace(cfg, DEV)
+    dx = torch.full((T, d), 7.0, dtype=torch.bfloat16, device=DEV)
+    B.moe_dispatch_backward(cfg, dxd, rt["idx"], rt["slot"], rt["offset"], wr, dl, dx, ws)
+    torch.cuda.synchronize()
+    want = O.dispatch_backward(f64(dxd), r["expert_idx"], r["slot"], r["expert_offset"], T)
+    if router:
+        want = want + O.router_backward(np.zeros((T, d)), f64(wr), f64(dl))[0]
+        close(f64(dx), O.store(want, "bf16"), 2e-2)
+    else:
+        # sums of at most two bf16 values in fp32, rounded once: exact
+        np.testing.assert_array_equal(f64(dx), O.store(want, "bf16"))
+    dropped_all = (r["slot"] < 0).all(axis=1)
+    if not router and dropped_all.any():
+        assert (f64(dx)[dropped_all] == 0).all()
+
+
+RB_CASES = [  # T, d, E
+    (600, 512, 8),
+    (5000, 256, 64),
+    (3000, 128, 128),
+    (100, 64, 4),
+    (2100, 192, 256),
+]
+
+
+@pytest.mark.parametrize("T,d,E", RB_CASES)
+def test_router_backward(T, d, E):
+    g = _gen(41 + T + d + E)
+    x = _draw(g, (T, d), 1.0, torch.bfloat16)
+    dl = _draw(g, (T, E), 0.05)
+    cfg = B.make_config(T, d, E, 1, 1.0, 1, True, 64, B.MOE_ACT_GELU, B.MOE_BF16, save_preact=True)
+    ws = workspace(cfg, DEV)
+    dw = torch.full((E, d), 7.0, dtype=torch.float32, device=DEV)
+    db = torch.full((E,), 7.0, dtype=torch.float32, device=DEV)
+    B.moe_router_backward(cfg, x, dl, dw, db, ws)
+    torch.cuda.synchronize()
+    _, want_w, want_b = O.router_backward(f64(x), np.zeros((E, d)), f64(dl))
+    close(f64(dw), want_w, 1e-5)
+    close(f64(db), want_b, 1e-5)
+    # bit-identical on a second run
+    dw2 = torch.empty_like(dw)
+    db2 = torch.empty_like(db)
+    B.moe_router_backward(cfg, x, dl, dw2, db2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(dw, dw2) and torch.equal(db, db2)
+
+
+# ---------------------------------------------------------------- fused layer backward
+LB_CASES = [  # T, d, E, k, h, cf, drop, act, norm, loss, router
+    (600, 256, 8, 2, 256, 0.8, True, O.ACT_GELU, False, O.LOSS_BALANCE, True),
+    (600, 256, 8, 2, 256, 0.8, True, O.ACT_GELU, True, O.LOSS_USAGE_STD, False),
+    (500, 128, 16, 2, 192, 1.0, False, O.ACT_RELU, False, O.LOSS_BALANCE, True),
+    (300, 192, 4, 1, 128, 0.9, True, O.ACT_NONE, True, O.LOSS_BALANCE, True),
+    (64, 128, 64, 2, 128, 1.25, True, O.ACT_GELU, False, O.LOSS_BALANCE, True),
+]
+
+
+def _layer(T, d, E, k, h, cf, drop, act, norm, loss, router, seed):
+    sp = spec("nodrop_e128", T=T, d=d, E=E, k=k, h=h, cf=cf, min_cap=1, drop=drop, act=act, logits_given=True,
+              backward=False, seed=seed)
+    inp = make_inputs(sp, DEV)
+    g = _gen(seed + 1)
+    wr = _draw(g, (E, d), 0.02, torch.bfloat16) if router else None
+    dout = _draw(g, (T, d), 1.0, torch.bfloat16)
+    cfg = B.make_config(T, d, E, k, cf, 1, drop, h, act, B.MOE_BF16, normalize_topk=norm, loss_kind=loss,
+                        save_preact=True)
+    return sp, inp, wr, dout, cfg
+
+
+def _run_layer(cfg, inp, wr, dout, dloss, T, d, E, k, h, keep_routing):
+    ws = workspace(cfg, DEV)
+    out = torch.empty(T, d, dtype=torch.bfloat16, device=DEV)
+    loss = torch.empty(1, dtype=torch.float32, device=DEV)
+    cnt = torch.empty(E, dtype=torch.int32, device=DEV)
+    rt = {}
+    if keep_routing:
+        rt = dict(expert_idx=torch.empty(T, k, dtype=torch.int32, device=DEV),
+                  slot=torch.empty(T, k, dtype=torch.int32, device=DEV),
+                  weight=torch.empty(T, k, dtype=torch.float32, device=DEV))
+    B.moe_layer_forward(cfg, inp["x"], None, None, inp["logits"], inp["w1"], inp["b1"], inp["w2"], inp["b2"], out,
+                        loss, cnt, ws=ws, **rt)
+    gr = dict(dx=torch.full((T, d), 7.0, dtype=torch.bfloat16, device=DEV),
+              dlogits=torch.full((T, E), 7.0, dtype=torch.float32, device=DEV),
+              dw1=torch.full((E, h, d), 7.0, dtype=torch.bfloat16, device=DEV),
+              dw2=torch.full((E, d, h), 7.0, dtype=torch.bfloat16, device=DEV),
+              db1=torch.full((E, h), 7.0, dtype=torch.float32, device=DEV),
+              db2=torch.full((E, d), 7.0, dtype=torch.float32, device=DEV))
+    if wr is not None:
+        gr["dw_router"] = torch.full((E, d), 7.0, dtype=torch.float32, device=DEV)
+        gr["db_router"] = torch.full((E,), 7.0, dtype=torch.float32, device=DEV)
+    dls = torch.tensor([dloss], dtype=torch.float32, device=DEV)
+    B.moe_layer_backward(cfg, inp["x"], wr, inp["w1"], inp["w2"], dout, dls, gr["dx"], gr["dw1"], gr["dw2"],
+                         logits=inp["logits"], dlogits=gr["dlogits"], dw_router=gr.get("dw_router"),
+                         db_router=gr.get("db_router"), db1=gr["db1"], db2=gr["db2"], ws=ws, **rt)
+    torch.cuda.synchronize()
+    return gr, cnt
+
+
+@pytest.mark.parametrize("T,d,E,k,h,cf,drop,act,norm,loss,router", LB_CASES)
+def test_layer_backward(T, d, E, k, h, cf, drop, act, norm, loss, router):
+    seed = 500 + T + d + E
+    sp, inp, wr, dout, cfg = _layer(T, d, E, k, h, cf, drop, act, norm, loss, router, seed)
+    dloss = 0.8
+    gr, cnt = _run_layer(cfg, inp, wr, dout, dloss, T, d, E, k, h, keep_routing=(T % 2 == 0))
+    x, L = f64(inp["x"]), f64(inp["logits"])
+    w1, b1, w2, b2 = experts(inp["w1"]), experts(inp["b1"]), experts(inp["w2"]), experts(inp["b2"])
+    r = O.layer_forward(x, L, w1, b1, w2, b2, k=k, capacity_factor=cf, min_capacity=1, drop_tokens=drop, act=act,
+                        dtype="bf16", normalize_topk=norm, loss_kind=loss)
+    np.testing.assert_array_equal(i64(cnt), r["expert_count"])
+    want = O.layer_backward(x, None if wr is None else f64(wr), r, w1, w2, f64(dout), dloss, act=act, dtype="bf16",
+                            normalize_topk=norm, loss_kind=loss)
+    for key in ("dx", "dlogits", "dw1", "dw2", "db1", "db2", "dw_router", "db_router"):
+        if key in gr:
+            close(f64(gr[key]), want[key], 2e-2)
+
+
+def test_layer_backward_is_deterministic():
+    args = (400, 256, 8, 2, 128, 1.0, True, O.ACT_GELU, False, O.LOSS_BALANCE, True)
+    sp, inp, wr, dout, cfg = _layer(*args, seed=77)
+    g1, _ = _run_layer(cfg, inp, wr, dout, 0.3, 400, 256, 8, 2, 128, False)
+    g2, _ = _run_layer(cfg, inp, wr, dout, 0.3, 400, 256, 8, 2, 128, False)
+    for key in g1:
+        assert torch.equal(g1[key], g2[key]), key
+
+
+def test_layer_backward_no_tokens():
+    cfg = B.make_config(0, 128, 4, 2, 1.0, 1, True, 64, B.MOE_ACT_GELU, B.MOE_BF16, save_preact=True)
+    ws = workspace(cfg, DEV)
+    E, d, h = 4, 128, 64
+    w1 = torch.zeros(E, h, d, dtype=torch.bfloat16, device=DEV)
+    w2 = torch.zeros(E, d, h, dtype=torch.bfloat16, device=DEV)
+    wr = torch.zeros(E, d, dtype=torch.bfloat16, device=DEV)
+    dw1 = torch.full((E, h, d), 7.0, dtype=torch.bfloat16, device=DEV)
+    dw2 = torch.full((E, d, h), 7.0, dtype=torch.bfloat16, device=DEV)
+    db1 = torch.full((E, h), 7.0, dtype=torch.float32, device=DEV)
+    dwr = torch.full((E, d), 7.0, dtype=torch.float32, device=DEV)
+    dbr = torch.full((E,), 7.0, dtype=torch.float32, device=DEV)
+    B.moe_layer_backward(cfg, None, wr, w1, w2, None, None, None, dw1, dw2, dw_router=dwr, db_router=dbr, db1=db1,
+                         ws=ws)
+    torch.cuda.synchronize()
+    for t in (dw1, dw2, db1, dwr, dbr):
+        assert not t.float().abs().sum().item()
+
+
+def test_layer_backward_full_size_sampled():
+    """The no-drop workload (T=65536, d=4096, E=128, h=1536) through the fused
+    backward with the router: sampled rows of dX and dlogits against the
+    oracle's formulas computed token by token (the routing of the drawn
+    logits is the oracle's, checked through expert_count)."""
+    sp = spec("nodrop_e128", logits_given=True, backward=False)
+    T, d, E, h, k = sp["T"], sp["d"], sp["E"], sp["h"], sp["k"]
+    inp = make_inputs(sp, DEV)
+    g = _gen(4321)
+    wr = _draw(g, (E, d), 0.02, torch.bfloat16)
+    dout = _draw(g, (T, d), 1.0, torch.bfloat16)
+    dloss = 0.5
+    cfg = B.make_config(T, d, E, k, 1.0, 4, False, h, O.ACT_GELU, B.MOE_BF16, save_preact=True)
+    gr, cnt = _run_layer(cfg, inp, wr, dout, dloss, T, d, E, k, h, keep_routing=True)
+    r = O.route(f64(inp["logits"]), k, 1.0, 4, False)
+    np.testing.assert_array_equal(i64(cnt), r["expert_count"])
+    rng = np.random.default_rng(9)
+    toks = rng.choice(T, 12, replace=False)
+    w1, b1, w2, b2 = experts(inp["w1"]), experts(inp["b1"]), experts(inp["w2"]), experts(inp["b2"])
+    X = f64(inp["x"][torch.from_numpy(toks).to(DEV)])
+    dO = f64(dout[torch.from_numpy(toks).to(DEV)])
+    dws = np.zeros((len(toks), k))
+    dxd = np.zeros((len(toks), d))
+    for i, t in enumerate(toks):
+        for j in range(k):
+            e = int(r["expert_idx"][t, j])
+            a, hh, y = O._ffn_rows(X[i:i + 1], e, w1, b1, w2, b2, O.ACT_GELU, "bf16")
+            dws[i, j] = float(dO[i] @ y[0])
+            dy = O.store(r["weight"][t, j] * dO[i:i + 1], "bf16")
+            dA = O.store((dy @ np.asarray(w2[e], np.float64)) * O.gelu_grad(a), "bf16")
+            dxd[i] += O.store(dA @ np.asarray(w1[e], np.float64), "bf16")[0]
+    top1 = np.bincount(r["expert_idx"][:, 0], minlength=E)
+    dl = O.gate_backward(r["probs"][toks], r["expert_idx"][toks], O.store(dws, "f32"), False, O.LOSS_BALANCE,
+                         dloss, top1_count=top1, num_tokens=T)
+    close(f64(gr["dlogits"])[toks], dl, 2e-2)
+    dxr, _, _ = O.router_backward(X, f64(wr), dl)
+    close(f64(gr["dx"])[toks], O.store(dxd + dxr, "bf16"), 2e-2)
+
+
+def test_router_backward_full_size_sampled():
+    """The router weight gradient at the no-drop workload's size (T=65536,
+    d=4096, E=128) from a drawn logit gradient: sampled entries of dW_r and
+    db_r, each a 65536-term sum computed by the oracle."""
+    T, d, E = 65536, 4096, 128
+    g = _gen(8765)
+    x = _draw(g, (T, d), 1.0, torch.bfloat16)
+    dl = _draw(g, (T, E), 0.01)
+    cfg = B.make_config(T, d, E, 2, 1.0, 4, False, 1536, B.MOE_ACT_GELU, B.MOE_BF16, save_preact=True)
+    ws = workspace(cfg, DEV)
+    dw = torch.full((E, d), 7.0, dtype=torch.float32, device=DEV)
+    db = torch.full((E,), 7.0, dtype=torch.float32, device=DEV)
+    B.moe_router_backward(cfg, x, dl, dw, db, ws)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(3)
+    ee = rng.integers(0, E, 24)
+    ff = rng.integers(0, d, 24)
+    D = f64(dl)
+    xs = f64(x[:, torch.from_numpy(ff).to(DEV)])
+    want = np.array([O.router_backward(xs[:, i:i + 1], np.zeros((E, 1)), D)[1][ee[i], 0] for i in range(len(ee))])
+    close(f64(dw)[ee, ff], want, 1e-5)
+    close(f64(db), D.sum(axis=0), 1e-5)
