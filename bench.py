@@ -4,8 +4,10 @@
 One step is one full pass of the layer over one batch of synthetic input:
 gate (router GEMM, softmax, top-k, capacity slots, counts, loss), dispatch,
 expert FFN grouped GEMMs, combine -- the fused moe_layer_forward call -- plus,
-for the no-drop workload, the backward of the expert FFNs.  Inputs are seeded
-synthetic tensors already resident in HBM.  Prints one JSON line.
+for the no-drop workload, the backward of the expert FFNs (nodrop_e128) or of
+the whole layer (nodrop_e128_layer: moe_layer_backward with the router, bias
+and gate_loss gradients).  Inputs are seeded synthetic tensors already
+resident in HBM.  Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload top2_e64]
 
@@ -61,6 +63,11 @@ def load_traffic(workload):
     return rec.get("bytes_per_launch")
 
 
+def bwd_label(sp):
+    b = sp.get("backward")
+    return "" if not b else (", layer backward" if b == "layer" else ", expert FFN backward")
+
+
 def cpu_baseline(sp, inp, target_s=15.0):
     """The oracle (as it stands) on the first Ts tokens of the same workload:
     router logits, routing, dispatch, float64 expert FFNs, combine."""
@@ -82,7 +89,9 @@ def cpu_baseline(sp, inp, target_s=15.0):
         logits = lg_given[:ts] if lg_given is not None else O.router_logits(x[:ts], wr, br)
         r = O.layer_forward(x[:ts], logits, w1, b1, w2, b2, k=sp["k"], capacity_factor=sp["cf"],
                             min_capacity=sp["min_cap"], drop_tokens=sp["drop"], act=sp["act"], dtype=sp["dtype"])
-        if sp.get("backward"):
+        if sp.get("backward") == "layer":
+            O.layer_backward(x[:ts], wr, r, w1, w2, dy[:ts], 1.0, act=sp["act"], dtype=sp["dtype"])
+        elif sp.get("backward"):
             n = int(r["expert_offset"][-1])
             O.expert_ffn_backward(r["x_disp"], r["expert_offset"], w1, w2, r["a"], r["h"], dy[:n], sp["act"],
                                   sp["dtype"])
@@ -106,7 +115,7 @@ def cpu_baseline(sp, inp, target_s=15.0):
     return {"value": ts / el, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
             "sample": f"first {ts} of {sp['T']} tokens of {sp['name']} (capacity recomputed for {ts} tokens): "
                       f"router, routing, dispatch, float64 expert FFNs, combine"
-                      f"{', expert FFN backward' if sp.get('backward') else ''}; {el:.1f} s"}
+                      f"{bwd_label(sp)}; {el:.1f} s"}
 
 
 def main(argv=None):
@@ -153,16 +162,30 @@ def main(argv=None):
     stream = torch.cuda.current_stream()
 
     bwd = bool(sp.get("backward"))
+    layer = sp.get("backward") == "layer"
     if bwd:
         rows = B.moe_max_rows(cfg)
         xd_p, a_p, h_p, _, off_p = B.moe_workspace_views(cfg, ws)
-        dx = torch.empty(rows, d, dtype=torch.bfloat16, device=dev)
+        dx = torch.empty(T if layer else rows, d, dtype=torch.bfloat16, device=dev)
         dw1 = torch.empty_like(inp["w1"])
         dw2 = torch.empty_like(inp["w2"])
+    if layer:
+        f32 = dict(dtype=torch.float32, device=dev)
+        db1 = torch.empty(E, h, **f32)
+        db2 = torch.empty(E, d, **f32)
+        dwr = torch.empty(E, d, **f32)
+        dbr = torch.empty(E, **f32)
+        dlg = torch.empty(T, E, **f32)
+        dwg = torch.empty(T, k, **f32)
+        dloss = torch.ones(1, **f32)
 
     def backward():
-        B.moe_expert_ffn_backward(cfg, xd_p, off_p, inp["w1"], inp["w2"], a_p, h_p, inp["dy"], dx, dw1, None, dw2,
-                                  None, ws, stream=stream)
+        if layer:
+            B.moe_layer_backward(cfg, inp["x"], inp["w_router"], inp["w1"], inp["w2"], inp["dy"], dloss, dx, dw1, dw2,
+                                 dlogits=dlg, dw_router=dwr, db_router=dbr, db1=db1, db2=db2, ws=ws, stream=stream)
+        else:
+            B.moe_expert_ffn_backward(cfg, xd_p, off_p, inp["w1"], inp["w2"], a_p, h_p, inp["dy"], dx, dw1, None,
+                                      dw2, None, ws, stream=stream)
 
     def step():
         B.moe_layer_forward(cfg, inp["x"], inp["w_router"], inp["b_router"], inp["logits"], inp["w1"], inp["b1"],
@@ -188,11 +211,13 @@ def main(argv=None):
              weight=torch.empty(T, k, dtype=torch.float32, device=dev),
              offset=torch.empty(E + 1, dtype=torch.int32, device=dev))
     xd, a_p, hd_p, yd_p, _ = B.moe_workspace_views(cfg, ws)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
-    acc = [0.0] * 5
+    nst = 9 if layer else 5
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)]
+    acc = [0.0] * nst
+    lg_out = torch.empty(T, E, dtype=torch.float32, device=dev) if layer else None
     for it in range(a.warmup + a.steps):
         ev[0].record(stream)
-        B.moe_gate(cfg, inp["x"], inp["w_router"], inp["b_router"], inp["logits"], None, g["idx"], g["slot"],
+        B.moe_gate(cfg, inp["x"], inp["w_router"], inp["b_router"], inp["logits"], lg_out, g["idx"], g["slot"],
                    g["weight"], count, g["offset"], loss, ws, stream=stream)
         ev[1].record(stream)
         B.moe_dispatch(cfg, inp["x"], g["idx"], g["slot"], g["offset"], xd, stream=stream)
@@ -202,13 +227,28 @@ def main(argv=None):
         ev[3].record(stream)
         B.moe_combine(cfg, yd_p, g["idx"], g["slot"], g["weight"], g["offset"], out, stream=stream)
         ev[4].record(stream)
-        if bwd:
+        if layer:
+            # the backward as its separate calls: combine, expert FFNs, gate,
+            # dispatch + router input, router weights
+            B.moe_combine_backward(cfg, inp["dy"], yd_p, g["idx"], g["slot"], g["weight"], g["offset"], yd_p, dwg,
+                                   stream=stream)
+            ev[5].record(stream)
+            B.moe_expert_ffn_backward(cfg, xd, g["offset"], inp["w1"], inp["w2"], a_p, hd_p, yd_p, yd_p, dw1, db1,
+                                      dw2, db2, ws, stream=stream)
+            ev[6].record(stream)
+            B.moe_gate_backward(cfg, lg_out, g["idx"], dwg, dloss, dlg, ws, stream=stream)
+            ev[7].record(stream)
+            B.moe_dispatch_backward(cfg, yd_p, g["idx"], g["slot"], g["offset"], inp["w_router"], dlg, dx, ws,
+                                    stream=stream)
+            ev[8].record(stream)
+            B.moe_router_backward(cfg, inp["x"], dlg, dwr, dbr, ws, stream=stream)
+        elif bwd:
             B.moe_expert_ffn_backward(cfg, xd, g["offset"], inp["w1"], inp["w2"], a_p, hd_p, inp["dy"], dx, dw1,
                                       None, dw2, None, ws, stream=stream)
-        ev[5].record(stream)
+        ev[nst].record(stream)
         if it >= a.warmup:
             torch.cuda.synchronize()
-            for i in range(5):
+            for i in range(nst):
                 acc[i] += ev[i].elapsed_time(ev[i + 1])
     st_ms = [v / a.steps for v in acc]
 
@@ -236,12 +276,32 @@ def main(argv=None):
         "combine": {"ms": st_ms[3], "bytes": comb_bytes, "GB/s": gbs(comb_bytes, st_ms[3]),
                     "frac_hbm": gbs(comb_bytes, st_ms[3]) / PEAK_HBM_GBS},
     }
-    if bwd:
-        bflops = 2 * ffn_flops   # dgrad (dH, dX) + wgrad (dW2, dW1): 4 GEMMs of 2*N*d*h
+    bflops = 2 * ffn_flops   # dgrad (dH, dX) + wgrad (dW2, dW1): 4 GEMMs of 2*N*d*h
+    if bwd and not layer:
         stages["expert_ffn_backward"] = {"ms": st_ms[4], "flops": bflops,
                                          "TFLOP/s": bflops / (st_ms[4] * 1e-3) / 1e12,
                                          "frac_mfma": bflops / (st_ms[4] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                                          "launches": 4}
+    if layer:
+        ep = (E + 31) // 32 * 32
+        cb_bytes = T * d * esz + 2 * N * d * esz + T * k * 16
+        gb_bytes = 2 * T * E * 4 + T * k * 8
+        ib_bytes = N * d * esz + T * d * esz + T * E * 4 + T * 2 * ep * 2 + T * k * 8
+        rb_flops = 2 * T * E * d
+        stages["combine_backward"] = {"ms": st_ms[4], "bytes": cb_bytes, "GB/s": gbs(cb_bytes, st_ms[4]),
+                                      "frac_hbm": gbs(cb_bytes, st_ms[4]) / PEAK_HBM_GBS}
+        stages["expert_ffn_backward"] = {"ms": st_ms[5], "flops": bflops,
+                                         "TFLOP/s": bflops / (st_ms[5] * 1e-3) / 1e12,
+                                         "frac_mfma": bflops / (st_ms[5] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                                         "launches": 4, "with": "db1, db2"}
+        stages["gate_backward"] = {"ms": st_ms[6], "bytes": gb_bytes, "GB/s": gbs(gb_bytes, st_ms[6]),
+                                   "frac_hbm": gbs(gb_bytes, st_ms[6]) / PEAK_HBM_GBS}
+        stages["dispatch_router_input_backward"] = {"ms": st_ms[7], "bytes": ib_bytes, "GB/s": gbs(ib_bytes, st_ms[7]),
+                                                    "frac_hbm": gbs(ib_bytes, st_ms[7]) / PEAK_HBM_GBS}
+        stages["router_weight_backward"] = {"ms": st_ms[8], "flops": rb_flops,
+                                            "TFLOP/s": rb_flops / (st_ms[8] * 1e-3) / 1e12,
+                                            "bytes": T * d * esz + T * E * 4,
+                                            "GB/s": gbs(T * d * esz + T * E * 4, st_ms[8])}
     gemm_ms = st_ms[2] / n_gemm
     achieved = (ffn_flops / n_gemm) / (gemm_ms * 1e-3) / 1e12
     # the expert GEMM: one kernel template launched once per Linear (the GELU
@@ -256,7 +316,7 @@ def main(argv=None):
             "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
             "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
             "dtype": sp["dtype"], "data": "synthetic",
-            "config": {"workload": describe(sp) + (" + expert FFN backward" if bwd else ""),
+            "config": {"workload": describe(sp) + bwd_label(sp).replace(",", " +"),
                        "tokens_per_step": T, "rows_kept": N},
             "roofline": roofline, "stages": stages}
     if not a.no_cpu_baseline:

@@ -16,6 +16,8 @@ Workloads (shapes from the five benchmark configurations of the layer):
               router bias ln(p_e) with p_e proportional to (e+1)^-1.2 (Zipf s=1.2)
   nodrop_e128 T=65536, d=4096, E=128, k=2, 4096->1536->4096 GELU, bf16, no drop,
               plus an N(0,1) upstream gradient for the expert backward
+  nodrop_e128_layer  the same layer with an N(0,1) upstream gradient of the
+              layer output [T, d] for the whole layer's backward
 Activations and upstream gradients ~ N(0,1); weights and biases ~ N(0, 0.02)
 unless stated.
 """
@@ -43,6 +45,9 @@ WORKLOADS = {
     "nodrop_e128": dict(T=65536, d=4096, E=128, k=2, h=1536, act=ACT_GELU, dtype="bf16",
                         cf=1.0, min_cap=4, drop=False, wstd=0.02, logits_given=False,
                         zipf=None, seed=1005, backward=True),
+    "nodrop_e128_layer": dict(T=65536, d=4096, E=128, k=2, h=1536, act=ACT_GELU, dtype="bf16",
+                              cf=1.0, min_cap=4, drop=False, wstd=0.02, logits_given=False,
+                              zipf=None, seed=1005, backward="layer"),
 }
 
 
@@ -70,7 +75,8 @@ def make_inputs(sp, device="cpu", seed=None, n_rows_grad=None):
 
     Returns a dict with x, w_router (or None), b_router (or None), logits
     (given logits, or None), w1, b1, w2 (or None), b2 (or None) and, for
-    workloads with a backward, dy of shape [n_rows_grad, d].
+    workloads with a backward, dy of shape [n_rows_grad, d] (default: k*T
+    dispatched rows for the expert backward, T token rows for the layer's).
     """
     dev = torch.device(device)
     g = torch.Generator(device=dev)
@@ -97,6 +103,6 @@ def make_inputs(sp, device="cpu", seed=None, n_rows_grad=None):
         out["w2"] = None
         out["b2"] = None
     if sp.get("backward"):
-        n = sp["k"] * T if n_rows_grad is None else n_rows_grad
+        n = (T if sp["backward"] == "layer" else sp["k"] * T) if n_rows_grad is None else n_rows_grad
         out["dy"] = _draw(g, (n, d), 1.0, dev).to(dt)
     return out
