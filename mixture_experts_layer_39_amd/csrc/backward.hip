@@ -22,17 +22,18 @@
 //    row of y_disp once, and dY_disp is written over y_disp in place (each
 //    packed row belongs to exactly one claim, so one wavefront owns it).
 //  * Gate backward: a group of 32 or 64 lanes per token, each lane holding
-//    one to four experts; softmax and the two reductions are xor-shuffles
-//    inside the group.  It also writes the logit gradient as a bf16 hi/lo
-//    pair (hi = bf16(g), lo = bf16(g - hi)) and per-workgroup column sums.
+//    one to four consecutive experts; the softmax's max and sum are
+//    xor-shuffles inside the group, the chosen probabilities one shuffle
+//    each.  It also writes the logit gradient as a bf16 hi/lo pair
+//    (hi = bf16(g), lo = bf16(g - hi)) and per-workgroup column sums.
 //  * The router's input gradient dlogits · W_r has K = E (at most 256): it
 //    runs on v_mfma_f32_32x32x16_bf16 twice (hi and lo), which keeps ~16
-//    bits of the fp32 gradient, with fragments loaded straight from global
-//    memory (W_r^T is 1 MB at most and stays in L2).  Features are the MFMA
-//    rows, in the permuted order that gives each lane 16 consecutive output
-//    features of one token, so the dispatch-backward gather (dX_disp rows of
-//    the token's kept claims) and the bf16 store are 32-byte vectors in the
-//    same kernel; the sum is rounded once.
+//    bits of the fp32 gradient.  W_r is packed once per call into MFMA
+//    fragment order (1 MB at most, L2-resident), so each fragment is one
+//    contiguous 1 KB load.  The result goes through LDS to token rows, where
+//    the dispatch-backward gather (the dX_disp rows of the token's kept
+//    claims) and the bf16 store are whole contiguous row segments; the sum is
+//    rounded once.
 //  * dW_r = dlogits^T x has K = T: the token range is cut into chunks, each
 //    chunk's product runs on the large-tile GEMM (both operands transposed,
 //    fp32 partial output), and one kernel adds the chunks and the hi/lo
@@ -56,9 +57,39 @@ unsigned row_grid(int64_t T) {
 }
 
 // ---------------------------------------------------------------- combine backward
-// y and dy may be the same buffer: each lane reads its vector of a row before
-// it writes the same vector, and no other wavefront touches that row (so the
-// two pointers are deliberately not restrict-qualified).
+// y and dy may be the same buffer: each lane reads its vectors of a row before
+// it writes the same vectors, and no other wavefront touches that row (so the
+// two pointers are deliberately not restrict-qualified).  Each lane loads
+// U vectors of dOut and of both rows before any store, so that U x 3 loads
+// are in flight (a store may alias a later load, which keeps the compiler
+// from hoisting loads across stores by itself).
+template <int DT>
+__device__ __forceinline__ void cb_unpack(const u32x4 v, float (&f)[8]) {
+  if constexpr (DT == DT_BF16) {
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = lo16(u[i]);
+      f[2 * i + 1] = hi16(u[i]);
+    }
+  } else {
+    f[0] = __uint_as_float(v.x);
+    f[1] = __uint_as_float(v.y);
+    f[2] = __uint_as_float(v.z);
+    f[3] = __uint_as_float(v.w);
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ u32x4 cb_scale(float w, const float (&f)[8]) {
+  if constexpr (DT == DT_BF16)
+    return u32x4{pack_bf16x2(w * f[0], w * f[1]), pack_bf16x2(w * f[2], w * f[3]), pack_bf16x2(w * f[4], w * f[5]),
+                 pack_bf16x2(w * f[6], w * f[7])};
+  else
+    return u32x4{__float_as_uint(w * f[0]), __float_as_uint(w * f[1]), __float_as_uint(w * f[2]),
+                 __float_as_uint(w * f[3])};
+}
+
 template <int DT>
 __global__ __launch_bounds__(256) void combine_backward_kernel(const u32x4* __restrict__ dout, const u32x4* y,
                                                                const int32_t* __restrict__ expert_idx,
@@ -66,6 +97,8 @@ __global__ __launch_bounds__(256) void combine_backward_kernel(const u32x4* __re
                                                                const float* __restrict__ weight,
                                                                const int32_t* __restrict__ offset, u32x4* dy,
                                                                float* __restrict__ dw, int64_t T, int k, int nvec) {
+  constexpr int U = 4;
+  constexpr int NE = DT == DT_BF16 ? 8 : 4;   // elements per vector
   const int lane = threadIdx.x & 63;
   const int64_t wave_id = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * kWaves;
@@ -89,59 +122,32 @@ __global__ __launch_bounds__(256) void combine_backward_kernel(const u32x4* __re
     float dot0 = 0.f, dot1 = 0.f;
     if (r0 >= 0 || r1 >= 0) {
       const u32x4* src = dout + t * nvec;
-      for (int v = lane; v < nvec; v += 64) {
-        const u32x4 o = __builtin_nontemporal_load(src + v);
-        if constexpr (DT == DT_BF16) {
-          const uint32_t ou[4] = {o.x, o.y, o.z, o.w};
-          float of[8];
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      for (int v0 = lane; v0 < nvec; v0 += 64 * U) {
+        u32x4 o[U], ya[U], yb[U];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            of[2 * i] = lo16(ou[i]);
-            of[2 * i + 1] = hi16(ou[i]);
-          }
-          if (r0 >= 0) {
-            const u32x4 a = y[r0 * nvec + v];
-            const uint32_t au[4] = {a.x, a.y, a.z, a.w};
+        for (int u = 0; u < U; ++u) {
+          const int v = v0 + 64 * u;
+          const bool in = v < nvec;
+          o[u] = in ? __builtin_nontemporal_load(src + v) : z;
+          ya[u] = (in && r0 >= 0) ? y[r0 * nvec + v] : z;
+          yb[u] = (in && r1 >= 0) ? y[r1 * nvec + v] : z;
+        }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              dot0 = fmaf(of[2 * i], lo16(au[i]), dot0);
-              dot0 = fmaf(of[2 * i + 1], hi16(au[i]), dot0);
-            }
-            dy[r0 * nvec + v] = u32x4{pack_bf16x2(w0 * of[0], w0 * of[1]), pack_bf16x2(w0 * of[2], w0 * of[3]),
-                                      pack_bf16x2(w0 * of[4], w0 * of[5]), pack_bf16x2(w0 * of[6], w0 * of[7])};
-          }
-          if (r1 >= 0) {
-            const u32x4 b = y[r1 * nvec + v];
-            const uint32_t bu[4] = {b.x, b.y, b.z, b.w};
+        for (int u = 0; u < U; ++u) {
+          const int v = v0 + 64 * u;
+          if (v >= nvec) break;
+          float of[8], fa[8], fb[8];
+          cb_unpack<DT>(o[u], of);
+          cb_unpack<DT>(ya[u], fa);
+          cb_unpack<DT>(yb[u], fb);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              dot1 = fmaf(of[2 * i], lo16(bu[i]), dot1);
-              dot1 = fmaf(of[2 * i + 1], hi16(bu[i]), dot1);
-            }
-            dy[r1 * nvec + v] = u32x4{pack_bf16x2(w1 * of[0], w1 * of[1]), pack_bf16x2(w1 * of[2], w1 * of[3]),
-                                      pack_bf16x2(w1 * of[4], w1 * of[5]), pack_bf16x2(w1 * of[6], w1 * of[7])};
+          for (int i = 0; i < NE; ++i) {
+            dot0 = fmaf(of[i], fa[i], dot0);
+            dot1 = fmaf(of[i], fb[i], dot1);
           }
-        } else {
-          const float of[4] = {__uint_as_float(o.x), __uint_as_float(o.y), __uint_as_float(o.z),
-                               __uint_as_float(o.w)};
-          if (r0 >= 0) {
-            const u32x4 a = y[r0 * nvec + v];
-            dot0 = fmaf(of[0], __uint_as_float(a.x), dot0);
-            dot0 = fmaf(of[1], __uint_as_float(a.y), dot0);
-            dot0 = fmaf(of[2], __uint_as_float(a.z), dot0);
-            dot0 = fmaf(of[3], __uint_as_float(a.w), dot0);
-            dy[r0 * nvec + v] = u32x4{__float_as_uint(w0 * of[0]), __float_as_uint(w0 * of[1]),
-                                      __float_as_uint(w0 * of[2]), __float_as_uint(w0 * of[3])};
-          }
-          if (r1 >= 0) {
-            const u32x4 b = y[r1 * nvec + v];
-            dot1 = fmaf(of[0], __uint_as_float(b.x), dot1);
-            dot1 = fmaf(of[1], __uint_as_float(b.y), dot1);
-            dot1 = fmaf(of[2], __uint_as_float(b.z), dot1);
-            dot1 = fmaf(of[3], __uint_as_float(b.w), dot1);
-            dy[r1 * nvec + v] = u32x4{__float_as_uint(w1 * of[0]), __float_as_uint(w1 * of[1]),
-                                      __float_as_uint(w1 * of[2]), __float_as_uint(w1 * of[3])};
-          }
+          if (r0 >= 0) dy[r0 * nvec + v] = cb_scale<DT>(w0, of);
+          if (r1 >= 0) dy[r1 * nvec + v] = cb_scale<DT>(w1, of);
         }
       }
     }
@@ -189,32 +195,48 @@ __global__ __launch_bounds__(256) void top1_coef_kernel(const int32_t* __restric
 }
 
 // ---------------------------------------------------------------- gate backward
-// Group of G lanes per token (G = 32 or 64), lane gl holding experts
-// gl + G*i, i < EPL.  Reductions are xor-shuffles with offsets below G, so
-// they stay inside the group.
-template <int G>
-__device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int m = G / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m);
-  return v;
-}
+// Group of G lanes per token (G = 32 or 64), lane gl holding the EPL
+// consecutive experts gl*EPL .. +EPL-1.  The softmax needs one max and one
+// sum over the group (xor-shuffles with offsets below G, so they stay inside
+// the group); the chosen experts' probabilities are read from the lanes
+// that hold them; <p, dp> needs no further reduction, because dp is the
+// BALANCE coefficient (summed with the exponentials) plus the two chosen
+// terms.
 template <int G>
 __device__ __forceinline__ float group_max(float v) {
 #pragma unroll
   for (int m = G / 2; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
   return v;
 }
+template <int G>
+__device__ __forceinline__ void group_sum2(float& a, float& b) {
+#pragma unroll
+  for (int m = G / 2; m >= 1; m >>= 1) {
+    a += __shfl_xor(a, m);
+    b += __shfl_xor(b, m);
+  }
+}
 
 // bf16 bits of v (round to nearest even)
 __device__ __forceinline__ uint32_t bf16_bits(float v) { return pack_bf16x2(v, 0.f) & 0xffffu; }
 
+template <int EPL>
+__device__ __forceinline__ float pick(const float (&v)[EPL], int i) {
+  float r = v[0];
+#pragma unroll
+  for (int j = 1; j < EPL; ++j)
+    if (i == j) r = v[j];
+  return r;
+}
+
 template <int G, int EPL, bool FROM_LOGITS>
 __global__ __launch_bounds__(256) void gate_backward_kernel(GateBwdArgs a) {
   constexpr int GPW = 64 / G;   // tokens per wave and pass
-  __shared__ float s_db[kWaves * GPW][G * EPL];
+  __shared__ float s_db[kWaves * GPW][G * EPL + 1];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int grp = lane / G, gl = lane % G;
+  const int grp = lane / G, gl = lane % G, gbase = lane - gl;
   const int E = a.E, k = a.k, Ep = a.Ep;
+  const int eb = gl * EPL;      // this lane's first expert
   const int64_t T = a.T;
   const int64_t tb0 = (int64_t)blockIdx.x * kGateBwdTokens;
   float dbacc[EPL];
@@ -226,42 +248,39 @@ __global__ __launch_bounds__(256) void gate_backward_kernel(GateBwdArgs a) {
     const bool valid = t < T;
     float dl[EPL];
     if constexpr (FROM_LOGITS) {
-      float p[EPL];
+      float p[EPL], cf[EPL];
       float mx = -INFINITY;
 #pragma unroll
       for (int i = 0; i < EPL; ++i) {
-        const int e = gl + G * i;
+        const int e = eb + i;
         p[i] = (valid && e < E) ? a.logits[t * E + e] : -INFINITY;
+        cf[i] = (a.coef && e < E) ? a.coef[e] : 0.f;
         mx = fmaxf(mx, p[i]);
       }
       mx = group_max<G>(mx);
       if (!valid) mx = 0.f;
-      float sum = 0.f;
+      float sum = 0.f, sc = 0.f;
 #pragma unroll
       for (int i = 0; i < EPL; ++i) {
-        const int e = gl + G * i;
+        const int e = eb + i;
         p[i] = (valid && e < E) ? expf(p[i] - mx) : 0.f;
         sum += p[i];
+        sc = fmaf(p[i], cf[i], sc);
       }
-      sum = group_sum<G>(sum);
+      group_sum2<G>(sum, sc);
       if (!valid) sum = 1.f;
 #pragma unroll
       for (int i = 0; i < EPL; ++i) p[i] = p[i] / sum;
-      // the chosen experts, their gate-weight gradients and probabilities
-      // (each probability is held by one lane: the group sum is exact)
-      const int e0 = valid ? a.idx[t * k] : -1;
-      const int e1 = (valid && k == 2) ? a.idx[t * k + 1] : -1;
+      // the chosen experts and the probabilities their owner lanes hold
+      int e0 = valid ? a.idx[t * k] : 0;
+      int e1 = (valid && k == 2) ? a.idx[t * k + 1] : 0;
+      e0 = min(max(e0, 0), E - 1);
+      e1 = min(max(e1, 0), E - 1);
       const float g0 = valid ? a.dw[t * k] : 0.f;
       const float g1 = (valid && k == 2) ? a.dw[t * k + 1] : 0.f;
-      float pe0 = 0.f, pe1 = 0.f;
-#pragma unroll
-      for (int i = 0; i < EPL; ++i) {
-        const int e = gl + G * i;
-        if (e == e0) pe0 = p[i];
-        if (e == e1) pe1 = p[i];
-      }
-      pe0 = group_sum<G>(pe0);
-      pe1 = group_sum<G>(pe1);
+      const float pe0 = __shfl(pick<EPL>(p, e0 % EPL), gbase + e0 / EPL);
+      const float pe1 = k == 2 ? __shfl(pick<EPL>(p, e1 % EPL), gbase + e1 / EPL) : 0.f;
+      if (k != 2) e1 = -1;
       float c0 = g0, c1 = g1;
       if (a.normalize) {
         const float S = pe0 + pe1;
@@ -269,144 +288,228 @@ __global__ __launch_bounds__(256) void gate_backward_kernel(GateBwdArgs a) {
         c0 = (g0 - corr) / S;
         c1 = (g1 - corr) / S;
       }
-      float dp[EPL];
-      float pdp = 0.f;
+      // <p, dp> = sum_e p_e coef_e + p_e0 c0 + p_e1 c1
+      const float pdp = sc / sum + pe0 * c0 + pe1 * c1;
 #pragma unroll
       for (int i = 0; i < EPL; ++i) {
-        const int e = gl + G * i;
-        dp[i] = (a.coef && e < E) ? a.coef[e] : 0.f;
-        if (e == e0) dp[i] += c0;
-        if (e == e1) dp[i] += c1;
-        pdp = fmaf(p[i], dp[i], pdp);
+        const int e = eb + i;
+        float dp = cf[i];
+        if (e == e0) dp += c0;
+        if (e == e1) dp += c1;
+        dl[i] = p[i] * (dp - pdp);
       }
-      pdp = group_sum<G>(pdp);
-#pragma unroll
-      for (int i = 0; i < EPL; ++i) dl[i] = p[i] * (dp[i] - pdp);
     } else {
 #pragma unroll
       for (int i = 0; i < EPL; ++i) {
-        const int e = gl + G * i;
+        const int e = eb + i;
         dl[i] = (valid && e < E) ? a.dlogits[t * E + e] : 0.f;
       }
     }
     if (valid) {
+      uint32_t hb[EPL], lb[EPL];
 #pragma unroll
       for (int i = 0; i < EPL; ++i) {
-        const int e = gl + G * i;
+        const int e = eb + i;
         if (FROM_LOGITS && e < E) a.dlogits[t * E + e] = dl[i];
-        if (a.dl_hl && e < Ep) {
-          const uint32_t hb = bf16_bits(dl[i]);
-          const uint32_t lb = bf16_bits(dl[i] - __uint_as_float(hb << 16));
-          a.dl_hl[t * 2 * Ep + e] = (uint16_t)hb;
-          a.dl_hl[t * 2 * Ep + Ep + e] = (uint16_t)lb;
-        }
+        hb[i] = bf16_bits(dl[i]);
+        lb[i] = bf16_bits(dl[i] - __uint_as_float(hb[i] << 16));
         dbacc[i] += dl[i];
+      }
+      // (with EPL even and Ep a multiple of 32, eb < Ep covers the whole pair)
+      if (a.dl_hl && eb < Ep) {
+        uint16_t* hrow = a.dl_hl + t * 2 * Ep + eb;
+        if constexpr (EPL % 2 == 0) {
+#pragma unroll
+          for (int i = 0; i < EPL; i += 2) {
+            reinterpret_cast<uint32_t*>(hrow)[i / 2] = hb[i] | (hb[i + 1] << 16);
+            reinterpret_cast<uint32_t*>(hrow + Ep)[i / 2] = lb[i] | (lb[i + 1] << 16);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < EPL; ++i) {
+            if (eb + i < Ep) {
+              hrow[i] = (uint16_t)hb[i];
+              hrow[Ep + i] = (uint16_t)lb[i];
+            }
+          }
+        }
       }
     }
   }
   if (!a.dbpart) return;
-  // column partial sums of this workgroup's tokens, in a fixed order
+  // column partial sums of this workgroup's tokens, in a fixed order, stored
+  // expert-major: dbpart[e][workgroup]
 #pragma unroll
-  for (int i = 0; i < EPL; ++i) s_db[wave * GPW + grp][gl + G * i] = dbacc[i];
+  for (int i = 0; i < EPL; ++i) s_db[wave * GPW + grp][eb + i] = dbacc[i];
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += 256) {
     float s = 0.f;
     for (int r = 0; r < kWaves * GPW; ++r) s += s_db[r][e];
-    a.dbpart[(int64_t)blockIdx.x * E + e] = s;
+    a.dbpart[(int64_t)e * gridDim.x + blockIdx.x] = s;
   }
 }
 
 // ---------------------------------------------------------------- router input gradient
-// wrT[f][e] = W_r[e][f] for e < E, zero for E <= e < Ep.
-__global__ __launch_bounds__(256) void router_transpose_kernel(const uint16_t* __restrict__ wr,
-                                                               uint16_t* __restrict__ wrT, int E, int d, int Ep) {
-  const int64_t n = (int64_t)d * Ep;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
-    const int f = (int)(i / Ep), e = (int)(i % Ep);
-    wrT[i] = e < E ? wr[(int64_t)e * d + f] : (uint16_t)0;
+// The router weight in MFMA A-fragment order: for feature block fb (32
+// features), K step ks (16 experts) and lane l = 32*hh + n, the 8 values
+// W_r[ks*16 + 8*hh + j][fb*32 + fmap(n)], j = 0..7, with fmap(n) =
+// ((n>>2)&1)*16 + (n>>3)*4 + (n&3) (zero past E).  A wavefront then loads
+// one fragment as one contiguous kilobyte.
+__global__ __launch_bounds__(256) void router_pack_kernel(const uint16_t* __restrict__ wr,
+                                                          uint16_t* __restrict__ wfrag, int E, int d, int Ep) {
+  const int64_t total = (int64_t)d * Ep;
+  const int epk = Ep / 16;
+  for (int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x; o < total; o += (int64_t)gridDim.x * 256) {
+    const int j = (int)(o & 7);
+    const int l = (int)((o >> 3) & 63);
+    const int64_t q = o >> 9;
+    const int ks = (int)(q % epk), fb = (int)(q / epk);
+    const int hh = l >> 5, n = l & 31;
+    const int e = ks * 16 + 8 * hh + j;
+    const int f = fb * 32 + ((n >> 2) & 1) * 16 + (n >> 3) * 4 + (n & 3);
+    wfrag[o] = e < E ? wr[(int64_t)e * d + f] : (uint16_t)0;
   }
 }
 
 __device__ __forceinline__ bf16x8 ld8(const uint16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
-__device__ __forceinline__ void add16(float (&v)[16], const bf16* row) {
-  const uint4* p = reinterpret_cast<const uint4*>(row);
-  const uint4 a = p[0], b = p[1];
-  const uint32_t u[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    v[2 * q] += lo16(u[q]);
-    v[2 * q + 1] += hi16(u[q]);
-  }
-}
+// Workgroup: 32 tokens, all d features in chunks of 256.  Per chunk, phase
+// 1: wave w computes the router term for the 32 tokens (MFMA columns) and
+// features 64w .. +63 of the chunk (two 32-row MFMA blocks; row l&31 is
+// feature fmap(l&31), so accumulator register r of lane l is feature
+// 16*(l>>5) + r of its block) and writes it to LDS as [token][feature] fp32.
+// Phase 2: wave w takes tokens 8w .. 8w+7, two per instruction (half a
+// wavefront covers a token's 256 features as 16-byte vectors), adds the
+// token's gathered dX_disp rows and the router term and stores the row
+// segment.  One workgroup walks each token's rows from start to end, and its
+// B fragments (the tokens' logit gradient) are loaded once for all chunks.
+// The gathered rows of a chunk are issued after its operand loads (loads
+// complete in order, so the K loop never waits on them).  EPK = Ep / 16 K
+// steps (0: no router term).
+constexpr int kIgTok = 32, kIgFeat = 256, kIgPitch = kIgFeat + 4;
 
-// Workgroup tile: 64 tokens x 256 features; wave w takes tokens
-// 32*(w&1) .. +31 (MFMA columns) and features 128*(w>>1) .. +127 (four
-// 32-row MFMA blocks).  Lane l's MFMA row l&31 reads feature fmap(l&31), so
-// that accumulator register r of lane l is feature 16*(l>>5) + r of its block.
-template <bool ROUTER>
-__global__ __launch_bounds__(256) void input_grad_kernel(InputGradArgs a) {
-  const int d = a.d, k = a.k, Ep = a.Ep;
-  const int nft = (d + 255) / 256;
-  const int64_t tile = blockIdx.x;
-  const int ft = (int)(tile % nft);
-  const int64_t tt = tile / nft;
+template <int EPK>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) void input_grad_kernel(InputGradArgs a) {
+  __shared__ __attribute__((aligned(16))) float tile[EPK > 0 ? kIgTok : 1][kIgPitch];
+  constexpr int Ep = EPK * 16;
+  constexpr bool HOIST = false;       // B fragments reloaded per chunk (L1 hits): registers go to occupancy
+  const int d = a.d, k = a.k;
+  const int64_t t0 = (int64_t)blockIdx.x * kIgTok;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 31, hh = lane >> 5;
-  const int64_t tb = tt * 64 + (wave & 1) * 32 + n;
-  const int fw = ft * 256 + (wave >> 1) * 128;
-  const bool tv = tb < a.T;
-  f32x16 acc[4];
+
+  // phase 2: this lane's token pair rows (token 8w + 2i + hh), -1 if none
+  int64_t rw0[4], rw1[4];
 #pragma unroll
-  for (int b = 0; b < 4; ++b)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[b][r] = 0.f;
-  if constexpr (ROUTER) {
-    const int fm = ((n >> 2) & 1) * 16 + (n >> 3) * 4 + (n & 3);
-    const uint16_t* brow = a.dl_hl + (tv ? tb : 0) * 2 * Ep + 8 * hh;
-    const bf16x8 zero = {};
-    for (int kk = 0; kk < Ep; kk += 16) {
-      const bf16x8 bh = tv ? ld8(brow + kk) : zero;
-      const bf16x8 bl = tv ? ld8(brow + Ep + kk) : zero;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int fb = fw + 32 * b;
-        if (fb < d) {
-          const bf16x8 av = ld8(a.wrT + (int64_t)(fb + fm) * Ep + kk + 8 * hh);
-          acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bh, acc[b], 0, 0, 0);
-          acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bl, acc[b], 0, 0, 0);
-        }
+  for (int i = 0; i < 4; ++i) {
+    const int64_t t = t0 + 8 * wave + 2 * i + hh;
+    rw0[i] = rw1[i] = -1;
+    if (t < a.T) {
+      const int s0 = a.slot[t * k];
+      if (s0 >= 0) rw0[i] = (int64_t)a.offset[a.idx[t * k]] + s0;
+      if (k == 2) {
+        const int s1 = a.slot[t * k + 1];
+        if (s1 >= 0) rw1[i] = (int64_t)a.offset[a.idx[t * k + 1]] + s1;
       }
     }
   }
-  if (!tv) return;
-  int64_t r0 = -1, r1 = -1;
-  {
-    const int s0 = a.slot[tb * k];
-    if (s0 >= 0) r0 = (int64_t)a.offset[a.idx[tb * k]] + s0;
-    if (k == 2) {
-      const int s1 = a.slot[tb * k + 1];
-      if (s1 >= 0) r1 = (int64_t)a.offset[a.idx[tb * k + 1]] + s1;
+
+  // phase 1 operands
+  const int64_t tb = t0 + n;
+  const bool tv = tb < a.T;
+  const bf16x8 zero = {};
+  const uint16_t* brow = EPK > 0 ? a.dl_hl + (tv ? tb : 0) * 2 * Ep + 8 * hh : nullptr;
+  bf16x8 bh[HOIST ? (EPK > 0 ? EPK : 1) : 1], bl[HOIST ? (EPK > 0 ? EPK : 1) : 1];
+  if constexpr (HOIST && EPK > 0) {
+#pragma unroll
+    for (int ks = 0; ks < EPK; ++ks) {
+      bh[ks] = tv ? ld8(brow + ks * 16) : zero;
+      bl[ks] = tv ? ld8(brow + Ep + ks * 16) : zero;
     }
   }
+
+  for (int f0 = 0; f0 < d; f0 += kIgFeat) {
+    const int fl = f0 + 8 * n;            // phase 2: this lane's 8 features
+    const bool fin = fl < d;
+    uint4 g0[4], g1[4];
+    auto gather = [&]() {
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const int f0 = fw + 32 * b + 16 * hh;
-    if (fw + 32 * b >= d) break;
-    float v[16];
+      for (int i = 0; i < 4; ++i) {
+        g0[i] = g1[i] = make_uint4(0u, 0u, 0u, 0u);
+        if (fin && rw0[i] >= 0) g0[i] = *reinterpret_cast<const uint4*>(a.dx_disp + rw0[i] * d + fl);
+        if (fin && rw1[i] >= 0) g1[i] = *reinterpret_cast<const uint4*>(a.dx_disp + rw1[i] * d + fl);
+      }
+    };
+    if constexpr (EPK > 0) {
+      const int fw = f0 + 64 * wave;
+      const int nb = min(2, (d - fw) / 32);     // valid feature blocks (wave-uniform, may be <= 0)
+      f32x16 acc[2];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) v[r] = 0.f;
-    if (r0 >= 0) add16(v, a.dx_disp + r0 * d + f0);
-    if (r1 >= 0) add16(v, a.dx_disp + r1 * d + f0);
-    if constexpr (ROUTER) {
+      for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) v[r] += acc[b][r];
+        for (int r = 0; r < 16; ++r) acc[b][r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < EPK; ++ks) {
+        bf16x8 h, l;
+        if constexpr (HOIST) {
+          h = bh[ks];
+          l = bl[ks];
+        } else {
+          h = tv ? ld8(brow + ks * 16) : zero;
+          l = tv ? ld8(brow + Ep + ks * 16) : zero;
+        }
+        bf16x8 av[2];
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+          av[b] = b < nb ? ld8(a.wfrag + (((int64_t)(fw / 32 + b) * EPK + ks) * 64 + lane) * 8) : zero;
+        if (ks == EPK - 1) {
+          __builtin_amdgcn_sched_barrier(0);
+          gather();
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // hi products of both blocks, then lo: never two MFMAs back to back on one accumulator
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+          if (b < nb) acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[b], h, acc[b], 0, 0, 0);
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+          if (b < nb) acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[b], l, acc[b], 0, 0, 0);
+      }
+      __syncthreads();   // the previous chunk's phase 2 has read the tile
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        float4* dst = reinterpret_cast<float4*>(&tile[n][64 * wave + 32 * b + 16 * hh]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          dst[q] = make_float4(acc[b][4 * q], acc[b][4 * q + 1], acc[b][4 * q + 2], acc[b][4 * q + 3]);
+      }
+      __syncthreads();
+    } else {
+      gather();
     }
-    uint4* p = reinterpret_cast<uint4*>(a.dx + tb * d + f0);
-    p[0] = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
-                      pack_bf16x2(v[6], v[7]));
-    p[1] = make_uint4(pack_bf16x2(v[8], v[9]), pack_bf16x2(v[10], v[11]), pack_bf16x2(v[12], v[13]),
-                      pack_bf16x2(v[14], v[15]));
+
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tl = 8 * wave + 2 * i + hh;
+      const int64_t t = t0 + tl;
+      if (t >= a.T || !fin) continue;
+      const uint32_t u0[4] = {g0[i].x, g0[i].y, g0[i].z, g0[i].w};
+      const uint32_t u1[4] = {g1[i].x, g1[i].y, g1[i].z, g1[i].w};
+      float v[8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[2 * q] = lo16(u0[q]) + lo16(u1[q]);
+        v[2 * q + 1] = hi16(u0[q]) + hi16(u1[q]);
+      }
+      if constexpr (EPK > 0) {
+        const float4 r0 = *reinterpret_cast<const float4*>(&tile[tl][8 * n]);
+        const float4 r1 = *reinterpret_cast<const float4*>(&tile[tl][8 * n + 4]);
+        v[0] += r0.x; v[1] += r0.y; v[2] += r0.z; v[3] += r0.w;
+        v[4] += r1.x; v[5] += r1.y; v[6] += r1.z; v[7] += r1.w;
+      }
+      *reinterpret_cast<uint4*>(a.dx + t * d + fl) = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                                                pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+    }
   }
 }
 
@@ -437,22 +540,22 @@ __global__ __launch_bounds__(256) void router_reduce_kernel(const float4* __rest
   dw[i] = s;
 }
 
-// db[e] = sum of the gate-backward workgroups' partial sums: 64 experts per
-// workgroup, the four waves take contiguous quarters of the partial rows and
-// are added in wave order.
-__global__ __launch_bounds__(256) void db_reduce_kernel(const float* __restrict__ dbpart, int nb, int E,
+// db[e] = sum of the gate-backward workgroups' partial sums dbpart[e][0..nb):
+// one workgroup per expert, thread i adding partials i, i+256, ... in order,
+// then a fixed-order tree over the threads.
+__global__ __launch_bounds__(256) void db_reduce_kernel(const float* __restrict__ dbpart, int nb,
                                                         float* __restrict__ db) {
-  __shared__ float s[4][64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int e = blockIdx.x * 64 + lane;
-  const int per = (nb + 3) / 4;
-  const int b0 = wave * per, b1 = min(nb, b0 + per);
+  __shared__ float s[256];
+  const int e = blockIdx.x;
   float acc = 0.f;
-  if (e < E)
-    for (int b = b0; b < b1; ++b) acc += dbpart[(int64_t)b * E + e];
-  s[wave][lane] = acc;
+  for (int b = threadIdx.x; b < nb; b += 256) acc += dbpart[(int64_t)e * nb + b];
+  s[threadIdx.x] = acc;
   __syncthreads();
-  if (wave == 0 && e < E) db[e] = ((s[0][lane] + s[1][lane]) + s[2][lane]) + s[3][lane];
+  for (int w = 128; w >= 1; w >>= 1) {
+    if ((int)threadIdx.x < w) s[threadIdx.x] += s[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) db[e] = s[0];
 }
 
 __global__ __launch_bounds__(256) void zero_bytes_kernel(uint4* __restrict__ p16, size_t n16,
@@ -511,22 +614,31 @@ hipError_t launch_gate_backward(const GateBwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_router_transpose(const void* w_router, uint16_t* wrT, int E, int d, int Ep, hipStream_t s) {
+hipError_t launch_router_pack(const void* w_router, uint16_t* wfrag, int E, int d, int Ep, hipStream_t s) {
   const int64_t n = (int64_t)d * Ep;
   int64_t blocks = (n + 255) / 256;
   if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(router_transpose_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
-                     static_cast<const uint16_t*>(w_router), wrT, E, d, Ep);
+  hipLaunchKernelGGL(router_pack_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(w_router), wfrag, E, d, Ep);
   return hipGetLastError();
 }
 
 hipError_t launch_input_grad(const InputGradArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
-  const int64_t tiles = ((a.T + 63) / 64) * ((a.d + 255) / 256);
-  if (a.dl_hl)
-    hipLaunchKernelGGL(input_grad_kernel<true>, dim3((unsigned)tiles), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(input_grad_kernel<false>, dim3((unsigned)tiles), dim3(256), 0, s, a);
+  const int64_t tiles = (a.T + kIgTok - 1) / kIgTok;
+  const dim3 grid((unsigned)tiles);
+  switch (a.dl_hl ? a.Ep / 16 : 0) {
+    case 0: hipLaunchKernelGGL(input_grad_kernel<0>, grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL(input_grad_kernel<2>, grid, dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL(input_grad_kernel<4>, grid, dim3(256), 0, s, a); break;
+    case 6: hipLaunchKernelGGL(input_grad_kernel<6>, grid, dim3(256), 0, s, a); break;
+    case 8: hipLaunchKernelGGL(input_grad_kernel<8>, grid, dim3(256), 0, s, a); break;
+    case 10: hipLaunchKernelGGL(input_grad_kernel<10>, grid, dim3(256), 0, s, a); break;
+    case 12: hipLaunchKernelGGL(input_grad_kernel<12>, grid, dim3(256), 0, s, a); break;
+    case 14: hipLaunchKernelGGL(input_grad_kernel<14>, grid, dim3(256), 0, s, a); break;
+    case 16: hipLaunchKernelGGL(input_grad_kernel<16>, grid, dim3(256), 0, s, a); break;
+    default: return hipErrorNotSupported;
+  }
   return hipGetLastError();
 }
 
@@ -551,7 +663,7 @@ hipError_t launch_router_wgrad(const RouterWgradArgs& a, hipStream_t s) {
   }
   if (a.db_router) {
     const int nb = (int)((a.T + kGateBwdTokens - 1) / kGateBwdTokens);
-    hipLaunchKernelGGL(db_reduce_kernel, dim3((a.E + 63) / 64), dim3(256), 0, s, a.dbpart, nb, a.E, a.db_router);
+    hipLaunchKernelGGL(db_reduce_kernel, dim3(a.E), dim3(256), 0, s, a.dbpart, nb, a.db_router);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;

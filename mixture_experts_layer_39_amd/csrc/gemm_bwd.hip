@@ -339,16 +339,52 @@ __global__ __launch_bounds__(256) void bwd_gemm_kernel(BwdGemm g) {
   }
 }
 
-// colsum[e][j] = sum over the rows of expert e of M[row][j]  (fp32)
+// Column sums over each expert's packed rows, out[e][c] = sum of M[r][c] for
+// the rows r of e (fp32, in a fixed order).  Workgroup: 256 columns of one
+// expert; thread = (group of 8 columns, row lane 0..7): the 32 column groups
+// of a row lane read one row's 512 contiguous bytes, four rows in flight per
+// thread; the eight row lanes are added in order through LDS.
 __global__ __launch_bounds__(256) void colsum_kernel(const bf16* __restrict__ M, const int32_t* __restrict__ offset,
                                                      float* __restrict__ out, int ncols) {
+  __shared__ float red[8][257];
   const int e = blockIdx.y;
-  const int j = blockIdx.x * 256 + threadIdx.x;
-  if (j >= ncols) return;
+  const int cg = threadIdx.x & 31, rl = threadIdx.x >> 5;
+  const int c0 = blockIdx.x * 256 + cg * 8;
   const int r0 = offset[e], r1 = offset[e + 1];
-  float s = 0.f;
-  for (int r = r0; r < r1; ++r) s += static_cast<float>(M[(int64_t)r * ncols + j]);
-  out[(int64_t)e * ncols + j] = s;
+  float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  auto add = [&](const uint4 v) {
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      s[2 * q] += __uint_as_float(u[q] << 16);
+      s[2 * q + 1] += __uint_as_float(u[q] & 0xffff0000u);
+    }
+  };
+  if (c0 < ncols) {
+    const bf16* base = M + c0;
+    int r = r0 + rl;
+    for (; r + 24 < r1; r += 32) {
+      const uint4 a = *reinterpret_cast<const uint4*>(base + (int64_t)r * ncols);
+      const uint4 b = *reinterpret_cast<const uint4*>(base + (int64_t)(r + 8) * ncols);
+      const uint4 c = *reinterpret_cast<const uint4*>(base + (int64_t)(r + 16) * ncols);
+      const uint4 d = *reinterpret_cast<const uint4*>(base + (int64_t)(r + 24) * ncols);
+      add(a);
+      add(b);
+      add(c);
+      add(d);
+    }
+    for (; r < r1; r += 8) add(*reinterpret_cast<const uint4*>(base + (int64_t)r * ncols));
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) red[rl][cg * 8 + i] = s[i];
+  __syncthreads();
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c < ncols) {
+    float t = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) t += red[i][threadIdx.x];
+    out[(int64_t)e * ncols + c] = t;
+  }
 }
 
 template <int LA, int LB, int MODE, int EPI>

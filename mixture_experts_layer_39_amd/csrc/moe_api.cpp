@@ -66,7 +66,7 @@ struct Layout {
   // backward regions (save_preact == 1 only)
   int Ep;
   RouterChunks rc;
-  size_t logits, dwg, dlg, dl_hl, wrT, top1, coef, dbpart, choff, wpart;
+  size_t logits, dwg, dlg, dl_hl, wfrag, top1, coef, dbpart, choff, wpart;
   size_t total;
 };
 
@@ -107,7 +107,7 @@ Layout layout_of(const moe_config* c) {
   L.dwg = take(train ? (size_t)L.T * k * 4 : 0);
   L.dlg = take(train ? (size_t)L.T * E * 4 : 0);
   L.dl_hl = take(train ? (size_t)L.T * 2 * L.Ep * 2 : 0);
-  L.wrT = take(train ? (size_t)d * L.Ep * 2 : 0);
+  L.wfrag = take(train ? (size_t)d * L.Ep * 2 : 0);
   L.top1 = take(train ? (size_t)kTop1Parts * E * 4 : 0);
   L.coef = take(train ? (size_t)E * 4 : 0);
   L.dbpart = take(train ? nbt * E * 4 : 0);
@@ -445,14 +445,14 @@ moe_status run_input_grad(const moe_config* c, const Layout& L, const void* dx_d
   g.slot = slot;
   g.offset = offset;
   g.dl_hl = w_router ? at<uint16_t>(ws, L.dl_hl) : nullptr;
-  g.wrT = at<uint16_t>(ws, L.wrT);
+  g.wfrag = at<uint16_t>(ws, L.wfrag);
   g.dx = static_cast<bf16*>(dx);
   g.T = L.T;
   g.d = c->hidden_size;
   g.k = c->k;
   g.Ep = L.Ep;
   if (w_router)
-    MOE_TRY_HIP(launch_router_transpose(w_router, at<uint16_t>(ws, L.wrT), c->num_experts, c->hidden_size, L.Ep, s));
+    MOE_TRY_HIP(launch_router_pack(w_router, at<uint16_t>(ws, L.wfrag), c->num_experts, c->hidden_size, L.Ep, s));
   MOE_TRY_HIP(launch_input_grad(g, s));
   return MOE_OK;
 }

@@ -140,7 +140,7 @@ inline RouterChunks router_chunks(int64_t T, int d, int E) {
 }
 constexpr int kRouterMaxChunks = 256;
 constexpr int kTop1Parts = 64;          // workgroups of the top-1 histogram
-constexpr int kGateBwdTokens = 128;     // tokens per gate-backward workgroup
+constexpr int kGateBwdTokens = 32;      // tokens per gate-backward workgroup
 
 hipError_t launch_combine_backward(const void* dout, const void* y_disp, const int32_t* expert_idx,
                                    const int32_t* slot, const float* weight, const int32_t* expert_offset,
@@ -154,7 +154,7 @@ struct GateBwdArgs {
   const float* coef;        // [E] dloss*E*ce_e/T (BALANCE), or null
   float* dlogits;           // [T, E]: output (from logits) or input
   uint16_t* dl_hl;          // [T, 2*Ep] bf16 hi/lo split, or null
-  float* dbpart;            // [ceil(T/kGateBwdTokens), E] column partial sums, or null
+  float* dbpart;            // [E, ceil(T/kGateBwdTokens)] column partial sums, or null
   int64_t T;
   int32_t E, k, Ep, normalize;
 };
@@ -168,12 +168,12 @@ struct InputGradArgs {
   const int32_t* slot;      // [T, k]
   const int32_t* offset;    // [E+1]
   const uint16_t* dl_hl;    // [T, 2*Ep] or null (no router term)
-  const uint16_t* wrT;      // [d, Ep] router weight, transposed and padded
+  const uint16_t* wfrag;    // [d * Ep] router weight in MFMA fragment order, zero padded
   bf16* dx;                 // [T, d]
   int64_t T;
   int32_t d, k, Ep;
 };
-hipError_t launch_router_transpose(const void* w_router, uint16_t* wrT, int E, int d, int Ep, hipStream_t s);
+hipError_t launch_router_pack(const void* w_router, uint16_t* wfrag, int E, int d, int Ep, hipStream_t s);
 hipError_t launch_input_grad(const InputGradArgs& a, hipStream_t s);
 
 // dW_r (fp32 [E, d], nullable) and db_r (fp32 [E], nullable) from the split
@@ -181,7 +181,7 @@ hipError_t launch_input_grad(const InputGradArgs& a, hipStream_t s);
 struct RouterWgradArgs {
   const void* x;            // [T, d] bf16
   const uint16_t* dl_hl;    // [T, 2*Ep]
-  const float* dbpart;      // [ceil(T/kGateBwdTokens), E]
+  const float* dbpart;      // [E, ceil(T/kGateBwdTokens)]
   int32_t* choff;
   float* part;
   float* dw_router;
