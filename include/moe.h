@@ -131,7 +131,7 @@ moe_status moe_workspace_size(const moe_config* cfg, size_t* bytes);
  * exclusive prefix of expert_count (E+1 entries).
  *   x          device, [T, d] dtype            (ignored if logits_in)
  *   w_router   device, [E, d] dtype            (ignored if logits_in)
- *   b_router   device, [E] fp32, nullable
+ *   b_router   device, [E] fp32, nullable  (ignored if logits_in)
  *   logits_in  device, [T, E] fp32, nullable
  *   logits_out device, [T, E] fp32, nullable: the logits used
  *   expert_idx device, [T, k] int32 out;  slot device, [T, k] int32 out

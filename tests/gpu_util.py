@@ -93,3 +93,30 @@ def close(got, want, rtol):
         raise AssertionError(f"{int(bad.sum())}/{bad.size} outside tolerance; worst at {i}: got {got[i]!r} "
                              f"want {want[i]!r} (rtol {rtol}, rms {rms:.3g}); normwise "
                              f"{np.linalg.norm(got - want) / max(np.linalg.norm(want), 1e-300):.3g}")
+
+
+def with_given_logits(inp):
+    """Make a drawn workload's routing input explicit: its drawn logits plus
+    the workload's router bias (if any), given to both the GPU (logits_in)
+    and the oracle, so that both route identical logits."""
+    if inp.get("logits") is None:
+        raise ValueError("draw the workload with logits_given=True")
+    if inp.get("b_router") is not None:
+        inp["logits"] = inp["logits"] + inp["b_router"][None, :]
+        inp["b_router"] = None
+    return inp
+
+
+def unambiguous_topk(logits, k, bound):
+    """Tokens whose top-k choice (and its order) cannot change under a
+    perturbation of every logit by at most ``bound`` (per element): the gaps
+    between consecutive ones of the k+1 largest exceed twice the bound."""
+    L = np.asarray(logits, np.float64)
+    B = np.broadcast_to(np.asarray(bound, np.float64), L.shape)
+    order = np.argsort(-L, axis=1, kind="stable")
+    top = np.take_along_axis(L, order, axis=1)
+    btop = np.take_along_axis(B, order, axis=1)
+    ok = np.ones(L.shape[0], bool)
+    for j in range(min(k, L.shape[1] - 1)):
+        ok &= (top[:, j] - top[:, j + 1]) > (btop[:, j] + btop[:, j + 1])
+    return ok

@@ -13,7 +13,7 @@ import torch
 from mixture_experts_layer_39_amd import binding as B
 from mixture_experts_layer_39_amd.synthetic import make_inputs, spec
 from oracle import moe_oracle as O
-from tests.gpu_util import cfg_of, gate_np, run_gate, workspace
+from tests.gpu_util import cfg_of, gate_np, run_gate, unambiguous_topk, workspace
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -109,10 +109,24 @@ def test_router_gemm_and_routing(name, T):
     w = inp["w_router"].float().cpu().numpy().astype(np.float64)
     b = None if inp["b_router"] is None else inp["b_router"].cpu().numpy().astype(np.float64)
     want = O.router_logits(x, w, b)
+    bound = _router_bound(x, w, sp["d"]) + (0 if b is None else 1e-6)
     err = np.abs(g["logits"] - want)
-    assert (err <= _router_bound(x, w, sp["d"]) + (0 if b is None else 1e-6)).all()
+    assert (err <= bound).all()
     assert np.linalg.norm(g["logits"] - want) / np.linalg.norm(want) < 1e-5
-    check_routing(cfg, g["logits"], g)
+    # the oracle's own routing of its own logits: the same top-k on every
+    # token whose choice no perturbation within the bound can change
+    r = O.route(O.store(want, "f32"), cfg.k, cfg.capacity_factor, cfg.min_capacity, bool(cfg.drop_tokens))
+    sure = unambiguous_topk(want, cfg.k, bound)
+    assert sure.mean() > 0.5
+    np.testing.assert_array_equal(g["idx"][sure], r["expert_idx"][sure])
+    # the router path hands exactly its logits to the selection: a second
+    # gate given those logits (whose routing is checked bit-exact against the
+    # oracle above) returns the same bits
+    lg = torch.from_numpy(g["logits"].astype(np.float32)).to(DEV)
+    g2 = gate_np(run_gate(cfg, inp, DEV, logits_in=lg))
+    for key in ("logits", "idx", "slot", "weight", "count", "offset"):
+        np.testing.assert_array_equal(g2[key], g[key])
+    assert g2["loss"] == g["loss"]
 
 
 def test_gate_is_deterministic_and_reuses_workspace():

@@ -3,8 +3,11 @@ against the CPU oracle, through the C ABI, on the five workloads' shapes.
 
 Bar (tolerance of the bf16 / fp32 outputs, elementwise):
   |g - o| <= rtol*|o| + rtol*rms(o),  rtol = 2e-2 for bf16, 1e-5 for fp32;
-x_disp (a pure copy) and all routing outputs bit-exact.  The oracle runs on
-the GPU's router logits, whose own parity is checked in test_gpu_gate.
+x_disp (a pure copy) and all routing outputs bit-exact.  Both sides route
+the same drawn logits (the workload's logits drawn N(0,1), plus its router
+bias where it has one), given to the GPU as logits_in; the router GEMM's own
+parity, and that the router path hands exactly its logits to the same
+selection, are checked in test_gpu_gate and in the full-size test here.
 Small sizes run the whole oracle; the full sizes check the routing of every
 token, the dispatch permutation of every row, and the output of sampled
 tokens computed one by one."""
@@ -15,7 +18,7 @@ import torch
 from mixture_experts_layer_39_amd import binding as B
 from mixture_experts_layer_39_amd.synthetic import make_inputs, spec
 from oracle import moe_oracle as O
-from tests.gpu_util import alloc_gate, cfg_of, close, experts, f64, i64, workspace
+from tests.gpu_util import alloc_gate, cfg_of, close, experts, f64, i64, with_given_logits, workspace
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -53,14 +56,13 @@ PARITY = [("tiny_fp32", 64), ("tiny_fp32", 61), ("top2_e8", 4096), ("top2_e8", 1
 
 @pytest.mark.parametrize("name,T", PARITY, ids=lambda v: str(v))
 def test_layer_parity_small(name, T):
-    sp = spec(name, T=T)
-    inp = make_inputs(sp, DEV)
+    sp = spec(name, T=T, logits_given=True)
+    inp = with_given_logits(make_inputs(sp, DEV))
     cfg = cfg_of(sp, save_preact=1)
     g, out, ws, v = run_fused(sp, inp, cfg)
     torch.cuda.synchronize()
-    logits = f64(g["logits"])
-    if inp["logits"] is not None:
-        np.testing.assert_array_equal(logits, f64(inp["logits"]))
+    logits = f64(inp["logits"])
+    np.testing.assert_array_equal(f64(g["logits"]), logits)
     x, w1, b1, w2, b2 = oracle_inputs(inp)
     r = O.layer_forward(x, logits, w1, b1, w2, b2, k=sp["k"], capacity_factor=sp["cf"],
                         min_capacity=sp["min_cap"], drop_tokens=sp["drop"], act=sp["act"], dtype=sp["dtype"])
@@ -82,9 +84,6 @@ def test_layer_parity_small(name, T):
     y_gpu = f64(view(v["y"], n, sp["d"], tdt, ws))
     close(y_gpu, r["y_disp"], rt)
     close(f64(out), r["out"], rt)
-    # combine alone, on the GPU's own expert outputs
-    want_comb = O.combine(y_gpu, r["expert_idx"], r["slot"], r["weight"], r["expert_offset"], T, sp["dtype"])
-    close(f64(out), want_comb, rt)
     # dropped tokens are zero rows
     dropped = np.where((r["slot"] < 0).all(axis=1))[0]
     if dropped.size:
@@ -128,13 +127,13 @@ FULL = ["top2_e8", "top2_e64", "skew_e16", "nodrop_e128"]
 
 @pytest.mark.parametrize("name", FULL)
 def test_layer_full_size_sampled(name):
-    sp = spec(name)
-    inp = make_inputs(sp, DEV)
+    sp = spec(name, logits_given=True)
+    inp = with_given_logits(make_inputs(sp, DEV))
     cfg = cfg_of(sp)
     g, out, ws, v = run_fused(sp, inp, cfg)
     torch.cuda.synchronize()
     T, E, k, d = sp["T"], sp["E"], sp["k"], sp["d"]
-    logits = f64(g["logits"])
+    logits = f64(inp["logits"])
     r = O.route(logits, k, sp["cf"], sp["min_cap"], sp["drop"])
     np.testing.assert_array_equal(i64(g["idx"]), r["expert_idx"])
     np.testing.assert_array_equal(i64(g["slot"]), r["slot"])
@@ -155,17 +154,10 @@ def test_layer_full_size_sampled(name):
     toks = torch.arange(T, device=DEV)[:, None].expand(T, k)
     assert torch.equal(xd[rows[kept]], inp["x"][toks[kept]])
     assert int(kept.sum()) == n
-    # sampled logits against the oracle's router on those rows
     rng = np.random.default_rng(3)
     sample = np.unique(np.concatenate([rng.choice(T, 40, replace=False),
                                        np.where((r["slot"] < 0).any(axis=1))[0][:8], [0, T - 1]]))
     xs = f64(inp["x"][torch.from_numpy(sample).to(DEV)])
-    w = f64(inp["w_router"])
-    b = None if inp["b_router"] is None else f64(inp["b_router"])
-    want = O.router_logits(xs, w, b)
-    u = 2.0 ** -24
-    bound = d * u / (1 - d * u) * (np.abs(xs) @ np.abs(w).T) + 1e-6
-    assert (np.abs(logits[sample] - want) <= bound).all()
     # sampled outputs, one token at a time, with the (bit-exact) routing
     _, w1, b1, w2, b2 = oracle_inputs(inp)
     got = f64(out[torch.from_numpy(sample).to(DEV)])
@@ -173,6 +165,36 @@ def test_layer_full_size_sampled(name):
                                          [r["weight"][t, j] for j in range(k) if r["slot"][t, j] >= 0],
                                          w1, b1, w2, b2, sp["act"], sp["dtype"]) for i, t in enumerate(sample)])
     close(got, want_out, RTOL[sp["dtype"]])
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_router_path_full_size(name):
+    """The fused forward with the router at full size: sampled logits within
+    the fp32 dot-product bound of the oracle's router, and the same output
+    bits as the fused forward given those logits (whose parity is checked
+    above)."""
+    sp = spec(name)
+    inp = make_inputs(sp, DEV)
+    cfg = cfg_of(sp)
+    g, out, ws, _ = run_fused(sp, inp, cfg)
+    out = out.clone()
+    torch.cuda.synchronize()
+    T, d = sp["T"], sp["d"]
+    rng = np.random.default_rng(4)
+    sample = np.unique(np.concatenate([rng.choice(T, 40, replace=False), [0, T - 1]]))
+    xs = f64(inp["x"][torch.from_numpy(sample).to(DEV)])
+    w = f64(inp["w_router"])
+    b = None if inp["b_router"] is None else f64(inp["b_router"])
+    want = O.router_logits(xs, w, b)
+    u = 2.0 ** -24
+    bound = d * u / (1 - d * u) * (np.abs(xs) @ np.abs(w).T) + 1e-6
+    assert (np.abs(f64(g["logits"])[sample] - want) <= bound).all()
+    given = dict(inp, logits=g["logits"].clone(), w_router=None, b_router=None)
+    g2, out2, _, _ = run_fused(sp, given, cfg, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out2, out)
+    for key in ("idx", "slot", "weight", "count", "loss"):
+        assert torch.equal(g2[key], g[key]), key
 
 
 def test_empty_batch():
@@ -208,12 +230,13 @@ def test_everything_to_one_expert_drops_the_rest():
 @pytest.mark.parametrize("E,k,d,h", [(1, 1, 8, 8), (256, 2, 64, 32), (200, 2, 128, 0), (3, 2, 24, 40)])
 def test_odd_shapes(E, k, d, h):
     T = 333
-    sp = spec("top2_e8", T=T, E=E, k=k, d=d, h=h, act=B.MOE_ACT_GELU if h else B.MOE_ACT_NONE, cf=1.5)
-    inp = make_inputs(sp, DEV)
+    sp = spec("top2_e8", T=T, E=E, k=k, d=d, h=h, act=B.MOE_ACT_GELU if h else B.MOE_ACT_NONE, cf=1.5,
+              logits_given=True)
+    inp = with_given_logits(make_inputs(sp, DEV))
     cfg = cfg_of(sp, normalize_topk=1, loss_kind=B.MOE_LOSS_USAGE_STD)
     g, out, _, _ = run_fused(sp, inp, cfg)
     torch.cuda.synchronize()
-    logits = f64(g["logits"])
+    logits = f64(inp["logits"])
     x, w1, b1, w2, b2 = oracle_inputs(inp)
     r = O.layer_forward(x, logits, w1, b1, w2, b2, k=k, capacity_factor=1.5, min_capacity=sp["min_cap"],
                         drop_tokens=True, act=sp["act"], dtype="bf16", normalize_topk=True,
