@@ -124,7 +124,10 @@ moe_status moe_workspace_size(const moe_config* cfg, size_t* bytes);
  * logits[t,e] = x[t]·w_router[e] (+ b_router[e]) accumulated in fp32, or
  * logits_in when it is non-NULL (then x / w_router are not read).
  * p = softmax over the E logits; the k chosen experts are the k largest
- * logits, ties to the lower expert index (-0.0 equals +0.0).
+ * logits, ties to the lower expert index (-0.0 equals +0.0).  Non-finite
+ * logits are outside the contract, but the chosen experts are always valid
+ * indices: a NaN ranks as -inf, so a token whose logits are all -inf or NaN
+ * takes the lowest indices.
  * Capacity slots: every top-1 claim in token order, then every top-2 claim in
  * token order, takes the next free slot of its expert; a slot >= C is dropped
  * (slot = -1).  expert_count[e] = kept claims of e, expert_offset the

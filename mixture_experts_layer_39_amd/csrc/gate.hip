@@ -59,15 +59,23 @@ __device__ __forceinline__ void merge_best(float& v, int& i, int mask) {
   }
 }
 
+// Router GEMM K chunk staged in LDS per step: 256 for up to 64 experts, 128
+// for 128, 64 for 256, so that the double-buffered weight chunk stays at
+// 64 KB at most; a long chunk keeps more bytes in flight per barrier.
+template <int EP>
+constexpr int gate_kc() { return EP <= 64 ? 256 : EP <= 128 ? 128 : 64; }
+
 template <int EP, int TG, int MODE>
 __global__ __launch_bounds__(256) void gate_kernel(GateArgs a) {
   constexpr int NET = EP / 16;   // 16-expert MFMA row tiles
   constexpr int TT = TG * 16;    // tokens per tile
-  constexpr size_t RED_BYTES = (MODE == MODE_BF16) ? size_t(4) * TG * NET * 64 * 16 : 0;
+  constexpr int KC = gate_kc<EP>();
+  constexpr int CPR = KC / 8;    // 16-byte chunks per weight row of a K chunk
+  constexpr size_t W_BYTES = (MODE == MODE_BF16) ? size_t(2) * EP * KC * 2 : 0;
+  static_assert(MODE != MODE_BF16 || TG == 4, "the router GEMM gives each wave its own 16 tokens");
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  f32x4* red = reinterpret_cast<f32x4*>(smem);                       // [4][TG][NET][64]
-  int* s_sel = reinterpret_cast<int*>(smem + RED_BYTES);              // [2][TT]
+  int* s_sel = reinterpret_cast<int*>(smem + W_BYTES);                // [2][TT]
   int* s_rnk = s_sel + 2 * TT;                                        // [2][TT]
   float* s_me = reinterpret_cast<float*>(s_rnk + 2 * TT);             // [TG][EP]
   const int tid = threadIdx.x;
@@ -82,65 +90,83 @@ __global__ __launch_bounds__(256) void gate_kernel(GateArgs a) {
   // lg[et][r] = logit of expert et*16 + q*4 + r for token t0 + wave*16 + n
   float lg[NET][4];
   if constexpr (MODE == MODE_BF16) {
+    // Each wave computes its own 16 tokens over the whole hidden dimension,
+    // so no cross-wave reduction is needed.  The router weight streams
+    // through LDS in K chunks of KC (double-buffered, loaded once per
+    // workgroup and read by all four waves); chunk c of weight row r sits in
+    // slot c ^ (r & 15), so the 16 rows one fragment read touches fall in 16
+    // different banks.  The x fragments come straight from global memory,
+    // one K step ahead.
     const bf16* x = static_cast<const bf16*>(a.x);
     const bf16* w = static_cast<const bf16*>(a.w_router);
     const int d = a.d;
-    f32x4 acc[NET][TG];
-#pragma unroll
-    for (int et = 0; et < NET; ++et)
-#pragma unroll
-      for (int g = 0; g < TG; ++g) acc[et][g] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int nsteps = (d + KC - 1) / KC;
+    constexpr int WL = EP * CPR / 256;   // weight chunk loads per thread and step
     const bf16x8 zero8 = {};
-    const int nsteps = (d + 127) / 128;
-    for (int ms = wave; ms < nsteps; ms += 4) {
-      const int kb = ms * 128 + q * 32;
-      bf16x8 xb[TG][4];
+    auto load_w = [&](int ks, bf16x8 (&wr)[WL]) {
 #pragma unroll
-      for (int g = 0; g < TG; ++g) {
-        const int64_t t = t0 + g * 16 + n;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int kk = kb + i * 8;
-          xb[g][i] = (t < T && kk < d) ? ld_bf16x8(x + t * d + kk) : zero8;
-        }
+      for (int j = 0; j < WL; ++j) {
+        const int c = tid + 256 * j;
+        const int row = c / CPR, col = c % CPR;
+        const int kk = ks * KC + col * 8;
+        wr[j] = (row < E && kk < d) ? ld_bf16x8(w + (int64_t)row * d + kk) : zero8;
       }
+    };
+    auto store_w = [&](int buf, const bf16x8 (&wr)[WL]) {
+      unsigned char* base = smem + (size_t)buf * EP * KC * 2;
+#pragma unroll
+      for (int j = 0; j < WL; ++j) {
+        const int c = tid + 256 * j;
+        const int row = c / CPR, col = c % CPR;
+        *reinterpret_cast<bf16x8*>(base + (size_t)row * KC * 2 + ((col ^ (row & 15)) % CPR) * 16) = wr[j];
+      }
+    };
+    const int64_t tx = t0 + wave * 16 + n;
+    auto load_x = [&](int ks, bf16x8 (&xb)[KC / 32]) {
+#pragma unroll
+      for (int i = 0; i < KC / 32; ++i) {
+        const int kk = ks * KC + q * (KC / 4) + i * 8;
+        xb[i] = (tx < T && kk < d) ? ld_bf16x8(x + tx * d + kk) : zero8;
+      }
+    };
+    f32x4 acc[NET];
+#pragma unroll
+    for (int et = 0; et < NET; ++et) acc[et] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bf16x8 wr[WL], xb[KC / 32], xn[KC / 32];
+    load_w(0, wr);
+    load_x(0, xb);
+    store_w(0, wr);
+    __syncthreads();
+    for (int ks = 0; ks < nsteps; ++ks) {
+      const bool more = ks + 1 < nsteps;
+      if (more) {
+        load_w(ks + 1, wr);
+        load_x(ks + 1, xn);
+      }
+      const unsigned char* wb = smem + (size_t)(ks & 1) * EP * KC * 2;
+      // fragment i covers K values q*(KC/4) + 8i .. +7 of the chunk for lane
+      // quarter q (the same order on both operands)
 #pragma unroll
       for (int et = 0; et < NET; ++et) {
-        const int e = et * 16 + n;
-        bf16x8 wa[4];
+        const int row = et * 16 + n;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int kk = kb + i * 8;
-          wa[i] = (e < E && kk < d) ? ld_bf16x8(w + (int64_t)e * d + kk) : zero8;
+        for (int i = 0; i < KC / 32; ++i) {
+          const int col = q * (KC / 32) + i;
+          const bf16x8 wa = *reinterpret_cast<const bf16x8*>(wb + (size_t)row * KC * 2 + ((col ^ (row & 15)) % CPR) * 16);
+          acc[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, xb[i], acc[et], 0, 0, 0);
         }
-#pragma unroll
-        for (int g = 0; g < TG; ++g)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            acc[et][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[i], xb[g][i], acc[et][g], 0, 0, 0);
       }
+      if (more) {
+        store_w((ks + 1) & 1, wr);
+#pragma unroll
+        for (int i = 0; i < KC / 32; ++i) xb[i] = xn[i];
+      }
+      __syncthreads();
     }
 #pragma unroll
     for (int et = 0; et < NET; ++et)
 #pragma unroll
-      for (int g = 0; g < TG; ++g) red[((wave * TG + g) * NET + et) * 64 + lane] = acc[et][g];
-    __syncthreads();
-    if (wave < TG) {
-#pragma unroll
-      for (int et = 0; et < NET; ++et) {
-        f32x4 s = red[((0 * TG + wave) * NET + et) * 64 + lane];
-#pragma unroll
-        for (int ws = 1; ws < 4; ++ws) {
-          const f32x4 o = red[((ws * TG + wave) * NET + et) * 64 + lane];
-          s[0] += o[0];
-          s[1] += o[1];
-          s[2] += o[2];
-          s[3] += o[3];
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) lg[et][r] = s[r];
-      }
-    }
+      for (int r = 0; r < 4; ++r) lg[et][r] = acc[et][r];
   } else if constexpr (MODE == MODE_F32) {
     if (wave < TG) {
       const float* x = static_cast<const float*>(a.x);
@@ -210,16 +236,20 @@ __global__ __launch_bounds__(256) void gate_kernel(GateArgs a) {
     sum += __shfl_xor(sum, 16);
     sum += __shfl_xor(sum, 32);
 
-    // top-1
+    // top-1, by (value desc, index asc).  The selection key of a NaN logit
+    // is -inf and the running index starts past every expert, so that even a
+    // token whose logits are all -inf or NaN (outside the contract) gets a
+    // valid expert (the lowest index) and no later step indexes out of range.
     float v0 = -INFINITY;
-    int i0 = 0x7fffffff;
+    int i0 = E;
 #pragma unroll
     for (int et = 0; et < NET; ++et)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int e = et * 16 + q * 4 + r;
-        if (e < E && lg[et][r] > v0) {
-          v0 = lg[et][r];
+        const float key = lg[et][r] != lg[et][r] ? -INFINITY : lg[et][r];
+        if (e < E && (key > v0 || (key == v0 && e < i0))) {
+          v0 = key;
           i0 = e;
         }
       }
@@ -227,15 +257,16 @@ __global__ __launch_bounds__(256) void gate_kernel(GateArgs a) {
     merge_best(v0, i0, 32);
     // top-2 (best other than the top-1)
     float v1 = -INFINITY;
-    int i1 = 0x7fffffff;
+    int i1 = E;
     if (K == 2) {
 #pragma unroll
       for (int et = 0; et < NET; ++et)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int e = et * 16 + q * 4 + r;
-          if (e < E && e != i0 && lg[et][r] > v1) {
-            v1 = lg[et][r];
+          const float key = lg[et][r] != lg[et][r] ? -INFINITY : lg[et][r];
+          if (e < E && e != i0 && (key > v1 || (key == v1 && e < i1))) {
+            v1 = key;
             i1 = e;
           }
         }
@@ -442,9 +473,9 @@ __global__ void gate_empty_kernel(int32_t* count, int32_t* offset, float* loss, 
 
 template <int EP, int TG, int MODE>
 size_t gate_lds_bytes() {
-  constexpr int NET = EP / 16, TT = TG * 16;
-  size_t red = (MODE == MODE_BF16) ? size_t(4) * TG * NET * 64 * 16 : 0;
-  return red + 4 * (2 * TT + 2 * TT + TG * EP);
+  constexpr int TT = TG * 16;
+  const size_t wbytes = (MODE == MODE_BF16) ? size_t(2) * EP * gate_kc<EP>() * 2 : 0;
+  return wbytes + 4 * (2 * TT + 2 * TT + TG * EP);
 }
 
 template <int EP, int TG, int MODE>
@@ -467,7 +498,7 @@ hipError_t launch_gate_mode(const GateArgs& a, hipStream_t s) {
   if (E <= 32) return launch_gate_t<32, 4, MODE>(a, s);
   if (E <= 64) return launch_gate_t<64, 4, MODE>(a, s);
   if (E <= 128) return launch_gate_t<128, 4, MODE>(a, s);
-  return launch_gate_t<256, 2, MODE>(a, s);
+  return launch_gate_t<256, 4, MODE>(a, s);
 }
 
 }  // namespace

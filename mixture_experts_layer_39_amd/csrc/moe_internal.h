@@ -29,9 +29,8 @@ enum { ACT_NONE = 0, ACT_RELU = 1, ACT_GELU = 2 };
 enum { LOSS_BALANCE = 0, LOSS_USAGE_STD = 1 };
 
 // ---------------------------------------------------------------- gate
-// Tokens per gate tile: 64 (4 groups of 16) while the padded expert count is
-// at most 128, else 32, so the cross-wave logit reduction fits in LDS.
-inline int gate_tile_tokens(int E) { return E <= 128 ? 64 : 32; }
+// Tokens per gate tile: 64, four groups of 16, one per wavefront.
+inline int gate_tile_tokens(int) { return 64; }
 
 struct GateArgs {
   const void* x;            // [T, d] dtype (router GEMM modes)

@@ -139,3 +139,25 @@ def test_gate_is_deterministic_and_reuses_workspace():
     for key in ("logits", "idx", "slot", "weight", "count", "offset"):
         np.testing.assert_array_equal(g1[key], g2[key])
     assert g1["loss"] == g2["loss"]
+
+
+def test_non_finite_logits_give_valid_experts():
+    """Regression: a token whose logits are all NaN or -inf must still get
+    valid expert indices (the lowest ones), so that no later step indexes
+    outside its buffers; finite tokens of the same batch route as usual."""
+    T, E = 300, 64
+    rng = np.random.default_rng(17)
+    L = rng.normal(size=(T, E)).astype(np.float32)
+    L[3] = np.nan
+    L[7] = -np.inf
+    L[11, 5] = np.nan             # one NaN among finite values ranks last
+    L[11, 9] = 40.0
+    cfg = B.make_config(T, 64, E, 2, 1.0, 4, True, 0, B.MOE_ACT_NONE, B.MOE_BF16)
+    g = gate_np(run_gate(cfg, {}, DEV, logits_in=torch.from_numpy(L).to(DEV)))
+    assert ((g["idx"] >= 0) & (g["idx"] < E)).all()
+    assert g["idx"][3].tolist() == [0, 1] and g["idx"][7].tolist() == [0, 1]
+    assert g["idx"][11, 0] == 9 and g["idx"][11, 1] != 5
+    assert g["count"].sum() == g["offset"][E] and (g["count"] >= 0).all()
+    fin = np.isfinite(L).all(axis=1)
+    r = O.route(np.where(np.isfinite(L), L, -np.inf).astype(np.float64), 2, 1.0, 4, True)
+    np.testing.assert_array_equal(g["idx"][fin], r["expert_idx"][fin])
