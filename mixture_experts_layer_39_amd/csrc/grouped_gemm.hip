@@ -57,32 +57,6 @@ __device__ __forceinline__ float act_apply(float v, int act) {
   return v;
 }
 
-// GELU(x) = x * Phi(x) with erf from Abramowitz & Stegun, Handbook of
-// Mathematical Functions, formula 7.1.26: for z >= 0,
-//   erf(z) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-z^2),
-//   t = 1 / (1 + p z),  |error| <= 1.5e-7,
-// extended to z < 0 by oddness.  Branch-free: one reciprocal, one exp.
-__device__ __forceinline__ float gelu_fast(float x) {
-  const float z = fabsf(x) * 0.7071067811865476f;
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.f));
-  float poly = fmaf(1.061405429f, t, -1.453152027f);
-  poly = fmaf(poly, t, 1.421413741f);
-  poly = fmaf(poly, t, -0.284496736f);
-  poly = fmaf(poly, t, 0.254829592f);
-  poly *= t;
-  const float e = __builtin_amdgcn_exp2f(-z * z * 1.4426950408889634f);
-  const float erf_abs = fmaf(-poly, e, 1.f);
-  const float erf_v = __builtin_copysignf(erf_abs, x);
-  return 0.5f * x * (1.f + erf_v);
-}
-
-template <int ACT>
-__device__ __forceinline__ float act_fixed(float v) {
-  if constexpr (ACT == ACT_RELU) return fmaxf(v, 0.f);
-  else if constexpr (ACT == ACT_GELU) return gelu_fast(v);
-  else return v;
-}
-
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) { return pack_bf16x2(lo, hi); }
 
 // Tile scheduler shared by the kernels: per-expert row-tile prefix (exclusive)

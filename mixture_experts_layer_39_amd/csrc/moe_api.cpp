@@ -63,6 +63,7 @@ struct Layout {
   int tiles, tile_tokens;
   size_t tile_cnt, me_tile, me_sum, demand, idx, slot, weight, offset;
   size_t x_disp, a_save, h_disp, y_disp, d_act;
+  size_t dec_logits, dec_prob, dec_bar;   // small-batch forward: logits, probabilities, barrier
   // backward regions (save_preact == 1 only)
   int Ep;
   RouterChunks rc;
@@ -99,6 +100,9 @@ Layout layout_of(const moe_config* c) {
   L.h_disp = take(h > 0 ? (size_t)L.rows * h * s : 0);
   L.y_disp = take((size_t)L.rows * d * s);
   L.d_act = take(h > 0 ? (size_t)L.rows * h * s : 0);
+  L.dec_logits = take(L.T <= kDecodeMaxTokens ? (size_t)L.T * E * 4 : 0);
+  L.dec_prob = take(L.T <= kDecodeMaxTokens ? (size_t)L.T * E * 4 : 0);
+  L.dec_bar = take(L.T <= kDecodeMaxTokens ? 4096 : 0);
   const bool train = c->save_preact != 0;
   L.Ep = router_ep(E);
   L.rc = train ? router_chunks(L.T, d, E) : RouterChunks{0, 0};
@@ -365,6 +369,46 @@ moe_status moe_layer_forward(const moe_config* cfg, const void* x, const void* w
   int32_t* sl = slot ? slot : at<int32_t>(ws, L.slot);
   float* wt = weight ? weight : at<float>(ws, L.weight);
   int32_t* off = at<int32_t>(ws, L.offset);
+  // a few tokens, inference: the whole forward in one cooperative launch
+  if (!cfg->save_preact && decode_fits(L.T, cfg->hidden_size, cfg->ffn_hidden, cfg->num_experts, cfg->k,
+                                       cfg->dtype)) {
+    DecodeArgs da{};
+    da.x = static_cast<const bf16*>(x);
+    da.w_router = static_cast<const bf16*>(w_router);
+    da.b_router = b_router;
+    da.logits_in = logits_in;
+    da.logits = logits_out ? logits_out : at<float>(ws, L.dec_logits);
+    da.w1 = static_cast<const bf16*>(w1);
+    da.b1 = static_cast<const bf16*>(b1);
+    da.w2 = static_cast<const bf16*>(w2);
+    da.b2 = static_cast<const bf16*>(b2);
+    da.out = static_cast<bf16*>(out);
+    da.gate_loss = gate_loss;
+    da.expert_count = expert_count;
+    da.expert_offset = off;
+    da.expert_idx = idx;
+    da.slot = sl;
+    da.weight = wt;
+    da.x_disp = at<bf16>(ws, L.x_disp);
+    da.h_disp = cfg->ffn_hidden > 0 ? at<bf16>(ws, L.h_disp) : nullptr;
+    da.y_disp = at<bf16>(ws, L.y_disp);
+    da.prob = at<float>(ws, L.dec_prob);
+    da.bar = at<unsigned>(ws, L.dec_bar);
+    da.C = L.C;
+    da.T = (int32_t)L.T;
+    da.d = cfg->hidden_size;
+    da.h = cfg->ffn_hidden;
+    da.E = cfg->num_experts;
+    da.k = cfg->k;
+    da.normalize = cfg->normalize_topk;
+    da.loss_kind = cfg->loss_kind;
+    da.act = cfg->activation;
+    const hipError_t e = launch_decode(da, s);
+    if (e == hipSuccess) return MOE_OK;
+    // a grid that cannot be co-resident on this device takes the multi-kernel path
+    if (e != hipErrorCooperativeLaunchTooLarge && e != hipErrorNotSupported) return MOE_ERR_HIP;
+    (void)hipGetLastError();
+  }
   // training: the backward needs the logits, so keep them when the caller does not
   float* lg = (logits_out || !cfg->save_preact) ? logits_out : at<float>(ws, L.logits);
   st = run_gate(cfg, L, x, w_router, b_router, logits_in, lg, idx, sl, wt, expert_count, off, gate_loss, ws, s);

@@ -28,6 +28,33 @@ enum { DT_F32 = 0, DT_BF16 = 1 };
 enum { ACT_NONE = 0, ACT_RELU = 1, ACT_GELU = 2 };
 enum { LOSS_BALANCE = 0, LOSS_USAGE_STD = 1 };
 
+// GELU(x) = x * Phi(x) with erf from Abramowitz & Stegun, Handbook of
+// Mathematical Functions, formula 7.1.26: for z >= 0,
+//   erf(z) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-z^2),
+//   t = 1 / (1 + p z),  |error| <= 1.5e-7,
+// extended to z < 0 by oddness.  Branch-free: one reciprocal, one exp.
+__device__ __forceinline__ float gelu_fast(float x) {
+  const float z = fabsf(x) * 0.7071067811865476f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.f));
+  float poly = fmaf(1.061405429f, t, -1.453152027f);
+  poly = fmaf(poly, t, 1.421413741f);
+  poly = fmaf(poly, t, -0.284496736f);
+  poly = fmaf(poly, t, 0.254829592f);
+  poly *= t;
+  const float e = __builtin_amdgcn_exp2f(-z * z * 1.4426950408889634f);
+  const float erf_abs = fmaf(-poly, e, 1.f);
+  const float erf_v = __builtin_copysignf(erf_abs, x);
+  return 0.5f * x * (1.f + erf_v);
+}
+
+template <int ACT>
+__device__ __forceinline__ float act_fixed(float v) {
+  if constexpr (ACT == ACT_RELU) return fmaxf(v, 0.f);
+  else if constexpr (ACT == ACT_GELU) return gelu_fast(v);
+  else return v;
+}
+
+
 // ---------------------------------------------------------------- gate
 // Tokens per gate tile: 64, four groups of 16, one per wavefront.
 inline int gate_tile_tokens(int) { return 64; }
@@ -192,6 +219,38 @@ hipError_t launch_router_wgrad(const RouterWgradArgs& a, hipStream_t s);
 // The chunked product on the large-tile GEMM: part[c] = dl_hl[chunk c]^T x[chunk c].
 hipError_t launch_router_partials(const uint16_t* dl_hl, const void* x, const int32_t* choff, float* part,
                                   int64_t T, int S, int d, int Ep, hipStream_t s);
+
+// ---------------------------------------------------------------- small-batch forward
+// The whole forward in one cooperative kernel for up to kDecodeMaxTokens
+// tokens (bf16, d and h multiples of 128, inference: no pre-activation kept).
+constexpr int kDecodeMaxTokens = 256;
+struct DecodeArgs {
+  const bf16* x;            // [T, d]
+  const bf16* w_router;     // [E, d] (unused with logits_in)
+  const float* b_router;    // [E] or null
+  const float* logits_in;   // [T, E] or null
+  float* logits;            // [T, E]: the logits used (caller's or workspace)
+  const bf16* w1;           // [E, n1, d], n1 = h (or d for a single Linear)
+  const bf16* b1;           // [E, n1] or null
+  const bf16* w2;           // [E, d, h] or null
+  const bf16* b2;           // [E, d] or null
+  bf16* out;                // [T, d]
+  float* gate_loss;
+  int32_t* expert_count;    // [E]
+  int32_t* expert_offset;   // [E+1]
+  int32_t* expert_idx;      // [T, k]
+  int32_t* slot;            // [T, k]
+  float* weight;            // [T, k]
+  bf16* x_disp;             // [rows, d]
+  bf16* h_disp;             // [rows, h]
+  bf16* y_disp;             // [rows, d]
+  float* prob;              // [T, E] softmax probabilities (BALANCE loss)
+  unsigned* bar;            // [1024] grid-barrier counters and status (zeroed per call)
+  int64_t C;                // capacity, < 0 = none
+  int32_t T, d, h, E, k, normalize, loss_kind, act;
+};
+bool decode_fits(int64_t T, int d, int h, int E, int k, int dtype);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 
 // Zero fill of n bytes (a kernel, so that it can sit in a captured graph).
 hipError_t launch_zero_bytes(void* p, size_t n, hipStream_t s);
