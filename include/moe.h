@@ -77,6 +77,9 @@ typedef enum { MOE_ACT_NONE = 0, MOE_ACT_RELU = 1, MOE_ACT_GELU = 2 } moe_act;
 typedef enum { MOE_LOSS_BALANCE = 0, MOE_LOSS_USAGE_STD = 1 } moe_loss_kind;
 
 #define MOE_MAX_EXPERTS 256
+/* Token counts of the fused small-batch forward (moe_config.small_batch). */
+#define MOE_SMALL_BATCH_MAX 256
+#define MOE_SMALL_BATCH_AUTO 64
 
 /* Layer configuration ([ds.moe] §2.1 MoE arguments). */
 typedef struct moe_config {
@@ -101,6 +104,12 @@ typedef struct moe_config {
                               Linear's pre-activation, and the logits when
                               logits_out is NULL), and the workspace has the
                               regions the *_backward calls below use          */
+  int32_t small_batch;     /* inference forward of a few tokens in one launch
+                              (the fused small-batch kernel, up to
+                              MOE_SMALL_BATCH_MAX tokens, bf16, d and h
+                              multiples of 128, save_preact == 0):
+                              0: when T <= MOE_SMALL_BATCH_AUTO;
+                              1: whenever it applies; -1: never               */
 } moe_config;
 
 /* Static text for a status code. */
@@ -203,7 +212,16 @@ moe_status moe_combine(const moe_config* cfg, const void* y_disp, const int32_t*
  * (nullable, shapes as in moe_gate); when NULL the workspace holds them.
  * x/w_router/b_router/logits_in as in moe_gate; w1/b1/w2/b2 as in
  * moe_expert_ffn.  Intermediates stay in the workspace; see
- * moe_workspace_views. */
+ * moe_workspace_views.
+ * Small batches at inference (cfg->small_batch, save_preact == 0) run as
+ * one persistent launch of one workgroup per CU ([ds.moe] §4 inference
+ * notes: gating and token assignment fused to save launches) with the same
+ * results: routing, slots, counts, offsets and packed rows identical, the
+ * floating-point outputs within rounding of the multi-kernel path (the
+ * router's K is split into slices added in order).  Its grid barriers wait
+ * a bounded time; on a device where some other kernel keeps CUs busy for
+ * seconds, a wait that runs out stops the kernel and sets *gate_loss to
+ * NaN (the other outputs are then undefined). */
 moe_status moe_layer_forward(const moe_config* cfg, const void* x, const void* w_router,
                              const float* b_router, const float* logits_in,
                              const void* w1, const void* b1, const void* w2, const void* b2,

@@ -20,18 +20,24 @@ class MoE:
     layer on the current stream and returns (output, gate_loss, expert_count).
 
     Arguments mirror MoE(hidden_size, num_experts, k, capacity_factor,
-    min_capacity, drop_tokens) of the deepspeed.moe overview (§2.1); the expert
-    is Linear(hidden, ffn_hidden) -> activation -> Linear(ffn_hidden, hidden),
+    eval_capacity_factor, min_capacity, drop_tokens) of the deepspeed.moe
+    overview (§2.1): capacity_factor applies in training mode (the default,
+    ``train()``), eval_capacity_factor after ``eval()``.  The expert is
+    Linear(hidden, ffn_hidden) -> activation -> Linear(ffn_hidden, hidden),
     or one Linear(hidden, hidden) when ffn_hidden == 0.  Weights use the
-    nn.Linear [out, in] layout, stacked over experts.
+    nn.Linear [out, in] layout, stacked over experts.  small_batch selects
+    the one-launch forward for a few tokens (0 automatic, 1 always when it
+    applies, -1 never).
     """
 
     def __init__(self, hidden_size, num_experts, w_router, w1, b1=None, w2=None, b2=None, b_router=None,
-                 k=1, capacity_factor=1.0, min_capacity=4, drop_tokens=True, ffn_hidden=0,
-                 activation=MOE_ACT_NONE, normalize_topk=False, loss_kind=MOE_LOSS_BALANCE):
+                 k=1, capacity_factor=1.0, eval_capacity_factor=1.0, min_capacity=4, drop_tokens=True,
+                 ffn_hidden=0, activation=MOE_ACT_NONE, normalize_topk=False, loss_kind=MOE_LOSS_BALANCE,
+                 small_batch=0):
         import torch
         self.hidden_size, self.num_experts, self.k = hidden_size, num_experts, k
         self.capacity_factor, self.min_capacity, self.drop_tokens = capacity_factor, min_capacity, drop_tokens
+        self.eval_capacity_factor, self.small_batch, self.training = eval_capacity_factor, small_batch, True
         self.ffn_hidden, self.activation = ffn_hidden, activation
         self.normalize_topk, self.loss_kind = normalize_topk, loss_kind
         self.w_router, self.b_router = w_router, b_router
@@ -39,10 +45,18 @@ class MoE:
         self.dtype = MOE_BF16 if w1.dtype == torch.bfloat16 else MOE_F32
         self._ws = None
 
+    def train(self, mode=True):
+        self.training = bool(mode)
+        return self
+
+    def eval(self):
+        return self.train(False)
+
     def config(self, num_tokens):
-        return make_config(num_tokens, self.hidden_size, self.num_experts, self.k, self.capacity_factor,
-                           self.min_capacity, self.drop_tokens, self.ffn_hidden, self.activation, self.dtype,
-                           self.normalize_topk, self.loss_kind)
+        cf = self.capacity_factor if self.training else self.eval_capacity_factor
+        return make_config(num_tokens, self.hidden_size, self.num_experts, self.k, cf, self.min_capacity,
+                           self.drop_tokens, self.ffn_hidden, self.activation, self.dtype, self.normalize_topk,
+                           self.loss_kind, small_batch=self.small_batch)
 
     def forward(self, x, logits=None):
         import torch

@@ -41,15 +41,16 @@ class MoeConfig(ctypes.Structure):
         ("normalize_topk", ctypes.c_int32),
         ("loss_kind", ctypes.c_int32),
         ("save_preact", ctypes.c_int32),
+        ("small_batch", ctypes.c_int32),
     ]
 
 
 def make_config(num_tokens, hidden_size, num_experts, k=1, capacity_factor=1.0, min_capacity=4,
                 drop_tokens=True, ffn_hidden=0, activation=MOE_ACT_NONE, dtype=MOE_BF16,
-                normalize_topk=False, loss_kind=MOE_LOSS_BALANCE, save_preact=False):
+                normalize_topk=False, loss_kind=MOE_LOSS_BALANCE, save_preact=False, small_batch=0):
     return MoeConfig(int(num_tokens), float(capacity_factor), int(hidden_size), int(num_experts), int(k),
                      int(min_capacity), int(bool(drop_tokens)), int(ffn_hidden), int(activation), int(dtype),
-                     int(bool(normalize_topk)), int(loss_kind), int(bool(save_preact)))
+                     int(bool(normalize_topk)), int(loss_kind), int(bool(save_preact)), int(small_batch))
 
 
 class MoeError(RuntimeError):

@@ -1,5 +1,5 @@
 // Small-batch (decode / evaluation) forward of the whole layer in one
-// cooperative kernel: router GEMM, softmax, top-k, capacity slots, counts,
+// persistent kernel: router GEMM, softmax, top-k, capacity slots, counts,
 // offsets, gate_loss, dispatch, both expert Linears and the combine.
 //
 // What is computed is the forward of "MoE混合专家架构：大模型高效推理的智能调度原理"
@@ -10,24 +10,28 @@
 // tokens the layer is one pass over the chosen experts' weights, and seven
 // launches of a few microseconds each would cost more than that pass.
 //
-// Design (gfx950), one workgroup per CU (a cooperative launch, so the grid
-// is co-resident), phases separated by grid barriers of our own: two levels
-// of arrival counters on separate cache lines, polled with a sleep (the
-// runtime's grid sync took 30-60 us per barrier here, one counter for all
-// workgroups about 10 us):
-//  1. Router logits: workgroup items of 16 experts x 16 tokens, the four
-//     wavefronts splitting K (v_mfma_f32_16x16x32_bf16), fp32 out.
-//  2. Routing: a wavefront per token (softmax max and sum, top-1 / top-2 by
-//     (value desc, index asc) with xor-shuffles), spread over the grid; then,
-//     after a barrier, every workgroup forms the capacity slots in claim
-//     order (all top-1 claims in token order, then all top-2) from 64-token
-//     chunks, where a lane's rank among equal experts comes from nine ballots
-//     over the bits of the expert id + 1, and keeps the packed row -> token
-//     map.  Workgroup 0 writes slots, counts, offsets and the loss.
-//  3. Expert Linear 1 (+ bias, activation): workgroup items of 16 output
-//     features of one expert; the four wavefronts split K and add their
-//     partial products through LDS in a fixed order; the token rows are
-//     gathered straight from x (dispatch fused in).
+// Design (gfx950): a plain launch of one workgroup per CU (so the whole grid
+// is resident), phases separated by grid barriers of our own: two levels of
+// arrival counters on separate cache lines, polled with a sleep (the
+// runtime's cooperative grid sync took 30-60 us per barrier here, and its
+// launch about 20 us more than a plain one):
+//  1. Router products: items of 16 experts x 16 tokens x one of ks slices of
+//     K (ks grows while the items fit the grid, so a few tokens still spread
+//     the router weight over many CUs), the four wavefronts splitting the
+//     slice (v_mfma_f32_16x16x32_bf16), fp32 partials.
+//  2. Routing: a wavefront per token adds the slices in order (+ bias), then
+//     softmax max and sum, top-1 / top-2 by (value desc, index asc) with
+//     xor-shuffles; then, after a barrier, every workgroup forms the capacity
+//     slots in claim order (all top-1 claims in token order, then all top-2)
+//     from 64-token chunks, where a lane's rank among equal experts comes
+//     from nine ballots over the bits of the expert id + 1, the offsets by a
+//     wavefront scan, and the packed row -> token map.  The last two
+//     workgroups write slots, counts, offsets and the loss.
+//  3. Expert Linear 1 (+ bias, activation): items of 16 output features of
+//     one expert; the four wavefronts split K, each streaming its weight
+//     quarter through a ring of loads that runs on across items, and add
+//     their partial products through LDS in a fixed order; the token rows
+//     are gathered straight from x (dispatch fused in).
 //  4. Expert Linear 2 (+ bias) on the packed hidden rows, the same way.
 //  5. Combine: out[t] = sum over kept choices, in order, of w * y_disp row.
 // The weights of the chosen experts are read once; every work loop has a
@@ -38,6 +42,7 @@ namespace moe {
 namespace {
 
 constexpr int kFB = 16;   // output features per work item (MFMA rows)
+constexpr int kRing = 16; // K-steps in flight per wavefront in the expert Linears
 
 __device__ __forceinline__ bf16x8 ldv(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
@@ -115,14 +120,17 @@ __device__ __forceinline__ float act_rt(float v, int act) {
 // which every workgroup polls with a sleep between reads.  Counters grow by
 // one per phase (zeroed by the init kernel that precedes the launch), so
 // phase p is complete when the top counter reaches p times the number of
-// groups.  The grid is co-resident (cooperative launch), so every wait
-// ends; the spin is bounded all the same, and a wait that gives up records
-// it in the status word.
+// groups.  The grid is one workgroup per CU and the kernel's resources allow
+// several per CU, so on a device not held by a kernel that never ends every
+// workgroup is resident and every wait ends.  The spin is bounded all the
+// same: a wait that gives up records it in the status word and returns
+// false, and the workgroup then stops (its reads would see data that was
+// never written) after setting gate_loss to NaN, the signal the caller sees.
 constexpr int kBarGroups = 16, kBarLine = 32;   // 32 words = 128 bytes
 constexpr int kBarTop = kBarGroups * kBarLine, kBarStatus = kBarTop + kBarLine;
 constexpr int kBarWords = kBarStatus + 1;
 
-__device__ __forceinline__ void grid_barrier(unsigned* bar, unsigned phase) {
+__device__ __forceinline__ bool grid_barrier(unsigned* bar, unsigned phase, int* ok) {
   __syncthreads();
   if (threadIdx.x == 0) {
     const unsigned nwg = gridDim.x;
@@ -137,16 +145,36 @@ __device__ __forceinline__ void grid_barrier(unsigned* bar, unsigned phase) {
     if (old + 1 == phase * gsize)
       __hip_atomic_fetch_add(&bar[kBarTop], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     unsigned spins = 0;
+    int done = 1;
     while (__hip_atomic_load(&bar[kBarTop], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < phase * groups) {
       __builtin_amdgcn_s_sleep(2);
-      if (++spins > (1u << 27)) {
+      if (++spins > (1u << 22)) {
         __hip_atomic_store(&bar[kBarStatus], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        done = 0;
         break;
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    *ok = done;
   }
   __syncthreads();
+  return *ok != 0;
+}
+
+// Sum over the workgroup's 256 threads in a fixed tree order (every thread
+// gets the total).
+__device__ double block_sum(double v, double* red) {
+  const int tid = threadIdx.x;
+  red[tid] = v;
+  __syncthreads();
+#pragma unroll
+  for (int m = 128; m >= 1; m >>= 1) {
+    if (tid < m) red[tid] += red[tid + m];
+    __syncthreads();
+  }
+  const double total = red[0];
+  __syncthreads();
+  return total;
 }
 
 // One token's softmax, top-1 / top-2 (value desc, index asc; a NaN ranks as
@@ -154,15 +182,34 @@ __device__ __forceinline__ void grid_barrier(unsigned* bar, unsigned phase) {
 // one wavefront with lane l holding experts l, l+64, ...  The probabilities
 // go to prob[t] when asked (the BALANCE loss sums them per expert).
 template <int EPL>
-__device__ void route_token(const DecodeArgs& a, const float* logits, int t, float* prob) {
+__device__ void route_token(const DecodeArgs& a, int t, float* prob) {
   const int lane = threadIdx.x & 63;
-  const int E = a.E, k = a.k;
+  const int E = a.E, k = a.k, T = a.T;
   float l[EPL];
   float mx = -INFINITY;
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
     const int e = lane + 64 * i;
-    l[i] = e < E ? logits[(int64_t)t * E + e] : -INFINITY;
+    if (e < E) {
+      if (a.logits_in) {
+        l[i] = a.logits_in[(int64_t)t * E + e];
+      } else {
+        // the K slices' partial products (all loads issued before the
+        // first add), added in slice order, then the bias
+        float pv[kDecodeMaxSlices];
+#pragma unroll
+        for (int sl = 0; sl < kDecodeMaxSlices; ++sl)
+          pv[sl] = sl < a.ks ? a.part[((int64_t)sl * T + t) * E + e] : 0.f;
+        float v = pv[0];
+#pragma unroll
+        for (int sl = 1; sl < kDecodeMaxSlices; ++sl)
+          if (sl < a.ks) v += pv[sl];
+        l[i] = v + (a.b_router ? a.b_router[e] : 0.f);
+      }
+      if (a.logits) a.logits[(int64_t)t * E + e] = l[i];
+    } else {
+      l[i] = -INFINITY;
+    }
     mx = fmaxf(mx, l[i]);
   }
   mx = gmax<64>(mx);
@@ -279,17 +326,41 @@ __device__ void assign_slots(const DecodeArgs& a, DecShared& S) {
     S.cnt[e] = (int)kept;
   }
   __syncthreads();
-  if (tid == 0) {
-    int acc = 0, it = 0;
+  if (wave == 0) {
+    // exclusive prefixes over experts: lane l holds experts 4l .. 4l+3
     const int nfb1 = ((a.h > 0 ? a.h : a.d) + kFB - 1) / kFB;
-    for (int e = 0; e < E; ++e) {
-      S.off[e] = acc;
-      S.ipre[e] = it;
-      acc += S.cnt[e];
-      it += S.cnt[e] > 0 ? nfb1 : 0;
+    int c[4], n = 0, it = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * lane + i;
+      c[i] = e < E ? S.cnt[e] : 0;
+      n += c[i];
+      it += c[i] > 0 ? nfb1 : 0;
     }
-    S.off[E] = acc;
-    S.ipre[E] = it;
+    int sn = n, sit = it;   // inclusive scans over lanes
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      const int un = __shfl_up(sn, m), uit = __shfl_up(sit, m);
+      if (lane >= m) {
+        sn += un;
+        sit += uit;
+      }
+    }
+    int acc = sn - n, iacc = sit - it;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * lane + i;
+      if (e < E) {
+        S.off[e] = acc;
+        S.ipre[e] = iacc;
+      }
+      acc += c[i];
+      iacc += c[i] > 0 ? nfb1 : 0;
+    }
+    if (lane == 63) {
+      S.off[E] = sn;
+      S.ipre[E] = sit;
+    }
   }
   __syncthreads();
   for (int i = tid; i < k * T; i += 256) {
@@ -302,38 +373,26 @@ __device__ void assign_slots(const DecodeArgs& a, DecShared& S) {
 
 // gate_loss, by workgroup 0: BALANCE = E * sum_e mean_t p[t,e] * (top-1
 // share of e), USAGE_STD = population std of the usage + 1e-6 (double).
-__device__ void write_loss(const DecodeArgs& a, const float* prob, DecShared& S) {
+__device__ float compute_loss(const DecodeArgs& a, const float* prob, DecShared& S) {
   const int tid = threadIdx.x;
   const int T = a.T, E = a.E, k = a.k;
-  double part = 0.0;
   if (a.loss_kind == LOSS_BALANCE) {
-    for (int e = tid; e < E; e += 256) {
+    // E * sum_e me_e * ce_e with me_e the mean probability, ce_e the top-1 share
+    double part = 0.0;
+    if (tid < E) {
       double me = 0.0;
-      for (int t = 0; t < T; ++t) me += (double)prob[(int64_t)t * E + e];
-      part += (me / (double)T) * ((double)S.run[0][e] / (double)T);
+      for (int t = 0; t < T; ++t) me += (double)prob[(int64_t)t * E + tid];
+      part = (me / (double)T) * ((double)S.run[0][tid] / (double)T);
     }
+    return (float)(block_sum(part, S.dred) * (double)E);
   }
-  S.dred[tid] = part;
-  __syncthreads();
-  if (tid == 0) {
-    double loss = 0.0;
-    if (a.loss_kind == LOSS_BALANCE) {
-      for (int i = 0; i < 256; ++i) loss += S.dred[i];
-      loss *= (double)E;
-    } else {
-      const double denom = (double)k * (double)T;
-      double mean = 0.0;
-      for (int e = 0; e < E; ++e) mean += (double)(S.run[0][e] + (k == 2 ? S.run[1][e] : 0)) / denom;
-      mean /= (double)E;
-      double var = 0.0;
-      for (int e = 0; e < E; ++e) {
-        const double u = (double)(S.run[0][e] + (k == 2 ? S.run[1][e] : 0)) / denom - mean;
-        var += u * u;
-      }
-      loss = sqrt(var / (double)E) + 1e-6;
-    }
-    *a.gate_loss = (float)loss;
-  }
+  // population standard deviation of the experts' shares of all k*T choices
+  const double denom = (double)k * (double)T;
+  const double u = tid < E ? (double)(S.run[0][tid] + (k == 2 ? S.run[1][tid] : 0)) / denom : 0.0;
+  const double mean = block_sum(u, S.dred) / (double)E;
+  const double dv = tid < E ? (u - mean) * (u - mean) : 0.0;
+  const double var = block_sum(dv, S.dred) / (double)E;
+  return (float)(sqrt(var) + 1e-6);
 }
 
 // One 16-output x 16-row block of a Linear, the four wavefronts splitting K
@@ -354,6 +413,131 @@ __device__ __forceinline__ f32x4 block_product(const bf16* wrow, const bf16* bro
   return s;
 }
 
+// Per-lane view of one work unit of an expert Linear: 16 output features of
+// one expert times one block of (up to) 16 of its rows.
+struct LinUnit {
+  const bf16* w;   // lane's weight row (feature f0 + lane % 16) at its K start
+  const bf16* b;   // lane's input row at the same K offset (a valid row when past the block's end)
+  int e, f0, rb;   // expert, first output feature, first row of the block
+};
+
+// One expert Linear (phase 1: x rows -> hidden with bias and activation,
+// phase 2: hidden rows -> y_disp with bias) over this workgroup's items
+// (blockIdx.x, + gridDim.x, ...; an item is 16 output features of one expert
+// with rows, split into 16-row blocks).  The four wavefronts split K into
+// quarters and add their partial products through LDS in wave order.  Each
+// wavefront keeps a ring of NB K-steps of (weight, input) fragments in
+// flight and refills a slot as soon as its product is issued, from the
+// current unit or, past its end, from the next one, so the weight stream
+// does not pause at unit boundaries.  A quarter whose step count is not a
+// multiple of NB is padded with steps that load a valid address and whose
+// products are skipped.
+template <int NB>
+__device__ void decode_linear(const DecodeArgs& a, DecShared& S, int phase) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n16 = lane & 15, q = lane >> 4;
+  const int E = a.E, d = a.d, h = a.h;
+  const int n1 = h > 0 ? h : d;
+  const int nfb1 = n1 / kFB;
+  const int K = phase == 1 ? d : h, nout = phase == 1 ? n1 : d;
+  const int nfb = nout / kFB;
+  const int items = phase == 1 ? S.ipre[E] : S.ipre[E] / nfb1 * nfb;
+  const int nst = K / 128;                       // K steps of 32 per wavefront
+  const int npad = (nst + NB - 1) / NB * NB;
+  const int kw = wave * nst * 32 + q * 8;        // lane's K offset
+  const bf16* W = phase == 1 ? a.w1 : a.w2;
+  const bf16* X = phase == 1 ? a.x : a.h_disp;
+  const bf16* bias = phase == 1 ? a.b1 : a.b2;
+  bf16* Y = (phase == 1 && h > 0) ? a.h_disp : a.y_disp;
+  const bool act = phase == 1;
+  const int nwg = gridDim.x;
+
+  auto unit = [&](int it, int rb) {
+    const int key = phase == 1 ? it : (it / nfb) * nfb1;   // the expert's first phase-1 item
+    int lo = 0, hi = E;                                     // expert e with ipre[e] <= key < ipre[e+1]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (S.ipre[mid] <= key) lo = mid; else hi = mid;
+    }
+    LinUnit u;
+    u.e = lo;
+    u.f0 = (phase == 1 ? it - S.ipre[lo] : it % nfb) * kFB;
+    u.rb = rb;
+    u.w = W + ((int64_t)lo * nout + u.f0 + n16) * K + kw;
+    const int rr = rb + n16;
+    const int r = S.off[lo] + (rr < S.cnt[lo] ? rr : 0);
+    u.b = X + (int64_t)(phase == 1 ? S.rowtok[r] : r) * K + kw;
+    return u;
+  };
+
+  int it = blockIdx.x;
+  if (it >= items) return;                       // uniform over the workgroup
+  LinUnit cur = unit(it, 0);
+  bf16x8 av[NB], bv[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const int s = j < nst ? j : nst - 1;
+    av[j] = ldv(cur.w + 32 * s);
+    bv[j] = ldv(cur.b + 32 * s);
+  }
+  for (;;) {
+    int nit = it, nrb = cur.rb + kFB;
+    if (nrb >= S.cnt[cur.e]) {
+      nit = it + nwg;
+      nrb = 0;
+    }
+    const bool more = nit < items;
+    const LinUnit nxt = more ? unit(nit, nrb) : cur;
+    // the unit's 16 biases come through scalar loads (a uniform address),
+    // whose counter is not the vector-memory one: waiting for them in the
+    // epilogue does not drain the ring of weight loads
+    uint32_t bw[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+    if (bias) {
+      const int eu = __builtin_amdgcn_readfirstlane(cur.e), fu = __builtin_amdgcn_readfirstlane(cur.f0);
+      typedef const __attribute__((address_space(4))) uint32_t* const_u32p;
+      const const_u32p bp = (const_u32p)(bias + (int64_t)eu * nout + fu);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) bw[i] = bp[i];
+    }
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int j0 = 0; j0 < npad; j0 += NB) {
+#pragma unroll
+      for (int jj = 0; jj < NB; ++jj) {
+        const int s = j0 + jj;
+        if (s < nst) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[jj], bv[jj], acc, 0, 0, 0);
+        const int s2 = s + NB;
+        const bool here = s2 < npad;
+        int ss = here ? s2 : s2 - npad;
+        ss = ss < nst ? ss : nst - 1;
+        av[jj] = ldv((here ? cur.w : nxt.w) + 32 * ss);
+        bv[jj] = ldv((here ? cur.b : nxt.b) + 32 * ss);
+      }
+    }
+    *reinterpret_cast<f32x4*>(S.red[wave][lane]) = acc;
+    __syncthreads();
+    const int rr = cur.rb + n16;
+    if (wave == 0 && rr < S.cnt[cur.e]) {
+      // lane holds row rr, outputs f0 + 4q .. +3
+      // this lane's outputs f0 + 4q .. +3 are the bf16 pairs 2q and 2q + 1
+      const uint32_t b0 = q == 0 ? bw[0] : q == 1 ? bw[2] : q == 2 ? bw[4] : bw[6];
+      const uint32_t b1 = q == 0 ? bw[1] : q == 1 ? bw[3] : q == 2 ? bw[5] : bw[7];
+      const float bv4[4] = {__uint_as_float(b0 << 16), __uint_as_float(b0 & 0xffff0000u),
+                            __uint_as_float(b1 << 16), __uint_as_float(b1 & 0xffff0000u)};
+      float v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[i] = (((S.red[0][lane][i] + S.red[1][lane][i]) + S.red[2][lane][i]) + S.red[3][lane][i]) + bv4[i];
+        if (act) v[i] = act_rt(v[i], a.act);
+      }
+      bf16* dst = Y + (int64_t)(S.off[cur.e] + rr) * nout + cur.f0 + 4 * q;
+      *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+    }
+    __syncthreads();
+    if (!more) break;
+    cur = nxt;
+    it = nit;
+  }
+}
+
 __global__ void decode_init_kernel(unsigned* bar) {
   for (int i = threadIdx.x; i < kBarWords; i += blockDim.x) bar[i] = 0u;
 }
@@ -365,44 +549,54 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const unsigned nwg = gridDim.x;
   const int n16 = lane & 15, q = lane >> 4;
 
+  __shared__ int bar_ok;
+  unsigned phase = 0;   // barriers passed (the counters' targets follow it)
+  // a barrier that gave up: the data it guards may be missing, so stop
+#define DECODE_BARRIER()                                  \
+  if (!grid_barrier(a.bar, ++phase, &bar_ok)) {           \
+    if (tid == 0) *a.gate_loss = __builtin_nanf("");      \
+    return;                                               \
+  }
+
   // ---------------------------------------------------------------- 1. logits
-  // workgroup items of 16 experts x 16 tokens, the four wavefronts splitting K
-  float* logits = a.logits;
+  // partial router products over a.ks slices of K: items of 16 experts x 16
+  // tokens x one slice, the four wavefronts splitting the slice (so that a
+  // few tokens still spread the router weight's read over many CUs); the
+  // routing phase adds the slices in order
   if (!a.logits_in) {
-    const int ne = (E + 15) / 16, nt = (T + 15) / 16;
-    for (int it = blockIdx.x; it < ne * nt; it += nwg) {
-      const int e0 = (it % ne) * 16, t0 = (it / ne) * 16;
+    const int ne = (E + 15) / 16, nt = (T + 15) / 16, ks = a.ks, kc = d / a.ks;
+    for (int it = blockIdx.x; it < ne * nt * ks; it += nwg) {
+      const int sl = it % ks, r = it / ks;
+      const int e0 = (r % ne) * 16, t0 = (r / ne) * 16;
       const int er = e0 + n16, tr = t0 + n16;
-      const bf16* wrow = a.w_router + (int64_t)(er < E ? er : 0) * d + q * 8;
-      const bf16* xrow = a.x + (int64_t)(tr < T ? tr : 0) * d + q * 8;
       // rows of the weight past E read expert 0's (their results are dropped)
-      const f32x4 acc = block_product(wrow, xrow, tr < T, d, S);
+      const bf16* wrow = a.w_router + (int64_t)(er < E ? er : 0) * d + sl * kc + q * 8;
+      const bf16* xrow = a.x + (int64_t)(tr < T ? tr : 0) * d + sl * kc + q * 8;
+      const f32x4 acc = block_product(wrow, xrow, tr < T, kc, S);
       if (wave == 0) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int e = e0 + 4 * q + i;
-          if (tr < T && e < E) logits[(int64_t)tr * E + e] = acc[i] + (a.b_router ? a.b_router[e] : 0.f);
+          if (tr < T && e < E) a.part[((int64_t)sl * T + tr) * E + e] = acc[i];
         }
       }
     }
-  } else if (a.logits) {
-    for (int64_t i = (int64_t)blockIdx.x * 256 + tid; i < (int64_t)T * E; i += (int64_t)nwg * 256)
-      logits[i] = a.logits_in[i];
+    DECODE_BARRIER();
   }
-  grid_barrier(a.bar, 1);
 
   // ---------------------------------------------------------------- 2. routing
-  const float* lg = a.logits_in ? a.logits_in : logits;
   float* prob = a.loss_kind == LOSS_BALANCE ? a.prob : nullptr;
   for (int t = blockIdx.x * 4 + wave; t < T; t += nwg * 4) {
-    if (E <= 64) route_token<1>(a, lg, t, prob);
-    else if (E <= 128) route_token<2>(a, lg, t, prob);
-    else if (E <= 192) route_token<3>(a, lg, t, prob);
-    else route_token<4>(a, lg, t, prob);
+    if (E <= 64) route_token<1>(a, t, prob);
+    else if (E <= 128) route_token<2>(a, t, prob);
+    else if (E <= 192) route_token<3>(a, t, prob);
+    else route_token<4>(a, t, prob);
   }
-  grid_barrier(a.bar, 2);
+  DECODE_BARRIER();
   assign_slots(a, S);
-  if (blockIdx.x == 0) {
+  // the caller's outputs of the routing go from the last workgroups, which
+  // have the fewest Linear items when the items do not divide evenly
+  if (blockIdx.x == nwg - 1) {
     for (int i = tid; i < k * T; i += 256) {
       const int t = i / k, j = i - t * k;
       a.slot[i] = S.slot[j][t];
@@ -411,7 +605,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       if (e < E) a.expert_count[e] = S.cnt[e];
       a.expert_offset[e] = S.off[e];
     }
-    write_loss(a, prob, S);
+  }
+  if (blockIdx.x == (nwg >= 2 ? nwg - 2 : 0)) {
+    const float loss = compute_loss(a, prob, S);
+    if (tid == 0) *a.gate_loss = loss;
   }
   // the packed copy of the token rows (x_disp), a row per workgroup in turn
   const int nrows = S.off[E];
@@ -421,73 +618,14 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     for (int v = tid; v < d / 8; v += 256) dst[v] = src[v];
   }
 
-  // ---------------------------------------------------------------- 3. Linear 1
-  const int n1 = h > 0 ? h : d;          // output features of the first Linear
-  const int nfb1 = (n1 + kFB - 1) / kFB;
-  for (int it = blockIdx.x; it < S.ipre[E]; it += nwg) {
-    int lo = 0, hi = E;                  // the expert e with ipre[e] <= it < ipre[e+1]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (S.ipre[mid] <= it) lo = mid; else hi = mid;
-    }
-    const int e = lo, f0 = (it - S.ipre[e]) * kFB;
-    const int rows = S.cnt[e], r0 = S.off[e];
-    const bf16* wrow = a.w1 + ((int64_t)e * n1 + f0 + n16) * d + q * 8;
-    for (int rb = 0; rb < rows; rb += 16) {
-      const int rr = rb + n16;
-      const bool rv = rr < rows;
-      const bf16* xrow = a.x + (int64_t)S.rowtok[r0 + (rv ? rr : 0)] * d + q * 8;
-      const f32x4 acc = block_product(wrow, xrow, rv, d, S);
-      if (wave == 0 && rv) {
-        // lane holds row rr, outputs f0 + 4q .. +3
-        float v[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int f = f0 + 4 * q + i;
-          const float b = a.b1 ? static_cast<float>(a.b1[(int64_t)e * n1 + f]) : 0.f;
-          v[i] = act_rt(acc[i] + b, a.act);
-        }
-        bf16* dst = (h > 0 ? a.h_disp : a.y_disp) + (int64_t)(r0 + rr) * n1 + f0 + 4 * q;
-        *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-      }
-    }
-  }
-  grid_barrier(a.bar, 3);
-
-  // ---------------------------------------------------------------- 4. Linear 2
+  // ---------------------------------------------------------------- 3./4. Linears
+  decode_linear<kRing>(a, S, 1);
+  DECODE_BARRIER();
   if (h > 0) {
-    const int nfb2 = (d + kFB - 1) / kFB;
-    const int items = S.ipre[E] / nfb1 * nfb2;   // experts with rows x output blocks
-    for (int it = blockIdx.x; it < items; it += nwg) {
-      const int ew = it / nfb2, fb = it - ew * nfb2;
-      const int key = ew * nfb1;         // the ew-th expert with rows
-      int lo = 0, hi = E;
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (S.ipre[mid] <= key) lo = mid; else hi = mid;
-      }
-      const int e = lo, f0 = fb * kFB;
-      const int rows = S.cnt[e], r0 = S.off[e];
-      const bf16* wrow = a.w2 + ((int64_t)e * d + f0 + n16) * h + q * 8;
-      for (int rb = 0; rb < rows; rb += 16) {
-        const int rr = rb + n16;
-        const bool rv = rr < rows;
-        const bf16* hrow = a.h_disp + (int64_t)(r0 + (rv ? rr : 0)) * h + q * 8;
-        const f32x4 acc = block_product(wrow, hrow, rv, h, S);
-        if (wave == 0 && rv) {
-          float v[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int f = f0 + 4 * q + i;
-            v[i] = acc[i] + (a.b2 ? static_cast<float>(a.b2[(int64_t)e * d + f]) : 0.f);
-          }
-          bf16* dst = a.y_disp + (int64_t)(r0 + rr) * d + f0 + 4 * q;
-          *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-        }
-      }
-    }
+    decode_linear<kRing>(a, S, 2);
+    DECODE_BARRIER();
   }
-  grid_barrier(a.bar, 4);
+#undef DECODE_BARRIER
 
   // ---------------------------------------------------------------- 5. combine
   const int nv = d / 8;
@@ -527,16 +665,23 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
   if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
   if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel, 256, 0)) != hipSuccess) return e;
-  if (per_cu < 1) return hipErrorNotSupported;
-  hipLaunchKernelGGL(decode_init_kernel, dim3(1), dim3(256), 0, s, a.bar);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  // one workgroup per CU (more per CU measured slower: the redundant slot
-  // pass and the barriers grow with the grid)
+  // one workgroup per CU: the whole grid is resident at once
+  if (per_cu < 1 || cus < 1) return hipErrorNotSupported;
   const int grid = cus;
   DecodeArgs args = a;
-  void* params[] = {&args};
-  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(decode_kernel), dim3(grid), dim3(256), params, 0,
-                                    s);
+  // K slices of the router product: the largest divisor of d / 128 (at most
+  // kDecodeMaxSlices) that keeps the item count within the grid
+  const int ntile = ((a.E + 15) / 16) * ((a.T + 15) / 16);
+  args.ks = 1;
+  for (int c = 2; c <= kDecodeMaxSlices; ++c)
+    if ((a.d / 128) % c == 0 && ntile * c <= grid) args.ks = c;
+  hipLaunchKernelGGL(decode_init_kernel, dim3(1), dim3(256), 0, s, a.bar);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // a plain launch: the cooperative launch API waits for the device to drain
+  // on both sides of the kernel (about 20 us here), and the grid is resident
+  // without it (see above)
+  hipLaunchKernelGGL(decode_kernel, dim3(grid), dim3(256), 0, s, args);
+  return hipGetLastError();
 }
 
 }  // namespace moe

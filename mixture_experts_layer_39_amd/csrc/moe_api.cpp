@@ -17,6 +17,8 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 int esize(const moe_config* c) { return c->dtype == MOE_BF16 ? 2 : 4; }
 
+static_assert(kDecodeMaxTokens == MOE_SMALL_BATCH_MAX, "small-batch token limit");
+
 moe_status check_config(const moe_config* c) {
   if (!c) return MOE_ERR_INVALID_ARG;
   if (c->num_tokens < 0 || c->num_tokens >= (int64_t(1) << 30)) return MOE_ERR_INVALID_ARG;
@@ -33,6 +35,7 @@ moe_status check_config(const moe_config* c) {
   if (c->normalize_topk != 0 && c->normalize_topk != 1) return MOE_ERR_INVALID_ARG;
   if (c->loss_kind != MOE_LOSS_BALANCE && c->loss_kind != MOE_LOSS_USAGE_STD) return MOE_ERR_INVALID_ARG;
   if (c->save_preact != 0 && c->save_preact != 1) return MOE_ERR_INVALID_ARG;
+  if (c->small_batch < -1 || c->small_batch > 1) return MOE_ERR_INVALID_ARG;
   // kernels move rows as 16-byte vectors
   const int vec = c->dtype == MOE_BF16 ? 8 : 4;
   if (c->hidden_size % vec) return MOE_ERR_UNSUPPORTED;
@@ -63,7 +66,7 @@ struct Layout {
   int tiles, tile_tokens;
   size_t tile_cnt, me_tile, me_sum, demand, idx, slot, weight, offset;
   size_t x_disp, a_save, h_disp, y_disp, d_act;
-  size_t dec_logits, dec_prob, dec_bar;   // small-batch forward: logits, probabilities, barrier
+  size_t dec_logits, dec_prob, dec_part, dec_bar;   // small-batch forward: logits, probabilities, partial logits, barrier
   // backward regions (save_preact == 1 only)
   int Ep;
   RouterChunks rc;
@@ -102,6 +105,7 @@ Layout layout_of(const moe_config* c) {
   L.d_act = take(h > 0 ? (size_t)L.rows * h * s : 0);
   L.dec_logits = take(L.T <= kDecodeMaxTokens ? (size_t)L.T * E * 4 : 0);
   L.dec_prob = take(L.T <= kDecodeMaxTokens ? (size_t)L.T * E * 4 : 0);
+  L.dec_part = take(L.T <= kDecodeMaxTokens ? (size_t)kDecodeMaxSlices * L.T * E * 4 : 0);
   L.dec_bar = take(L.T <= kDecodeMaxTokens ? 4096 : 0);
   const bool train = c->save_preact != 0;
   L.Ep = router_ep(E);
@@ -369,9 +373,10 @@ moe_status moe_layer_forward(const moe_config* cfg, const void* x, const void* w
   int32_t* sl = slot ? slot : at<int32_t>(ws, L.slot);
   float* wt = weight ? weight : at<float>(ws, L.weight);
   int32_t* off = at<int32_t>(ws, L.offset);
-  // a few tokens, inference: the whole forward in one cooperative launch
-  if (!cfg->save_preact && decode_fits(L.T, cfg->hidden_size, cfg->ffn_hidden, cfg->num_experts, cfg->k,
-                                       cfg->dtype)) {
+  // a few tokens, inference: the whole forward in one persistent launch
+  const bool small = cfg->small_batch > 0 || (cfg->small_batch == 0 && L.T <= MOE_SMALL_BATCH_AUTO);
+  if (small && !cfg->save_preact &&
+      decode_fits(L.T, cfg->hidden_size, cfg->ffn_hidden, cfg->num_experts, cfg->k, cfg->dtype)) {
     DecodeArgs da{};
     da.x = static_cast<const bf16*>(x);
     da.w_router = static_cast<const bf16*>(w_router);
@@ -393,6 +398,7 @@ moe_status moe_layer_forward(const moe_config* cfg, const void* x, const void* w
     da.h_disp = cfg->ffn_hidden > 0 ? at<bf16>(ws, L.h_disp) : nullptr;
     da.y_disp = at<bf16>(ws, L.y_disp);
     da.prob = at<float>(ws, L.dec_prob);
+    da.part = at<float>(ws, L.dec_part);
     da.bar = at<unsigned>(ws, L.dec_bar);
     da.C = L.C;
     da.T = (int32_t)L.T;
@@ -405,8 +411,8 @@ moe_status moe_layer_forward(const moe_config* cfg, const void* x, const void* w
     da.act = cfg->activation;
     const hipError_t e = launch_decode(da, s);
     if (e == hipSuccess) return MOE_OK;
-    // a grid that cannot be co-resident on this device takes the multi-kernel path
-    if (e != hipErrorCooperativeLaunchTooLarge && e != hipErrorNotSupported) return MOE_ERR_HIP;
+    // a device where the grid would not be resident takes the multi-kernel path
+    if (e != hipErrorNotSupported) return MOE_ERR_HIP;
     (void)hipGetLastError();
   }
   // training: the backward needs the logits, so keep them when the caller does not

@@ -221,9 +221,10 @@ hipError_t launch_router_partials(const uint16_t* dl_hl, const void* x, const in
                                   int64_t T, int S, int d, int Ep, hipStream_t s);
 
 // ---------------------------------------------------------------- small-batch forward
-// The whole forward in one cooperative kernel for up to kDecodeMaxTokens
+// The whole forward in one persistent kernel for up to kDecodeMaxTokens
 // tokens (bf16, d and h multiples of 128, inference: no pre-activation kept).
 constexpr int kDecodeMaxTokens = 256;
+constexpr int kDecodeMaxSlices = 16;
 struct DecodeArgs {
   const bf16* x;            // [T, d]
   const bf16* w_router;     // [E, d] (unused with logits_in)
@@ -245,9 +246,11 @@ struct DecodeArgs {
   bf16* h_disp;             // [rows, h]
   bf16* y_disp;             // [rows, d]
   float* prob;              // [T, E] softmax probabilities (BALANCE loss)
+  float* part;              // [kDecodeMaxSlices, T, E] partial router products
   unsigned* bar;            // [1024] grid-barrier counters and status (zeroed per call)
   int64_t C;                // capacity, < 0 = none
   int32_t T, d, h, E, k, normalize, loss_kind, act;
+  int32_t ks;               // K slices of the router product (set by launch_decode)
 };
 bool decode_fits(int64_t T, int d, int h, int E, int k, int dtype);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);

@@ -1,5 +1,6 @@
 """GPU parity of the small-batch forward (up to 256 tokens, inference), which
-moe_layer_forward runs as one cooperative kernel, against the CPU oracle.
+moe_layer_forward runs as one persistent kernel (small_batch = 1 forces it
+where it applies), against the CPU oracle.
 
 Both sides route the same drawn logits (given to the GPU as logits_in), so
 routing indices, slots, drops, counts and offsets are compared bit-exact;
@@ -62,7 +63,8 @@ def _forward(cfg, inp, T, d, E, given=True, ws=None):
 @pytest.mark.parametrize("T,d,E,k,h,act,cf,mc,drop,norm,loss", CASES, ids=lambda v: str(v))
 def test_small_batch_forward_parity(T, d, E, k, h, act, cf, mc, drop, norm, loss):
     inp = _inputs(T, d, E, h, seed=900 + T + E)
-    cfg = B.make_config(T, d, E, k, cf, mc, drop, h, act, B.MOE_BF16, normalize_topk=norm, loss_kind=loss)
+    cfg = B.make_config(T, d, E, k, cf, mc, drop, h, act, B.MOE_BF16, normalize_topk=norm, loss_kind=loss,
+                        small_batch=1)
     g, out, ws = _forward(cfg, inp, T, d, E)
     L = f64(inp["logits"])
     np.testing.assert_array_equal(f64(g["logits"]), L)
@@ -102,7 +104,7 @@ def test_small_batch_router_path(T):
     given-logits path fed with those logits."""
     d, E, h = 2048, 64, 512
     inp = _inputs(T, d, E, h, seed=77 + T)
-    cfg = B.make_config(T, d, E, 2, 1.25, 4, True, h, B.MOE_ACT_GELU, B.MOE_BF16)
+    cfg = B.make_config(T, d, E, 2, 1.25, 4, True, h, B.MOE_ACT_GELU, B.MOE_BF16, small_batch=1)
     g, out, _ = _forward(cfg, inp, T, d, E, given=False)
     x, w = f64(inp["x"]), f64(inp["w_router"])
     want = O.router_logits(x, w)
@@ -122,7 +124,7 @@ def test_small_batch_is_deterministic_and_matches_at_the_boundary():
     d, E, h = 256, 32, 256
     for T in (256, 257):
         inp = _inputs(T, d, E, h, seed=5 + T)
-        cfg = B.make_config(T, d, E, 2, 1.0, 4, True, h, B.MOE_ACT_GELU, B.MOE_BF16)
+        cfg = B.make_config(T, d, E, 2, 1.0, 4, True, h, B.MOE_ACT_GELU, B.MOE_BF16, small_batch=1)
         g1, o1, ws = _forward(cfg, inp, T, d, E)
         o1 = o1.clone()
         g2, o2, _ = _forward(cfg, inp, T, d, E, ws=ws)
@@ -132,3 +134,34 @@ def test_small_batch_is_deterministic_and_matches_at_the_boundary():
                             drop_tokens=True, act=O.ACT_GELU, dtype="bf16")
         np.testing.assert_array_equal(i64(g1["slot"]), r["slot"])
         close(f64(o1), r["out"], 2e-2)
+
+
+@pytest.mark.parametrize("T", [3, 64, 100])
+def test_small_batch_modes_agree(T):
+    """small_batch 1 (one launch where it applies), 0 (automatic: one launch
+    up to 64 tokens) and -1 (the multi-kernel path): identical routing,
+    slots and counts; weights, loss and outputs within rounding; the router
+    path's logits of the two kernels within the fp32 dot-product bound."""
+    d, E, h = 1024, 32, 768
+    inp = _inputs(T, d, E, h, seed=300 + T)
+    res = {}
+    for mode in (1, 0, -1):
+        cfg = B.make_config(T, d, E, 2, 1.25, 4, True, h, B.MOE_ACT_GELU, B.MOE_BF16, small_batch=mode)
+        g, out, _ = _forward(cfg, inp, T, d, E)
+        res[mode] = (g, out.clone())
+        if mode != 1:
+            for key in ("idx", "slot", "count"):
+                assert torch.equal(g[key], res[1][0][key]), (mode, key)
+            # the two softmax implementations round differently
+            assert (g["weight"] - res[1][0]["weight"]).abs().max().item() <= 1e-6
+            assert abs(g["loss"].item() - res[1][0]["loss"].item()) <= 1e-6 * abs(res[1][0]["loss"].item())
+            close(f64(out), f64(res[1][1]), 2e-2)
+    x, w = f64(inp["x"]), f64(inp["w_router"])
+    u = 2.0 ** -24
+    bound = 2 * d * u / (1 - d * u) * (np.abs(x) @ np.abs(w).T)
+    lg = {}
+    for mode in (1, -1):
+        cfg = B.make_config(T, d, E, 2, 1.25, 4, True, h, B.MOE_ACT_GELU, B.MOE_BF16, small_batch=mode)
+        g, _, _ = _forward(cfg, inp, T, d, E, given=False)
+        lg[mode] = f64(g["logits"])
+    assert (np.abs(lg[1] - lg[-1]) <= bound).all()
