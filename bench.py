@@ -16,6 +16,9 @@ Besides the headline value the line carries
                 dense MFMA peak, its per-launch time taken with HIP events on the
                 stream the kernels run on;
   stages:       every stage's event time and its algorithmic bytes or flops;
+  small_batch:  latency of the forward for 1, 16 and 64 tokens with the same
+                weights, through the one-launch kernel and the multi-kernel
+                path, and the fused kernel's read rate against HBM peak;
   cpu_baseline: the CPU oracle timed on this host on a bounded sample.
 """
 from __future__ import annotations
@@ -118,6 +121,49 @@ def cpu_baseline(sp, inp, target_s=15.0):
                       f"{bwd_label(sp)}; {el:.1f} s"}
 
 
+def small_batch_latency(B, torch, sp, inp, dt, stream, sizes=(1, 16, 64), iters=50):
+    """Latency of moe_layer_forward for a few tokens (the first T rows of the
+    workload's x, the same weights) through the one-launch small-batch kernel
+    and through the multi-kernel path, with the bytes the fused kernel must
+    read: the chosen experts' weights and biases, x, the router weight, out."""
+    dev = inp["x"].device
+    T0, d, E, k, h = sp["T"], sp["d"], sp["E"], sp["k"], sp["h"]
+    res = {}
+    for T in sizes:
+        if T > T0:
+            continue
+        x = inp["x"][:T]
+        row = {}
+        for mode, name in ((1, "fused_us"), (-1, "multi_kernel_us")):
+            cfg = B.make_config(T, d, E, k, sp["cf"], sp["min_cap"], sp["drop"], h, sp["act"], dt, small_batch=mode)
+            ws = torch.empty(B.moe_workspace_size(cfg), dtype=torch.uint8, device=dev)
+            out = torch.empty(T, d, dtype=x.dtype, device=dev)
+            loss = torch.empty(1, dtype=torch.float32, device=dev)
+            count = torch.empty(E, dtype=torch.int32, device=dev)
+
+            def call():
+                B.moe_layer_forward(cfg, x, inp["w_router"], inp["b_router"], None, inp["w1"], inp["b1"], inp["w2"],
+                                    inp["b2"], out, loss, count, ws=ws, stream=stream)
+            for _ in range(5):
+                call()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(iters):
+                call()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            row[name] = e0.elapsed_time(e1) / iters * 1e3
+        esz = 2 if dt == B.MOE_BF16 else 4
+        touched = int((count > 0).sum())
+        per_expert = (2 * h * d + h + d) * esz if h else (d * d + d) * esz
+        nbytes = touched * per_expert + 2 * T * d * esz + E * d * esz
+        gbs = nbytes / (row["fused_us"] * 1e-6) / 1e9
+        row.update({"experts_touched": touched, "bytes": nbytes, "GB/s": gbs, "frac_hbm": gbs / PEAK_HBM_GBS})
+        res[str(T)] = row
+    return {"kernel": "decode_kernel (one launch, one workgroup per CU)", "bound": "hbm",
+            "tokens": res}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -125,6 +171,9 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="top2_e64")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-small-batch", action="store_true", help="skip the small-batch latency object")
+    ap.add_argument("--small-batch-only", action="store_true",
+                    help="only time the small-batch forward (1, 16, 64 tokens) and print that object")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (scales HBM byte counters)")
     a = ap.parse_args(argv)
@@ -160,6 +209,9 @@ def main(argv=None):
     loss = torch.empty(1, dtype=torch.float32, device=dev)
     count = torch.empty(E, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
+    if a.small_batch_only:
+        print(json.dumps(small_batch_latency(B, torch, sp, inp, dt, stream)), flush=True)
+        return 0
 
     bwd = bool(sp.get("backward"))
     layer = sp.get("backward") == "layer"
@@ -319,6 +371,8 @@ def main(argv=None):
             "config": {"workload": describe(sp) + bwd_label(sp).replace(",", " +"),
                        "tokens_per_step": T, "rows_kept": N},
             "roofline": roofline, "stages": stages}
+    if not a.no_small_batch and not bwd and sp["h"] and dt == B.MOE_BF16:
+        line["small_batch"] = small_batch_latency(B, torch, sp, inp, dt, stream)
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(sp, inp)
     print(json.dumps(line), flush=True)
