@@ -76,6 +76,9 @@ typedef enum { MOE_ACT_NONE = 0, MOE_ACT_RELU = 1, MOE_ACT_GELU = 2 } moe_act;
  *            balance-loss table: lambda * (std(usage_prob) + 1e-6)). */
 typedef enum { MOE_LOSS_BALANCE = 0, MOE_LOSS_USAGE_STD = 1 } moe_loss_kind;
 
+/* Gate noise policy ([ds.moe] §2.1 noisy_gate_policy: "jitter" or "rsample"). */
+typedef enum { MOE_NOISE_NONE = 0, MOE_NOISE_JITTER = 1, MOE_NOISE_RSAMPLE = 2 } moe_noise;
+
 #define MOE_MAX_EXPERTS 256
 /* Token counts of the fused small-batch forward (moe_config.small_batch). */
 #define MOE_SMALL_BATCH_MAX 256
@@ -110,6 +113,30 @@ typedef struct moe_config {
                               multiples of 128, save_preact == 0):
                               0: when T <= MOE_SMALL_BATCH_AUTO;
                               1: whenever it applies; -1: never               */
+  /* Seeded random gate options ([ds.moe] §2.1 noisy_gate_policy, use_rts,
+   * top2_2nd_expert_sampling; the formulas, which the pages do not give,
+   * follow the published DeepSpeed gate).  Every draw comes from
+   * Philox4x32-10 keyed by seed: draw n of stream s is word n % 4 of the
+   * block at counter (n / 4 low, n / 4 high, s, 0), key (seed low, seed
+   * high); a word w gives u = ((w >> 9) + 0.5) * 2^-23 in (0, 1).  Streams:
+   * 0 jitter (n = t*d + i), 1 RSample (n = t*E + e), 2 second expert
+   * (n = t*E + e), 3 RTS (n = t).  All 0: the deterministic gate.  These
+   * are training options: the caller sets them only when training; the
+   * one-launch small-batch forward does not take them.                     */
+  int32_t noisy_gate_policy;      /* moe_noise.  JITTER: the router reads
+                              bf16(x * ((1 - 0.01) + 0.02 * u)) (fp32 product
+                              and sum, each rounded once); the experts read
+                              x; needs the router (not logits_in) and bf16.
+                              RSample (k == 1): the expert is the argmax of
+                              fp32(logit + g), g = -log(-log u); the weight
+                              stays the clean softmax probability.          */
+  int32_t use_rts;                /* k == 1: an expert whose demand exceeds C
+                              keeps the C claims with the largest stream-3
+                              words (ties to the lower token), in token
+                              order; counts, offsets and loss unchanged     */
+  int32_t second_expert_sampling; /* k == 2: the second expert is the argmax
+                              over the other experts of fp32(logit + g)     */
+  uint64_t seed;                  /* Philox key                             */
 } moe_config;
 
 /* Static text for a status code. */

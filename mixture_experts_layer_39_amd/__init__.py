@@ -10,7 +10,7 @@ from __future__ import annotations
 
 from . import binding
 from .binding import (MOE_ACT_GELU, MOE_ACT_NONE, MOE_ACT_RELU, MOE_BF16, MOE_F32,  # noqa: F401
-                      MOE_LOSS_BALANCE, MOE_LOSS_USAGE_STD, MoeConfig, MoeError, make_config,
+                      MOE_LOSS_BALANCE, MOE_LOSS_USAGE_STD, MOE_NOISE_JITTER, MOE_NOISE_NONE, MOE_NOISE_RSAMPLE, MoeConfig, MoeError, make_config,
                       moe_capacity, moe_combine, moe_dispatch, moe_expert_ffn, moe_expert_ffn_backward,
                       moe_gate, moe_layer_forward, moe_max_rows, moe_workspace_size, moe_workspace_views)
 
@@ -28,16 +28,30 @@ class MoE:
     nn.Linear [out, in] layout, stacked over experts.  small_batch selects
     the one-launch forward for a few tokens (0 automatic, 1 always when it
     applies, -1 never).
+
+    The random gate options noisy_gate_policy ("Jitter" or "RSample"),
+    use_rts and top2_2nd_expert_sampling act in training mode only and, as
+    in the gate they come from, each where it applies: RSample and RTS with
+    k = 1, second-expert sampling with k = 2, jitter with either.  Their
+    Philox seed is ``seed`` plus the number of training forwards so far, so
+    each step draws fresh noise and a run is reproducible.  They default to
+    off (the deterministic gate).
     """
 
     def __init__(self, hidden_size, num_experts, w_router, w1, b1=None, w2=None, b2=None, b_router=None,
                  k=1, capacity_factor=1.0, eval_capacity_factor=1.0, min_capacity=4, drop_tokens=True,
                  ffn_hidden=0, activation=MOE_ACT_NONE, normalize_topk=False, loss_kind=MOE_LOSS_BALANCE,
-                 small_batch=0):
+                 small_batch=0, noisy_gate_policy=None, use_rts=False, top2_2nd_expert_sampling=False, seed=0):
         import torch
         self.hidden_size, self.num_experts, self.k = hidden_size, num_experts, k
         self.capacity_factor, self.min_capacity, self.drop_tokens = capacity_factor, min_capacity, drop_tokens
         self.eval_capacity_factor, self.small_batch, self.training = eval_capacity_factor, small_batch, True
+        policies = {None: MOE_NOISE_NONE, "jitter": MOE_NOISE_JITTER, "rsample": MOE_NOISE_RSAMPLE}
+        key = noisy_gate_policy.lower() if isinstance(noisy_gate_policy, str) else noisy_gate_policy
+        if key not in policies:
+            raise ValueError(f"noisy_gate_policy must be None, 'Jitter' or 'RSample', not {noisy_gate_policy!r}")
+        self.noisy_gate_policy, self.use_rts = policies[key], bool(use_rts)
+        self.top2_2nd_expert_sampling, self.seed, self.steps = bool(top2_2nd_expert_sampling), int(seed), 0
         self.ffn_hidden, self.activation = ffn_hidden, activation
         self.normalize_topk, self.loss_kind = normalize_topk, loss_kind
         self.w_router, self.b_router = w_router, b_router
@@ -54,9 +68,17 @@ class MoE:
 
     def config(self, num_tokens):
         cf = self.capacity_factor if self.training else self.eval_capacity_factor
+        rnd = {}
+        if self.training:
+            noise = self.noisy_gate_policy
+            if noise == MOE_NOISE_RSAMPLE and self.k != 1:
+                noise = MOE_NOISE_NONE
+            rnd = dict(noisy_gate_policy=noise, use_rts=self.use_rts and self.k == 1,
+                       second_expert_sampling=self.top2_2nd_expert_sampling and self.k == 2,
+                       seed=(self.seed + self.steps) % 2 ** 64)
         return make_config(num_tokens, self.hidden_size, self.num_experts, self.k, cf, self.min_capacity,
                            self.drop_tokens, self.ffn_hidden, self.activation, self.dtype, self.normalize_topk,
-                           self.loss_kind, small_batch=self.small_batch)
+                           self.loss_kind, small_batch=self.small_batch, **rnd)
 
     def forward(self, x, logits=None):
         import torch
@@ -71,6 +93,8 @@ class MoE:
         count = torch.empty(self.num_experts, dtype=torch.int32, device=x.device)
         moe_layer_forward(cfg, x2, self.w_router, self.b_router, logits, self.w1, self.b1, self.w2, self.b2,
                           out, loss, count, ws=self._ws)
+        if self.training:
+            self.steps += 1
         return out.reshape(shape), loss[0], count
 
     __call__ = forward

@@ -18,6 +18,7 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 MOE_F32, MOE_BF16 = 0, 1
 MOE_ACT_NONE, MOE_ACT_RELU, MOE_ACT_GELU = 0, 1, 2
 MOE_LOSS_BALANCE, MOE_LOSS_USAGE_STD = 0, 1
+MOE_NOISE_NONE, MOE_NOISE_JITTER, MOE_NOISE_RSAMPLE = 0, 1, 2
 MOE_MAX_EXPERTS = 256
 
 EXPORTED = ("moe_status_string", "moe_capacity", "moe_max_rows", "moe_workspace_size", "moe_gate",
@@ -42,15 +43,22 @@ class MoeConfig(ctypes.Structure):
         ("loss_kind", ctypes.c_int32),
         ("save_preact", ctypes.c_int32),
         ("small_batch", ctypes.c_int32),
+        ("noisy_gate_policy", ctypes.c_int32),
+        ("use_rts", ctypes.c_int32),
+        ("second_expert_sampling", ctypes.c_int32),
+        ("seed", ctypes.c_uint64),
     ]
 
 
 def make_config(num_tokens, hidden_size, num_experts, k=1, capacity_factor=1.0, min_capacity=4,
                 drop_tokens=True, ffn_hidden=0, activation=MOE_ACT_NONE, dtype=MOE_BF16,
-                normalize_topk=False, loss_kind=MOE_LOSS_BALANCE, save_preact=False, small_batch=0):
+                normalize_topk=False, loss_kind=MOE_LOSS_BALANCE, save_preact=False, small_batch=0,
+                noisy_gate_policy=0, use_rts=False, second_expert_sampling=False, seed=0):
     return MoeConfig(int(num_tokens), float(capacity_factor), int(hidden_size), int(num_experts), int(k),
                      int(min_capacity), int(bool(drop_tokens)), int(ffn_hidden), int(activation), int(dtype),
-                     int(bool(normalize_topk)), int(loss_kind), int(bool(save_preact)), int(small_batch))
+                     int(bool(normalize_topk)), int(loss_kind), int(bool(save_preact)), int(small_batch),
+                     int(noisy_gate_policy), int(bool(use_rts)), int(bool(second_expert_sampling)),
+                     int(seed) & (2 ** 64 - 1))
 
 
 class MoeError(RuntimeError):

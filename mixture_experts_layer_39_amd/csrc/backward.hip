@@ -39,6 +39,7 @@
 //    fp32 partial output), and one kernel adds the chunks and the hi/lo
 //    halves in a fixed order, so results are bit-identical run to run.
 #include "moe_internal.h"
+#include "philox.h"
 
 namespace moe {
 namespace {
@@ -504,8 +505,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
       if constexpr (EPK > 0) {
         const float4 r0 = *reinterpret_cast<const float4*>(&tile[tl][8 * n]);
         const float4 r1 = *reinterpret_cast<const float4*>(&tile[tl][8 * n + 4]);
-        v[0] += r0.x; v[1] += r0.y; v[2] += r0.z; v[3] += r0.w;
-        v[4] += r1.x; v[5] += r1.y; v[6] += r1.z; v[7] += r1.w;
+        float rv[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+        if (a.jitter) {
+          // the router read x * factor, so its input gradient carries the
+          // factor (the bf16 rounding of the product taken as identity)
+          const uint64_t n0 = (uint64_t)t * d + fl;   // a multiple of 8
+          const uint4 w0 = philox_block(a.seed_lo, a.seed_hi, kStreamJitter, n0 >> 2);
+          const uint4 w1 = philox_block(a.seed_lo, a.seed_hi, kStreamJitter, (n0 >> 2) + 1);
+          const uint32_t wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+          for (int j = 0; j < 8; ++j) rv[j] *= __fadd_rn(0.99f, __fmul_rn(0.02f, philox_uniform(wv[j])));
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] += rv[j];
       }
       *reinterpret_cast<uint4*>(a.dx + t * d + fl) = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
                                                                 pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
@@ -677,6 +689,37 @@ hipError_t launch_zero_bytes(void* p, size_t n, hipStream_t s) {
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL(zero_bytes_kernel, dim3((unsigned)blocks), dim3(256), 0, s, static_cast<uint4*>(p), n16,
                      static_cast<unsigned char*>(p) + n16 * 16, ntail);
+  return hipGetLastError();
+}
+
+namespace {
+// x_j = bf16(x * ((1 - 0.01) + 0.02 u)), u the stream-0 uniform of element
+// t*d + i, the product and the sum each rounded once in fp32: what the gate
+// kernel's router read under jitter.
+__global__ __launch_bounds__(256) void jitter_input_kernel(const bf16* __restrict__ x, bf16* __restrict__ xj,
+                                                           int64_t nvec, uint32_t seed_lo, uint32_t seed_hi) {
+  for (int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x; v < nvec; v += (int64_t)gridDim.x * 256) {
+    bf16x8 xv = *reinterpret_cast<const bf16x8*>(x + v * 8);
+    const uint4 w0 = philox_block(seed_lo, seed_hi, kStreamJitter, (uint64_t)v * 2);
+    const uint4 w1 = philox_block(seed_lo, seed_hi, kStreamJitter, (uint64_t)v * 2 + 1);
+    const uint32_t wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float f = __fadd_rn(0.99f, __fmul_rn(0.02f, philox_uniform(wv[j])));
+      xv[j] = static_cast<bf16>(__fmul_rn(static_cast<float>(xv[j]), f));
+    }
+    *reinterpret_cast<bf16x8*>(xj + v * 8) = xv;
+  }
+}
+}  // namespace
+
+hipError_t launch_jitter_input(const bf16* x, bf16* xj, int64_t T, int d, uint32_t seed_lo, uint32_t seed_hi,
+                               hipStream_t s) {
+  const int64_t nvec = T * d / 8;
+  if (nvec == 0) return hipSuccess;
+  const int64_t blocks = (nvec + 255) / 256;
+  hipLaunchKernelGGL(jitter_input_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0, s, x, xj,
+                     nvec, seed_lo, seed_hi);
   return hipGetLastError();
 }
 

@@ -34,9 +34,15 @@
 //    choice 1), dropped at or past the capacity; its last workgroup forms
 //    the expert counts, offsets and the loss.  Kernel boundaries order all of
 //    this, so no kernel waits on another workgroup.
+//  * Random gate options (seeded, Philox4x32-10; reading R15): jitter
+//    multiplies the x fragments by their factors just before the router's
+//    MFMAs; RSample and second-expert sampling add Gumbel draws to the
+//    selection keys only; Random Token Selection re-picks the kept claims of
+//    an over-capacity expert in a kernel of its own after the fix-up.
 #include <math.h>
 
 #include "moe_internal.h"
+#include "philox.h"
 
 namespace moe {
 namespace {
@@ -143,6 +149,25 @@ __global__ __launch_bounds__(256) void gate_kernel(GateArgs a) {
         load_w(ks + 1, wr);
         load_x(ks + 1, xn);
       }
+      if (a.jitter) {
+        // the router reads x * ((1 - eps) + 2 eps u), eps = 0.01, each
+        // product and sum rounded once in fp32, then stored as bf16
+#pragma unroll
+        for (int i = 0; i < KC / 32; ++i) {
+          const int kk = ks * KC + q * (KC / 4) + i * 8;
+          if (tx < T && kk < d) {
+            const uint64_t n0 = (uint64_t)tx * d + kk;   // a multiple of 8
+            const uint4 w0 = philox_block(a.seed_lo, a.seed_hi, kStreamJitter, n0 >> 2);
+            const uint4 w1 = philox_block(a.seed_lo, a.seed_hi, kStreamJitter, (n0 >> 2) + 1);
+            const uint32_t wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const float f = __fadd_rn(0.99f, __fmul_rn(0.02f, philox_uniform(wv[j])));
+              xb[i][j] = static_cast<bf16>(__fmul_rn(static_cast<float>(xb[i][j]), f));
+            }
+          }
+        }
+      }
       const unsigned char* wb = smem + (size_t)(ks & 1) * EP * KC * 2;
       // fragment i covers K values q*(KC/4) + 8i .. +7 of the chunk for lane
       // quarter q (the same order on both operands)
@@ -240,6 +265,14 @@ __global__ __launch_bounds__(256) void gate_kernel(GateArgs a) {
     // is -inf and the running index starts past every expert, so that even a
     // token whose logits are all -inf or NaN (outside the contract) gets a
     // valid expert (the lowest index) and no later step indexes out of range.
+    // With RSample (k = 1) the top-1 key is fp32(logit + g), g a Gumbel draw
+    // of stream 1 at t*E + e; with second-expert sampling (k = 2) the top-2
+    // key is the same with stream 2.  The weights use the clean logits.
+    const bool noisy0 = a.rsample != 0, noisy1 = a.second != 0 && K == 2;
+    auto gumbel = [&](uint32_t stream, int e) {
+      const uint32_t w = philox_draw(a.seed_lo, a.seed_hi, stream, (uint64_t)t * E + e);
+      return -logf(-logf(philox_uniform(w)));
+    };
     float v0 = -INFINITY;
     int i0 = E;
 #pragma unroll
@@ -247,7 +280,8 @@ __global__ __launch_bounds__(256) void gate_kernel(GateArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int e = et * 16 + q * 4 + r;
-        const float key = lg[et][r] != lg[et][r] ? -INFINITY : lg[et][r];
+        float key = lg[et][r] != lg[et][r] ? -INFINITY : lg[et][r];
+        if (noisy0 && e < E) key = __fadd_rn(key, gumbel(kStreamRSample, e));
         if (e < E && (key > v0 || (key == v0 && e < i0))) {
           v0 = key;
           i0 = e;
@@ -264,7 +298,8 @@ __global__ __launch_bounds__(256) void gate_kernel(GateArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int e = et * 16 + q * 4 + r;
-          const float key = lg[et][r] != lg[et][r] ? -INFINITY : lg[et][r];
+          float key = lg[et][r] != lg[et][r] ? -INFINITY : lg[et][r];
+          if (noisy1 && e < E) key = __fadd_rn(key, gumbel(kStreamSecond, e));
           if (e < E && e != i0 && (key > v1 || (key == v1 && e < i1))) {
             v1 = key;
             i1 = e;
@@ -272,6 +307,25 @@ __global__ __launch_bounds__(256) void gate_kernel(GateArgs a) {
         }
       merge_best(v1, i1, 16);
       merge_best(v1, i1, 32);
+    }
+    if (noisy0 || noisy1) {
+      // a noisy key is not the logit: fetch the chosen experts' clean logits
+      // from the lanes that hold them
+      float o0 = -INFINITY, o1 = -INFINITY;
+#pragma unroll
+      for (int et = 0; et < NET; ++et)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int e = et * 16 + q * 4 + r;
+          if (e == i0) o0 = lg[et][r];
+          if (e == i1) o1 = lg[et][r];
+        }
+      o0 = fmaxf(o0, __shfl_xor(o0, 16));
+      o0 = fmaxf(o0, __shfl_xor(o0, 32));
+      o1 = fmaxf(o1, __shfl_xor(o1, 16));
+      o1 = fmaxf(o1, __shfl_xor(o1, 32));
+      if (noisy0) v0 = o0;
+      if (noisy1) v1 = o1;
     }
     float p0 = expf(v0 - mx) / sum;
     float p1 = (K == 2) ? expf(v1 - mx) / sum : 0.f;
@@ -463,6 +517,86 @@ __global__ __launch_bounds__(256) void slot_finalize_kernel(GateArgs a, int tile
   a.slot[i] = (a.C >= 0 && s >= a.C) ? -1 : (int32_t)s;
 }
 
+// Exclusive rank of the calling thread's flag among the workgroup's 256
+// flags (thread order), and their total; ballots within a wavefront, wave
+// totals through LDS.
+__device__ __forceinline__ int block_rank(bool flag, int* wave_tot, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint64_t b = __ballot(flag);
+  const uint64_t lt = lane ? (~0ull >> (64 - lane)) : 0ull;
+  if (lane == 0) wave_tot[wave] = __popcll(b);
+  __syncthreads();
+  int before = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    if (w < wave) before += wave_tot[w];
+    total += wave_tot[w];
+  }
+  __syncthreads();
+  return before + __popcll(b & lt);
+}
+
+// Random Token Selection (k = 1 with a capacity; DeepSpeed's use_rts as
+// reading R15 takes it): an expert whose demand D exceeds C keeps the C
+// claimants of largest priority (the stream-3 word of the token; equal words
+// to the lower token) and numbers them 0.. in token order; the rest are
+// dropped.  Counts, offsets and the loss do not change.  One workgroup per
+// expert: the C-th largest priority by a radix select over four 8-bit
+// digits (LDS histograms over the expert's claimants), then one pass in
+// token order that ranks the kept claims with workgroup scans.
+__global__ __launch_bounds__(256) void rts_select_kernel(GateArgs a) {
+  __shared__ int hist[256];
+  __shared__ int wave_tot[4];
+  __shared__ uint32_t s_prefix;
+  __shared__ int s_need;
+  const int e = blockIdx.x, tid = threadIdx.x;
+  const int64_t T = a.T, C = a.C;
+  if (C < 0 || (int64_t)a.demand[e] <= C) return;
+  uint32_t prefix = 0, mask = 0;
+  int need = (int)C;   // claimants still to take among those matching prefix
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    hist[tid] = 0;
+    __syncthreads();
+    for (int64_t t = tid; t < T; t += 256) {
+      if (a.expert_idx[t] != e) continue;
+      const uint32_t p = philox_draw(a.seed_lo, a.seed_hi, kStreamRts, (uint64_t)t);
+      if ((p & mask) == prefix) atomicAdd(&hist[(p >> shift) & 255u], 1);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      // the digit where the count from the top reaches `need`
+      int above = 0, b = 255;
+      for (; b > 0; --b) {
+        if (above + hist[b] >= need) break;
+        above += hist[b];
+      }
+      s_prefix = prefix | ((uint32_t)b << shift);
+      s_need = need - above;
+    }
+    __syncthreads();
+    prefix = s_prefix;
+    need = s_need;
+    mask |= 0xffu << shift;
+  }
+  // prefix is now the C-th largest priority; every claimant above it is kept,
+  // and the first `need` (in token order) of those equal to it
+  int run_eq = 0, run_kept = 0;
+  for (int64_t base = 0; base < T; base += 256) {
+    const int64_t t = base + tid;
+    const bool claim = t < T && a.expert_idx[t] == e;
+    const uint32_t p = claim ? philox_draw(a.seed_lo, a.seed_hi, kStreamRts, (uint64_t)t) : 0u;
+    const bool eq = claim && p == prefix;
+    int n_eq, n_kept;
+    const int eq_rank = run_eq + block_rank(eq, wave_tot, n_eq);
+    const bool keep = claim && (p > prefix || (eq && eq_rank < need));
+    const int kept_rank = run_kept + block_rank(keep, wave_tot, n_kept);
+    if (claim) a.slot[t] = keep ? kept_rank : -1;
+    run_eq += n_eq;
+    run_kept += n_kept;
+  }
+}
+
 __global__ void gate_empty_kernel(int32_t* count, int32_t* offset, float* loss, int E) {
   for (int e = threadIdx.x; e <= E; e += blockDim.x) {
     if (e < E) count[e] = 0;
@@ -516,6 +650,12 @@ hipError_t launch_gate(const GateArgs& a, int dtype, hipStream_t s) {
 hipError_t launch_slot_finalize(const GateArgs& a, int tile_tokens, hipStream_t s) {
   const int64_t n = a.T * a.k;
   hipLaunchKernelGGL(slot_finalize_kernel, dim3((unsigned)((n + 255) / 256 + 1)), dim3(256), 0, s, a, tile_tokens);
+  return hipGetLastError();
+}
+
+hipError_t launch_rts_select(const GateArgs& a, hipStream_t s) {
+  if (a.k != 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(rts_select_kernel, dim3((unsigned)a.E), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -36,6 +36,15 @@ moe_status check_config(const moe_config* c) {
   if (c->loss_kind != MOE_LOSS_BALANCE && c->loss_kind != MOE_LOSS_USAGE_STD) return MOE_ERR_INVALID_ARG;
   if (c->save_preact != 0 && c->save_preact != 1) return MOE_ERR_INVALID_ARG;
   if (c->small_batch < -1 || c->small_batch > 1) return MOE_ERR_INVALID_ARG;
+  // the random gate options: RSample and RTS are k = 1 options, second-expert
+  // sampling a k = 2 one (as in the gate the options come from)
+  if (c->noisy_gate_policy < MOE_NOISE_NONE || c->noisy_gate_policy > MOE_NOISE_RSAMPLE) return MOE_ERR_INVALID_ARG;
+  if (c->use_rts != 0 && c->use_rts != 1) return MOE_ERR_INVALID_ARG;
+  if (c->second_expert_sampling != 0 && c->second_expert_sampling != 1) return MOE_ERR_INVALID_ARG;
+  if (c->noisy_gate_policy == MOE_NOISE_RSAMPLE && c->k != 1) return MOE_ERR_INVALID_ARG;
+  if (c->use_rts && c->k != 1) return MOE_ERR_INVALID_ARG;
+  if (c->second_expert_sampling && c->k != 2) return MOE_ERR_INVALID_ARG;
+  if (c->noisy_gate_policy == MOE_NOISE_JITTER && c->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   // kernels move rows as 16-byte vectors
   const int vec = c->dtype == MOE_BF16 ? 8 : 4;
   if (c->hidden_size % vec) return MOE_ERR_UNSUPPORTED;
@@ -70,7 +79,7 @@ struct Layout {
   // backward regions (save_preact == 1 only)
   int Ep;
   RouterChunks rc;
-  size_t logits, dwg, dlg, dl_hl, wfrag, top1, coef, dbpart, choff, wpart;
+  size_t logits, dwg, dlg, dl_hl, wfrag, top1, coef, dbpart, choff, wpart, xj;
   size_t total;
 };
 
@@ -121,6 +130,8 @@ Layout layout_of(const moe_config* c) {
   L.dbpart = take(train ? nbt * E * 4 : 0);
   L.choff = take(train ? (size_t)(kRouterMaxChunks + 1) * 4 : 0);
   L.wpart = take(train ? (size_t)L.rc.S * 2 * L.Ep * d * 4 : 0);
+  // the router's jittered input, rebuilt for its weight gradient
+  L.xj = take(train && c->noisy_gate_policy == MOE_NOISE_JITTER ? (size_t)L.T * d * 2 : 0);
   L.total = off;
   return L;
 }
@@ -167,8 +178,16 @@ moe_status run_gate(const moe_config* c, const Layout& L, const void* x, const v
   a.normalize = c->normalize_topk;
   a.loss_kind = c->loss_kind;
   a.num_tiles = L.tiles;
+  a.jitter = c->noisy_gate_policy == MOE_NOISE_JITTER;
+  a.rsample = c->noisy_gate_policy == MOE_NOISE_RSAMPLE;
+  a.second = c->second_expert_sampling;
+  a.seed_lo = (uint32_t)(c->seed & 0xffffffffu);
+  a.seed_hi = (uint32_t)(c->seed >> 32);
+  // jitter acts on the router's input: there is none when the logits are given
+  if (a.jitter && logits_in) return MOE_ERR_INVALID_ARG;
   MOE_TRY_HIP(launch_gate(a, c->dtype, s));
   MOE_TRY_HIP(launch_slot_finalize(a, L.tile_tokens, s));
+  if (c->use_rts && L.C >= 0) MOE_TRY_HIP(launch_rts_select(a, s));
   return MOE_OK;
 }
 
@@ -375,7 +394,8 @@ moe_status moe_layer_forward(const moe_config* cfg, const void* x, const void* w
   int32_t* off = at<int32_t>(ws, L.offset);
   // a few tokens, inference: the whole forward in one persistent launch
   const bool small = cfg->small_batch > 0 || (cfg->small_batch == 0 && L.T <= MOE_SMALL_BATCH_AUTO);
-  if (small && !cfg->save_preact &&
+  const bool random_gate = cfg->noisy_gate_policy != MOE_NOISE_NONE || cfg->use_rts || cfg->second_expert_sampling;
+  if (small && !cfg->save_preact && !random_gate &&
       decode_fits(L.T, cfg->hidden_size, cfg->ffn_hidden, cfg->num_experts, cfg->k, cfg->dtype)) {
     DecodeArgs da{};
     da.x = static_cast<const bf16*>(x);
@@ -501,6 +521,9 @@ moe_status run_input_grad(const moe_config* c, const Layout& L, const void* dx_d
   g.d = c->hidden_size;
   g.k = c->k;
   g.Ep = L.Ep;
+  g.jitter = c->noisy_gate_policy == MOE_NOISE_JITTER;
+  g.seed_lo = (uint32_t)(c->seed & 0xffffffffu);
+  g.seed_hi = (uint32_t)(c->seed >> 32);
   if (w_router)
     MOE_TRY_HIP(launch_router_pack(w_router, at<uint16_t>(ws, L.wfrag), c->num_experts, c->hidden_size, L.Ep, s));
   MOE_TRY_HIP(launch_input_grad(g, s));
@@ -511,6 +534,13 @@ moe_status run_router_wgrad(const moe_config* c, const Layout& L, const void* x,
                             void* ws, hipStream_t s) {
   RouterWgradArgs r{};
   r.x = x;
+  if (c->noisy_gate_policy == MOE_NOISE_JITTER) {
+    // dW_r = dlogits^T x_j: the input the router read
+    bf16* xj = at<bf16>(ws, L.xj);
+    MOE_TRY_HIP(launch_jitter_input(static_cast<const bf16*>(x), xj, L.T, c->hidden_size,
+                                    (uint32_t)(c->seed & 0xffffffffu), (uint32_t)(c->seed >> 32), s));
+    r.x = xj;
+  }
   r.dl_hl = at<uint16_t>(ws, L.dl_hl);
   r.dbpart = at<float>(ws, L.dbpart);
   r.choff = at<int32_t>(ws, L.choff);

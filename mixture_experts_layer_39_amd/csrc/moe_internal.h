@@ -81,9 +81,15 @@ struct GateArgs {
   int32_t d, E, k;
   int32_t normalize, loss_kind;
   int32_t num_tiles;
+  int32_t jitter, rsample, second;   // random gate options (router input jitter,
+                                     // Gumbel top-1, Gumbel second expert)
+  uint32_t seed_lo, seed_hi;         // Philox4x32-10 key
 };
 
 hipError_t launch_gate(const GateArgs& a, int dtype, hipStream_t s);
+// Random Token Selection (k = 1, with a capacity): after the slot fix-up,
+// every expert whose demand exceeds C keeps its C claims of largest priority.
+hipError_t launch_rts_select(const GateArgs& a, hipStream_t s);
 hipError_t launch_slot_finalize(const GateArgs& a, int tile_tokens, hipStream_t s);
 hipError_t launch_gate_empty(int32_t* expert_count, int32_t* expert_offset, float* gate_loss,
                              int E, hipStream_t s);
@@ -198,9 +204,15 @@ struct InputGradArgs {
   bf16* dx;                 // [T, d]
   int64_t T;
   int32_t d, k, Ep;
+  int32_t jitter;           // the router read x * factor: its term is scaled by the factor
+  uint32_t seed_lo, seed_hi;
 };
 hipError_t launch_router_pack(const void* w_router, uint16_t* wfrag, int E, int d, int Ep, hipStream_t s);
 hipError_t launch_input_grad(const InputGradArgs& a, hipStream_t s);
+// The router's jittered input bf16(x * factor) [T, d] (the forward gate's
+// arithmetic), for the router weight gradient.
+hipError_t launch_jitter_input(const bf16* x, bf16* xj, int64_t T, int d, uint32_t seed_lo, uint32_t seed_hi,
+                               hipStream_t s);
 
 // dW_r (fp32 [E, d], nullable) and db_r (fp32 [E], nullable) from the split
 // logit gradient and x; part: [S, 2*Ep, d] fp32, choff: [S+1] int32.

@@ -510,11 +510,15 @@ def router_backward(x, w_router, dlogits):
 
 
 def layer_backward(x, w_router, r, w1, w2, dout, dloss, *, act, dtype,
-                   normalize_topk=False, loss_kind=LOSS_BALANCE):
+                   normalize_topk=False, loss_kind=LOSS_BALANCE, router_input=None, router_input_scale=None):
     """Gradients of <dOut, out> + dloss * gate_loss for the layer whose
     forward ``r`` is (``layer_forward``'s result, with ``probs`` from the
     same logits).  ``w_router`` None means the logits were inputs: the
     logit gradient is returned instead of router gradients.
+    ``router_input`` / ``router_input_scale``: when the router read
+    x * scale rather than x (the jitter option of ``stochastic_gate``), its
+    weight gradient contracts with that input and its input gradient carries
+    the scale (the chain rule of logits = (x * scale) W_r^T).
 
     Returns a dict: dx (stored ``dtype``), dlogits (f32), dw_router, db_router
     (f32, or None), dw1, db1, dw2, db2 (as ``expert_ffn_backward``), and the
@@ -528,7 +532,9 @@ def layer_backward(x, w_router, r, w1, w2, dout, dloss, *, act, dtype,
     dl = gate_backward(r["probs"], idx, dwg, normalize_topk, loss_kind, dloss, dtype)
     dwr = dbr = None
     if w_router is not None:
-        dxr, dwr, dbr = router_backward(x, w_router, dl)
+        dxr, dwr, dbr = router_backward(x if router_input is None else router_input, w_router, dl)
+        if router_input_scale is not None:
+            dxr = dxr * np.asarray(router_input_scale, np.float64)
         dx = dx + dxr
         dwr, dbr = store(dwr, _f32_or_f64(dtype)), store(dbr, _f32_or_f64(dtype))
     return dict(dx=store(dx, dtype), dlogits=dl, dw_router=dwr, db_router=dbr,

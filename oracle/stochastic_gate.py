@@ -221,3 +221,17 @@ def route(logits, k, capacity_factor=1.0, min_capacity=4, drop_tokens=True, norm
     loss = O.gate_loss(p, idx, E, loss_kind)
     return dict(probs=p, expert_idx=idx, weight=w, capacity=C, slot=slot, demand=demand,
                 expert_count=count, expert_offset=offset, gate_loss=loss)
+
+
+def layer_backward_jitter(x, w_router, r, w1, w2, dout, dloss, *, act, dtype, seed, eps=JITTER_EPS,
+                          normalize_topk=False, loss_kind=O.LOSS_BALANCE):
+    """The layer backward when the router read the jittered input (R15):
+    dW_r = dlogits^T x_j with x_j = ``jittered_input``, and the router's
+    input gradient (dlogits W_r) times the factors; the bf16 rounding of
+    x * factor is taken as the identity, as in R13 for stored tensors."""
+    x = np.asarray(x, np.float64)
+    T, d = x.shape
+    return O.layer_backward(x, w_router, r, w1, w2, dout, dloss, act=act, dtype=dtype,
+                            normalize_topk=normalize_topk, loss_kind=loss_kind,
+                            router_input=jittered_input(x, seed, eps),
+                            router_input_scale=jitter_factors(seed, T, d, eps).astype(np.float64))

@@ -222,3 +222,47 @@ def test_seed_determinism():
     c = S.route(lg, 2, 1.0, 4, True, seed=43, second_sampling=True)
     assert np.array_equal(a["expert_idx"], b["expert_idx"])
     assert not np.array_equal(a["expert_idx"], c["expert_idx"])
+
+
+def test_jitter_backward_against_finite_differences():
+    """The router gradients under jitter, checked by float64 central
+    differences of <dOut, out> + dloss * loss through a router that reads
+    x * factor (no bf16 rounding in the float64 mode, so the chain rule is
+    exact), on a tiny layer with no ties."""
+    rng = np.random.default_rng(12)
+    T, d, E, h, k, seed = 6, 8, 3, 5, 2, 9
+    x = rng.normal(size=(T, d))
+    wr = rng.normal(size=(E, d)) * 0.5
+    w1 = rng.normal(size=(E, h, d)) * 0.3
+    b1 = rng.normal(size=(E, h)) * 0.1
+    w2 = rng.normal(size=(E, d, h)) * 0.3
+    b2 = rng.normal(size=(E, d)) * 0.1
+    dout = rng.normal(size=(T, d))
+    dloss = 0.7
+    f = S.jitter_factors(seed, T, d).astype(np.float64)
+
+    def objective(xx, ww):
+        lg = O.router_logits(xx * f, ww)
+        r = O.layer_forward(xx, lg, w1, b1, w2, b2, k=k, capacity_factor=10.0, min_capacity=1, drop_tokens=True,
+                            act=O.ACT_GELU, dtype="f64")
+        return float((dout * r["out"]).sum() + dloss * r["gate_loss"]), r
+
+    _, r = objective(x, wr)
+    g = O.layer_backward(x, wr, r, w1, w2, dout, dloss, act=O.ACT_GELU, dtype="f64", router_input=x * f,
+                         router_input_scale=f)
+    eps = 1e-6
+    for (i, j) in [(0, 0), (2, 5), (5, 7), (3, 1)]:
+        xp, xm = x.copy(), x.copy()
+        xp[i, j] += eps
+        xm[i, j] -= eps
+        fd = (objective(xp, wr)[0] - objective(xm, wr)[0]) / (2 * eps)
+        assert abs(g["dx"][i, j] - fd) <= 1e-6 * max(1.0, abs(fd))
+    for (e, j) in [(0, 0), (1, 4), (2, 7)]:
+        wp, wm = wr.copy(), wr.copy()
+        wp[e, j] += eps
+        wm[e, j] -= eps
+        fd = (objective(x, wp)[0] - objective(x, wm)[0]) / (2 * eps)
+        assert abs(g["dw_router"][e, j] - fd) <= 1e-6 * max(1.0, abs(fd))
+    # without the scale the input gradient would be off by the factors
+    g0 = O.layer_backward(x, wr, r, w1, w2, dout, dloss, act=O.ACT_GELU, dtype="f64")
+    assert not np.allclose(g0["dx"], g["dx"], rtol=1e-4, atol=0)
