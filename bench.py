@@ -68,6 +68,8 @@ def load_traffic(workload):
 
 def bwd_label(sp):
     b = sp.get("backward")
+    if sp.get("residual"):
+        return ", residual MoE (dense MLP mixed by softmax coefficients)"
     return "" if not b else (", layer backward" if b == "layer" else ", expert FFN backward")
 
 
@@ -90,6 +92,13 @@ def cpu_baseline(sp, inp, target_s=15.0):
     def run(ts):
         t0 = time.perf_counter()
         logits = lg_given[:ts] if lg_given is not None else O.router_logits(x[:ts], wr, br)
+        if sp.get("residual"):
+            from oracle import residual_moe as R
+            mlp = (f(inp["mlp_w1"]), f(inp["mlp_b1"]), f(inp["mlp_w2"]), f(inp["mlp_b2"]))
+            r = R.forward(x[:ts], logits, w1, b1, w2, b2, mlp, f(inp["coef_w"]), f(inp["coef_b"]), k=sp["k"],
+                          capacity_factor=sp["cf"], min_capacity=sp["min_cap"], drop_tokens=sp["drop"],
+                          act=sp["act"], dtype=sp["dtype"])
+            return time.perf_counter() - t0
         r = O.layer_forward(x[:ts], logits, w1, b1, w2, b2, k=sp["k"], capacity_factor=sp["cf"],
                             min_capacity=sp["min_cap"], drop_tokens=sp["drop"], act=sp["act"], dtype=sp["dtype"])
         if sp.get("backward") == "layer":
@@ -203,7 +212,7 @@ def main(argv=None):
     dt = B.MOE_BF16 if sp["dtype"] == "bf16" else B.MOE_F32
     esz = 2 if dt == B.MOE_BF16 else 4
     cfg = B.make_config(T, d, E, k, sp["cf"], sp["min_cap"], sp["drop"], h, sp["act"], dt,
-                        save_preact=bool(sp.get("backward")))
+                        save_preact=bool(sp.get("backward")), use_residual=bool(sp.get("residual")))
     ws = torch.empty(B.moe_workspace_size(cfg), dtype=torch.uint8, device=dev)
     out = torch.empty_like(inp["x"])
     loss = torch.empty(1, dtype=torch.float32, device=dev)
@@ -239,9 +248,17 @@ def main(argv=None):
             B.moe_expert_ffn_backward(cfg, xd_p, off_p, inp["w1"], inp["w2"], a_p, h_p, inp["dy"], dx, dw1, None,
                                       dw2, None, ws, stream=stream)
 
+    res = bool(sp.get("residual"))
+
     def step():
-        B.moe_layer_forward(cfg, inp["x"], inp["w_router"], inp["b_router"], inp["logits"], inp["w1"], inp["b1"],
-                            inp["w2"], inp["b2"], out, loss, count, ws=ws, stream=stream)
+        if res:
+            B.moe_residual_layer_forward(cfg, inp["x"], inp["w_router"], inp["b_router"], inp["logits"], inp["w1"],
+                                         inp["b1"], inp["w2"], inp["b2"], inp["mlp_w1"], inp["mlp_b1"],
+                                         inp["mlp_w2"], inp["mlp_b2"], inp["coef_w"], inp["coef_b"], out, loss,
+                                         count, ws=ws, stream=stream)
+        else:
+            B.moe_layer_forward(cfg, inp["x"], inp["w_router"], inp["b_router"], inp["logits"], inp["w1"],
+                                inp["b1"], inp["w2"], inp["b2"], out, loss, count, ws=ws, stream=stream)
         if bwd:
             backward()
 
@@ -264,6 +281,14 @@ def main(argv=None):
              offset=torch.empty(E + 1, dtype=torch.int32, device=dev))
     xd, a_p, hd_p, yd_p, _ = B.moe_workspace_views(cfg, ws)
     nst = 9 if layer else 5
+    if res:
+        # the dense branch on its own: the expert FFN entry point with one
+        # expert holding all T rows
+        cfg1 = B.make_config(T, d, 1, 1, 1.0, 0, False, h, sp["act"], dt)
+        off1 = torch.tensor([0, T], dtype=torch.int32, device=dev)
+        h1 = torch.empty(T, h, dtype=inp["x"].dtype, device=dev)
+        y1 = torch.empty(T, d, dtype=inp["x"].dtype, device=dev)
+        ws1 = torch.empty(max(B.moe_workspace_size(cfg1), 1), dtype=torch.uint8, device=dev)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)]
     acc = [0.0] * nst
     lg_out = torch.empty(T, E, dtype=torch.float32, device=dev) if layer else None
@@ -297,6 +322,9 @@ def main(argv=None):
         elif bwd:
             B.moe_expert_ffn_backward(cfg, xd, g["offset"], inp["w1"], inp["w2"], a_p, hd_p, inp["dy"], dx, dw1,
                                       None, dw2, None, ws, stream=stream)
+        elif res:
+            B.moe_expert_ffn(cfg1, inp["x"], off1, inp["mlp_w1"], inp["mlp_b1"], inp["mlp_w2"], inp["mlp_b2"], None,
+                             h1, y1, ws1, stream=stream)
         ev[nst].record(stream)
         if it >= a.warmup:
             torch.cuda.synchronize()
@@ -328,6 +356,12 @@ def main(argv=None):
         "combine": {"ms": st_ms[3], "bytes": comb_bytes, "GB/s": gbs(comb_bytes, st_ms[3]),
                     "frac_hbm": gbs(comb_bytes, st_ms[3]) / PEAK_HBM_GBS},
     }
+    if res:
+        dflops = 4 * T * d * h
+        stages["dense_mlp"] = {"ms": st_ms[4], "flops": dflops, "TFLOP/s": dflops / (st_ms[4] * 1e-3) / 1e12,
+                               "frac_mfma": dflops / (st_ms[4] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "launches": 2}
+        stages["note"] = ("combine + mix is fused in the step (it reads x, the kept y rows and the dense output); "
+                          "the combine stage above is the plain combine")
     bflops = 2 * ffn_flops   # dgrad (dH, dX) + wgrad (dW2, dW1): 4 GEMMs of 2*N*d*h
     if bwd and not layer:
         stages["expert_ffn_backward"] = {"ms": st_ms[4], "flops": bflops,
@@ -371,7 +405,7 @@ def main(argv=None):
             "config": {"workload": describe(sp) + bwd_label(sp).replace(",", " +"),
                        "tokens_per_step": T, "rows_kept": N},
             "roofline": roofline, "stages": stages}
-    if not a.no_small_batch and not bwd and sp["h"] and dt == B.MOE_BF16:
+    if not a.no_small_batch and not bwd and not res and sp["h"] and dt == B.MOE_BF16:
         line["small_batch"] = small_batch_latency(B, torch, sp, inp, dt, stream)
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(sp, inp)

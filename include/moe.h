@@ -136,6 +136,12 @@ typedef struct moe_config {
                               order; counts, offsets and loss unchanged     */
   int32_t second_expert_sampling; /* k == 2: the second expert is the argmax
                               over the other experts of fp32(logit + g)     */
+  int32_t use_residual;           /* 1: the residual MoE of PR-MoE ([ds.moe]
+                              §2.1 use_residual, §2.3, §3.3): the layer runs
+                              through moe_residual_layer_forward / _backward
+                              (moe_layer_forward and moe_layer_backward
+                              refuse it) and the workspace holds the dense
+                              branch's buffers                               */
   uint64_t seed;                  /* Philox key                             */
 } moe_config;
 
@@ -338,6 +344,52 @@ moe_status moe_layer_backward(const moe_config* cfg, const void* x, const void* 
                               const float* dloss, void* dx, float* dlogits, float* dw_router,
                               float* db_router, void* dw1, float* db1, void* dw2, float* db2, void* ws,
                               size_t ws_bytes, void* stream);
+
+/* Residual MoE forward (PR-MoE: [ds.moe] §2.1 use_residual, §2.3, §3.3;
+ * the mix is not on the pages, the published layer's is taken):
+ *   out[t] = c0[t] * moe[t] + c1[t] * mlp(x[t])
+ * moe: this layer's MoE output before rounding (gate, dispatch, experts,
+ * combine exactly as moe_layer_forward);  mlp: the expert's architecture
+ * with its own weights on every token, mlp_w1 [h, d] (or [d, d] when
+ * ffn_hidden == 0), mlp_b1 [h] (nullable), mlp_w2 [d, h] (NULL when
+ * ffn_hidden == 0), mlp_b2 [d] (nullable), dtype; its activation output
+ * and output are stored as dtype like an expert's;
+ * c[t] = softmax(x[t] · coef_w^T + coef_b) over two entries, coef_w [2, d]
+ * dtype, coef_b [2] fp32 (nullable); with coef_w NULL, c = (1, 1), the plain
+ * residual sum.  The sum and the mix are fp32 with one rounding of out.
+ * coef_out [T, 2] fp32 (nullable; the backward reads the workspace copy).
+ * Other arguments as in moe_layer_forward.  Requires cfg->use_residual == 1
+ * and bf16; the one-launch small-batch path is not used.  With
+ * save_preact the workspace keeps the dense branch's pre-activation for
+ * moe_residual_layer_backward. */
+moe_status moe_residual_layer_forward(const moe_config* cfg, const void* x, const void* w_router,
+                                      const float* b_router, const float* logits_in, const void* w1,
+                                      const void* b1, const void* w2, const void* b2, const void* mlp_w1,
+                                      const void* mlp_b1, const void* mlp_w2, const void* mlp_b2,
+                                      const void* coef_w, const float* coef_b, void* out, float* gate_loss,
+                                      int32_t* expert_count, float* coef_out, float* logits_out,
+                                      int32_t* expert_idx, int32_t* slot, float* weight, void* ws,
+                                      size_t ws_bytes, void* stream);
+
+/* Residual MoE backward, after moe_residual_layer_forward with the same cfg
+ * (save_preact = 1, use_residual = 1, ffn_hidden > 0, bf16) and ws.
+ * Gradients of <dout, out> + dloss * gate_loss: the MoE branch as
+ * moe_layer_backward with dout scaled by c0; the dense branch as an expert
+ * backward with dout scaled by c1 (mlp_dw1 [h, d], mlp_dw2 [d, h] bf16,
+ * mlp_db1 [h], mlp_db2 [d] fp32 nullable); the coefficients' logit gradient
+ * c * (dc - <c, dc>) with dc = (<dout, moe>, <dout, mlp>), giving
+ * dcoef_w [2, d] and dcoef_b [2] fp32 (nullable; need coef_w) and its term
+ * in dx.  dx [T, d] bf16 sums the three input gradients with one rounding.
+ * Other arguments as in moe_layer_backward. */
+moe_status moe_residual_layer_backward(const moe_config* cfg, const void* x, const void* w_router,
+                                       const void* w1, const void* w2, const void* mlp_w1,
+                                       const void* mlp_w2, const void* coef_w, const float* logits,
+                                       const int32_t* expert_idx, const int32_t* slot, const float* weight,
+                                       const void* dout, const float* dloss, void* dx, float* dlogits,
+                                       float* dw_router, float* db_router, void* dw1, float* db1, void* dw2,
+                                       float* db2, void* mlp_dw1, float* mlp_db1, void* mlp_dw2,
+                                       float* mlp_db2, float* dcoef_w, float* dcoef_b, void* ws,
+                                       size_t ws_bytes, void* stream);
 
 /* Device addresses, inside a workspace ws, of the intermediates that
  * moe_layer_forward leaves there (valid until the next call that uses ws):

@@ -25,7 +25,11 @@ class MoE:
     ``train()``), eval_capacity_factor after ``eval()``.  The expert is
     Linear(hidden, ffn_hidden) -> activation -> Linear(ffn_hidden, hidden),
     or one Linear(hidden, hidden) when ffn_hidden == 0.  Weights use the
-    nn.Linear [out, in] layout, stacked over experts.  small_batch selects
+    nn.Linear [out, in] layout, stacked over experts.  ``residual`` =
+    (mlp_w1, mlp_b1, mlp_w2, mlp_b2, coef_w, coef_b) makes it the residual MoE
+    of PR-MoE (use_residual): a dense MLP of the expert's shape mixed in by
+    softmax(x coef_w^T + coef_b), or summed when coef_w is None; a pyramid
+    is a stack of such layers with their own num_experts.  small_batch selects
     the one-launch forward for a few tokens (0 automatic, 1 always when it
     applies, -1 never).
 
@@ -41,7 +45,8 @@ class MoE:
     def __init__(self, hidden_size, num_experts, w_router, w1, b1=None, w2=None, b2=None, b_router=None,
                  k=1, capacity_factor=1.0, eval_capacity_factor=1.0, min_capacity=4, drop_tokens=True,
                  ffn_hidden=0, activation=MOE_ACT_NONE, normalize_topk=False, loss_kind=MOE_LOSS_BALANCE,
-                 small_batch=0, noisy_gate_policy=None, use_rts=False, top2_2nd_expert_sampling=False, seed=0):
+                 small_batch=0, noisy_gate_policy=None, use_rts=False, top2_2nd_expert_sampling=False, seed=0,
+                 residual=None):
         import torch
         self.hidden_size, self.num_experts, self.k = hidden_size, num_experts, k
         self.capacity_factor, self.min_capacity, self.drop_tokens = capacity_factor, min_capacity, drop_tokens
@@ -52,6 +57,10 @@ class MoE:
             raise ValueError(f"noisy_gate_policy must be None, 'Jitter' or 'RSample', not {noisy_gate_policy!r}")
         self.noisy_gate_policy, self.use_rts = policies[key], bool(use_rts)
         self.top2_2nd_expert_sampling, self.seed, self.steps = bool(top2_2nd_expert_sampling), int(seed), 0
+        # residual MoE (use_residual): (mlp_w1, mlp_b1, mlp_w2, mlp_b2, coef_w, coef_b) or None
+        if residual is not None and len(residual) != 6:
+            raise ValueError("residual is (mlp_w1, mlp_b1, mlp_w2, mlp_b2, coef_w, coef_b)")
+        self.residual = residual
         self.ffn_hidden, self.activation = ffn_hidden, activation
         self.normalize_topk, self.loss_kind = normalize_topk, loss_kind
         self.w_router, self.b_router = w_router, b_router
@@ -78,7 +87,8 @@ class MoE:
                        seed=(self.seed + self.steps) % 2 ** 64)
         return make_config(num_tokens, self.hidden_size, self.num_experts, self.k, cf, self.min_capacity,
                            self.drop_tokens, self.ffn_hidden, self.activation, self.dtype, self.normalize_topk,
-                           self.loss_kind, small_batch=self.small_batch, **rnd)
+                           self.loss_kind, small_batch=self.small_batch, use_residual=self.residual is not None,
+                           **rnd)
 
     def forward(self, x, logits=None):
         import torch
@@ -91,8 +101,12 @@ class MoE:
         out = torch.empty_like(x2)
         loss = torch.empty(1, dtype=torch.float32, device=x.device)
         count = torch.empty(self.num_experts, dtype=torch.int32, device=x.device)
-        moe_layer_forward(cfg, x2, self.w_router, self.b_router, logits, self.w1, self.b1, self.w2, self.b2,
-                          out, loss, count, ws=self._ws)
+        if self.residual is None:
+            moe_layer_forward(cfg, x2, self.w_router, self.b_router, logits, self.w1, self.b1, self.w2, self.b2,
+                              out, loss, count, ws=self._ws)
+        else:
+            binding.moe_residual_layer_forward(cfg, x2, self.w_router, self.b_router, logits, self.w1, self.b1,
+                                               self.w2, self.b2, *self.residual, out, loss, count, ws=self._ws)
         if self.training:
             self.steps += 1
         return out.reshape(shape), loss[0], count

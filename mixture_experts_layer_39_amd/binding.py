@@ -24,7 +24,8 @@ MOE_MAX_EXPERTS = 256
 EXPORTED = ("moe_status_string", "moe_capacity", "moe_max_rows", "moe_workspace_size", "moe_gate",
             "moe_dispatch", "moe_expert_ffn", "moe_expert_ffn_backward", "moe_combine",
             "moe_layer_forward", "moe_workspace_views", "moe_combine_backward", "moe_gate_backward",
-            "moe_dispatch_backward", "moe_router_backward", "moe_layer_backward")
+            "moe_dispatch_backward", "moe_router_backward", "moe_layer_backward", "moe_residual_layer_forward",
+            "moe_residual_layer_backward")
 
 
 class MoeConfig(ctypes.Structure):
@@ -46,6 +47,7 @@ class MoeConfig(ctypes.Structure):
         ("noisy_gate_policy", ctypes.c_int32),
         ("use_rts", ctypes.c_int32),
         ("second_expert_sampling", ctypes.c_int32),
+        ("use_residual", ctypes.c_int32),
         ("seed", ctypes.c_uint64),
     ]
 
@@ -53,12 +55,12 @@ class MoeConfig(ctypes.Structure):
 def make_config(num_tokens, hidden_size, num_experts, k=1, capacity_factor=1.0, min_capacity=4,
                 drop_tokens=True, ffn_hidden=0, activation=MOE_ACT_NONE, dtype=MOE_BF16,
                 normalize_topk=False, loss_kind=MOE_LOSS_BALANCE, save_preact=False, small_batch=0,
-                noisy_gate_policy=0, use_rts=False, second_expert_sampling=False, seed=0):
+                noisy_gate_policy=0, use_rts=False, second_expert_sampling=False, seed=0, use_residual=False):
     return MoeConfig(int(num_tokens), float(capacity_factor), int(hidden_size), int(num_experts), int(k),
                      int(min_capacity), int(bool(drop_tokens)), int(ffn_hidden), int(activation), int(dtype),
                      int(bool(normalize_topk)), int(loss_kind), int(bool(save_preact)), int(small_batch),
                      int(noisy_gate_policy), int(bool(use_rts)), int(bool(second_expert_sampling)),
-                     int(seed) & (2 ** 64 - 1))
+                     int(bool(use_residual)), int(seed) & (2 ** 64 - 1))
 
 
 class MoeError(RuntimeError):
@@ -96,6 +98,8 @@ def lib():
         L.moe_dispatch_backward.argtypes = [CFG] + [P] * 7 + [P, S, P]
         L.moe_router_backward.argtypes = [CFG] + [P] * 4 + [P, S, P]
         L.moe_layer_backward.argtypes = [CFG] + [P] * 18 + [P, S, P]
+        L.moe_residual_layer_forward.argtypes = [CFG] + [P] * 22 + [P, S, P]
+        L.moe_residual_layer_backward.argtypes = [CFG] + [P] * 27 + [P, S, P]
         for name in EXPORTED:
             if name != "moe_status_string":
                 getattr(L, name).restype = ctypes.c_int
@@ -230,3 +234,24 @@ def moe_layer_backward(cfg, x, w_router, w1, w2, dout, dloss, dx, dw1, dw2, *, l
                                     _ptr(expert_idx), _ptr(slot), _ptr(weight), _ptr(dout), _ptr(dloss), _ptr(dx),
                                     _ptr(dlogits), _ptr(dw_router), _ptr(db_router), _ptr(dw1), _ptr(db1),
                                     _ptr(dw2), _ptr(db2), _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def moe_residual_layer_forward(cfg, x, w_router, b_router, logits_in, w1, b1, w2, b2, mlp_w1, mlp_b1, mlp_w2,
+                               mlp_b2, coef_w, coef_b, out, gate_loss, expert_count, *, coef_out=None,
+                               logits_out=None, expert_idx=None, slot=None, weight=None, ws=None, stream=None):
+    _check(lib().moe_residual_layer_forward(
+        ctypes.byref(cfg), _ptr(x), _ptr(w_router), _ptr(b_router), _ptr(logits_in), _ptr(w1), _ptr(b1), _ptr(w2),
+        _ptr(b2), _ptr(mlp_w1), _ptr(mlp_b1), _ptr(mlp_w2), _ptr(mlp_b2), _ptr(coef_w), _ptr(coef_b), _ptr(out),
+        _ptr(gate_loss), _ptr(expert_count), _ptr(coef_out), _ptr(logits_out), _ptr(expert_idx), _ptr(slot),
+        _ptr(weight), _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def moe_residual_layer_backward(cfg, x, w_router, w1, w2, mlp_w1, mlp_w2, coef_w, dout, dloss, dx, dw1, dw2,
+                                mlp_dw1, mlp_dw2, *, logits=None, expert_idx=None, slot=None, weight=None,
+                                dlogits=None, dw_router=None, db_router=None, db1=None, db2=None, mlp_db1=None,
+                                mlp_db2=None, dcoef_w=None, dcoef_b=None, ws=None, stream=None):
+    _check(lib().moe_residual_layer_backward(
+        ctypes.byref(cfg), _ptr(x), _ptr(w_router), _ptr(w1), _ptr(w2), _ptr(mlp_w1), _ptr(mlp_w2), _ptr(coef_w),
+        _ptr(logits), _ptr(expert_idx), _ptr(slot), _ptr(weight), _ptr(dout), _ptr(dloss), _ptr(dx), _ptr(dlogits),
+        _ptr(dw_router), _ptr(db_router), _ptr(dw1), _ptr(db1), _ptr(dw2), _ptr(db2), _ptr(mlp_dw1), _ptr(mlp_db1),
+        _ptr(mlp_dw2), _ptr(mlp_db2), _ptr(dcoef_w), _ptr(dcoef_b), _ptr(ws), _nbytes(ws), _stream(stream)))

@@ -519,6 +519,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
 #pragma unroll
         for (int j = 0; j < 8; ++j) v[j] += rv[j];
       }
+      if (a.dx_add) {
+        // the residual MLP's input gradient
+        float xa[8];
+        const uint4 u = *reinterpret_cast<const uint4*>(a.dx_add + t * d + fl);
+        const uint32_t uu[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          xa[2 * q] = lo16(uu[q]);
+          xa[2 * q + 1] = hi16(uu[q]);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] += xa[j];
+      }
+      if (a.dlc) {
+        // the mixing coefficients' logit gradient through their Linear
+        const float g0 = a.dlc[2 * t], g1 = a.dlc[2 * t + 1];
+        const uint4 c0 = *reinterpret_cast<const uint4*>(a.coef_w + fl);
+        const uint4 c1 = *reinterpret_cast<const uint4*>(a.coef_w + d + fl);
+        const uint32_t u0[4] = {c0.x, c0.y, c0.z, c0.w}, u1[4] = {c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          v[2 * q] += g0 * lo16(u0[q]) + g1 * lo16(u1[q]);
+          v[2 * q + 1] += g0 * hi16(u0[q]) + g1 * hi16(u1[q]);
+        }
+      }
       *reinterpret_cast<uint4*>(a.dx + t * d + fl) = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
                                                                 pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
     }

@@ -45,6 +45,8 @@ moe_status check_config(const moe_config* c) {
   if (c->use_rts && c->k != 1) return MOE_ERR_INVALID_ARG;
   if (c->second_expert_sampling && c->k != 2) return MOE_ERR_INVALID_ARG;
   if (c->noisy_gate_policy == MOE_NOISE_JITTER && c->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (c->use_residual != 0 && c->use_residual != 1) return MOE_ERR_INVALID_ARG;
+  if (c->use_residual && c->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   // kernels move rows as 16-byte vectors
   const int vec = c->dtype == MOE_BF16 ? 8 : 4;
   if (c->hidden_size % vec) return MOE_ERR_UNSUPPORTED;
@@ -80,6 +82,7 @@ struct Layout {
   int Ep;
   RouterChunks rc;
   size_t logits, dwg, dlg, dl_hl, wfrag, top1, coef, dbpart, choff, wpart, xj;
+  size_t r_off, r_a, r_h, r_y, r_coef, r_dact, r_dx, r_dlc, r_cwpart, r_cbpart;   // residual MoE
   size_t total;
 };
 
@@ -132,6 +135,20 @@ Layout layout_of(const moe_config* c) {
   L.wpart = take(train ? (size_t)L.rc.S * 2 * L.Ep * d * 4 : 0);
   // the router's jittered input, rebuilt for its weight gradient
   L.xj = take(train && c->noisy_gate_policy == MOE_NOISE_JITTER ? (size_t)L.T * d * 2 : 0);
+  // the residual MoE's dense branch (one "expert" of all T rows), its
+  // coefficients, and for training its backward buffers
+  const bool res = c->use_residual != 0;
+  const int64_t nch = residual_coef_chunks(L.T);
+  L.r_off = take(res ? 8 : 0);
+  L.r_a = take(res && train && h > 0 ? (size_t)L.T * h * s : 0);
+  L.r_h = take(res && h > 0 ? (size_t)L.T * h * s : 0);
+  L.r_y = take(res ? (size_t)L.T * d * s : 0);
+  L.r_coef = take(res ? (size_t)L.T * 2 * 4 : 0);
+  L.r_dact = take(res && train && h > 0 ? (size_t)L.T * h * s : 0);
+  L.r_dx = take(res && train ? (size_t)L.T * d * s : 0);
+  L.r_dlc = take(res && train ? (size_t)L.T * 2 * 4 : 0);
+  L.r_cwpart = take(res && train ? (size_t)nch * 2 * d * 4 : 0);
+  L.r_cbpart = take(res && train ? (size_t)nch * 2 * 4 : 0);
   L.total = off;
   return L;
 }
@@ -230,6 +247,26 @@ moe_status run_ffn(const moe_config* c, const Layout& L, const void* x_disp, con
     MOE_TRY_HIP(launch_grouped_gemm(g, c->dtype, s));
   }
   return MOE_OK;
+}
+
+// Gate, dispatch and the expert FFNs of the multi-kernel forward (y_disp in
+// ws); the caller combines.
+moe_status forward_experts(const moe_config* cfg, const Layout& L, const void* x, const void* w_router,
+                           const float* b_router, const float* logits_in, const void* w1, const void* b1,
+                           const void* w2, const void* b2, float* gate_loss, int32_t* expert_count,
+                           float* logits_out, int32_t* idx, int32_t* sl, float* wt, int32_t* off, void* ws,
+                           hipStream_t s) {
+  // training: the backward needs the logits, so keep them when the caller does not
+  float* lg = (logits_out || !cfg->save_preact) ? logits_out : at<float>(ws, L.logits);
+  moe_status st =
+      run_gate(cfg, L, x, w_router, b_router, logits_in, lg, idx, sl, wt, expert_count, off, gate_loss, ws, s);
+  if (st != MOE_OK || L.T == 0) return st;
+  void* xd = at<void>(ws, L.x_disp);
+  void* hd = cfg->ffn_hidden > 0 ? at<void>(ws, L.h_disp) : nullptr;
+  void* as = (cfg->save_preact && cfg->ffn_hidden > 0) ? at<void>(ws, L.a_save) : nullptr;
+  void* yd = at<void>(ws, L.y_disp);
+  MOE_TRY_HIP(launch_dispatch(x, idx, sl, off, xd, L.T, cfg->k, cfg->hidden_size * esize(cfg), s));
+  return run_ffn(cfg, L, xd, off, w1, b1, w2, b2, as, hd, yd, s);
 }
 
 }  // namespace
@@ -380,6 +417,7 @@ moe_status moe_layer_forward(const moe_config* cfg, const void* x, const void* w
                              void* stream) {
   moe_status st = check_config(cfg);
   if (st != MOE_OK) return st;
+  if (cfg->use_residual) return MOE_ERR_INVALID_ARG;   // moe_residual_layer_forward takes the dense branch
   const bool tok = cfg->num_tokens > 0;
   if (tok && (!x || !out || (!logits_in && !w_router))) return MOE_ERR_INVALID_ARG;
   if (!w1 || !gate_loss || !expert_count || !ws) return MOE_ERR_INVALID_ARG;
@@ -435,18 +473,11 @@ moe_status moe_layer_forward(const moe_config* cfg, const void* x, const void* w
     if (e != hipErrorNotSupported) return MOE_ERR_HIP;
     (void)hipGetLastError();
   }
-  // training: the backward needs the logits, so keep them when the caller does not
-  float* lg = (logits_out || !cfg->save_preact) ? logits_out : at<float>(ws, L.logits);
-  st = run_gate(cfg, L, x, w_router, b_router, logits_in, lg, idx, sl, wt, expert_count, off, gate_loss, ws, s);
+  st = forward_experts(cfg, L, x, w_router, b_router, logits_in, w1, b1, w2, b2, gate_loss, expert_count,
+                       logits_out, idx, sl, wt, off, ws, s);
   if (st != MOE_OK || L.T == 0) return st;
-  void* xd = at<void>(ws, L.x_disp);
-  void* hd = cfg->ffn_hidden > 0 ? at<void>(ws, L.h_disp) : nullptr;
-  void* as = (cfg->save_preact && cfg->ffn_hidden > 0) ? at<void>(ws, L.a_save) : nullptr;
-  void* yd = at<void>(ws, L.y_disp);
-  MOE_TRY_HIP(launch_dispatch(x, idx, sl, off, xd, L.T, cfg->k, cfg->hidden_size * esize(cfg), s));
-  st = run_ffn(cfg, L, xd, off, w1, b1, w2, b2, as, hd, yd, s);
-  if (st != MOE_OK) return st;
-  MOE_TRY_HIP(launch_combine(yd, idx, sl, wt, off, out, L.T, cfg->k, cfg->hidden_size, cfg->dtype, s));
+  MOE_TRY_HIP(launch_combine(at<void>(ws, L.y_disp), idx, sl, wt, off, out, L.T, cfg->k, cfg->hidden_size,
+                             cfg->dtype, s));
   return MOE_OK;
 }
 
@@ -508,8 +539,12 @@ moe_status run_split(const moe_config* c, const Layout& L, const float* dlogits,
 
 moe_status run_input_grad(const moe_config* c, const Layout& L, const void* dx_disp, const int32_t* idx,
                           const int32_t* slot, const int32_t* offset, const void* w_router, void* dx, void* ws,
-                          hipStream_t s) {
+                          hipStream_t s, const void* dx_add = nullptr, const float* dlc = nullptr,
+                          const void* coef_w = nullptr) {
   InputGradArgs g{};
+  g.dx_add = static_cast<const bf16*>(dx_add);
+  g.dlc = dlc;
+  g.coef_w = static_cast<const bf16*>(coef_w);
   g.dx_disp = static_cast<const bf16*>(dx_disp);
   g.idx = idx;
   g.slot = slot;
@@ -567,6 +602,51 @@ moe_status check_backward(const moe_config* c, bool router_weights) {
   return MOE_OK;
 }
 
+// The layer backward after the combine's backward (dY_disp in ws's y_disp,
+// gate-weight gradient in ws): expert FFNs, gate, dispatch with the router
+// input term (plus the residual layer's extra terms), router weights.
+moe_status backward_experts(const moe_config* cfg, const Layout& L, const void* x, const void* w_router,
+                            const void* w1, const void* w2, const float* lg, const int32_t* idx, const int32_t* sl,
+                            const float* wt, const int32_t* off, const float* dloss, void* dx, float* dl,
+                            float* dw_router, float* db_router, void* dw1, float* db1, void* dw2, float* db2,
+                            void* ws, hipStream_t s, const void* dx_add = nullptr, const float* dlc = nullptr,
+                            const void* coef_w = nullptr) {
+  (void)wt;
+  const bool tok = L.T > 0;
+  void* yd = at<void>(ws, L.y_disp);
+  moe_status st;
+  // expert FFNs: dX_disp over dY_disp
+  GemmBwdArgs b;
+  b.X = at<void>(ws, L.x_disp);
+  b.W1 = w1;
+  b.W2 = w2;
+  b.A = at<void>(ws, L.a_save);
+  b.H = at<void>(ws, L.h_disp);
+  b.dY = yd;
+  b.dA = at<void>(ws, L.d_act);
+  b.dX = yd;
+  b.dW1 = dw1;
+  b.dW2 = dw2;
+  b.db1 = db1;
+  b.db2 = db2;
+  b.offset = off;
+  b.max_rows = L.T > 0 ? L.rows : 0;
+  b.E = cfg->num_experts;
+  b.d = cfg->hidden_size;
+  b.h = cfg->ffn_hidden;
+  b.act = cfg->activation;
+  MOE_TRY_HIP(launch_ffn_backward(b, cfg->dtype, s));
+  if (!tok) return run_router_wgrad(cfg, L, x, dw_router, db_router, ws, s);
+  // gate: logit gradient (and its split for the router products)
+  st = run_gate_backward(cfg, L, lg, idx, at<float>(ws, L.dwg), dloss, dl, w_router != nullptr, ws, s);
+  if (st != MOE_OK) return st;
+  // dispatch backward plus the router input gradient
+  st = run_input_grad(cfg, L, yd, idx, sl, off, w_router, dx, ws, s, dx_add, dlc, coef_w);
+  if (st != MOE_OK) return st;
+  if (dw_router || db_router) return run_router_wgrad(cfg, L, x, dw_router, db_router, ws, s);
+  return MOE_OK;
+}
+
 }  // namespace
 
 moe_status moe_gate_backward(const moe_config* cfg, const float* logits, const int32_t* expert_idx,
@@ -621,6 +701,7 @@ moe_status moe_layer_backward(const moe_config* cfg, const void* x, const void* 
                               void* ws, size_t ws_bytes, void* stream) {
   moe_status st = check_config(cfg);
   if (st != MOE_OK) return st;
+  if (cfg->use_residual) return MOE_ERR_INVALID_ARG;   // moe_residual_layer_backward
   if (cfg->ffn_hidden <= 0 || !ws || !w1 || !w2 || !dw1 || !dw2) return MOE_ERR_INVALID_ARG;
   if (!w_router && (dw_router || db_router)) return MOE_ERR_INVALID_ARG;
   const bool router_w = w_router && dw_router;
@@ -642,36 +723,173 @@ moe_status moe_layer_backward(const moe_config* cfg, const void* x, const void* 
   // combine backward: dY_disp over y_disp, gate-weight gradient
   MOE_TRY_HIP(launch_combine_backward(dout, yd, idx, sl, wt, off, yd, at<float>(ws, L.dwg), L.T, cfg->k,
                                       cfg->hidden_size, cfg->dtype, s));
-  // expert FFNs: dX_disp over dY_disp
-  GemmBwdArgs b;
-  b.X = at<void>(ws, L.x_disp);
-  b.W1 = w1;
-  b.W2 = w2;
-  b.A = at<void>(ws, L.a_save);
-  b.H = at<void>(ws, L.h_disp);
-  b.dY = yd;
-  b.dA = at<void>(ws, L.d_act);
-  b.dX = yd;
-  b.dW1 = dw1;
-  b.dW2 = dw2;
-  b.db1 = db1;
-  b.db2 = db2;
-  b.offset = off;
-  b.max_rows = L.T > 0 ? L.rows : 0;
-  b.E = cfg->num_experts;
-  b.d = cfg->hidden_size;
-  b.h = cfg->ffn_hidden;
-  b.act = cfg->activation;
-  MOE_TRY_HIP(launch_ffn_backward(b, cfg->dtype, s));
-  if (!tok) return run_router_wgrad(cfg, L, x, dw_router, db_router, ws, s);
-  // gate: logit gradient (and its split for the router products)
-  st = run_gate_backward(cfg, L, lg, idx, at<float>(ws, L.dwg), dloss, dl, w_router != nullptr, ws, s);
+  return backward_experts(cfg, L, x, w_router, w1, w2, lg, idx, sl, wt, off, dloss, dx, dl, dw_router, db_router,
+                          dw1, db1, dw2, db2, ws, s);
+}
+
+
+moe_status moe_residual_layer_forward(const moe_config* cfg, const void* x, const void* w_router,
+                                      const float* b_router, const float* logits_in, const void* w1,
+                                      const void* b1, const void* w2, const void* b2, const void* mlp_w1,
+                                      const void* mlp_b1, const void* mlp_w2, const void* mlp_b2,
+                                      const void* coef_w, const float* coef_b, void* out, float* gate_loss,
+                                      int32_t* expert_count, float* coef_out, float* logits_out,
+                                      int32_t* expert_idx, int32_t* slot, float* weight, void* ws,
+                                      size_t ws_bytes, void* stream) {
+  moe_status st = check_config(cfg);
   if (st != MOE_OK) return st;
-  // dispatch backward plus the router input gradient
-  st = run_input_grad(cfg, L, yd, idx, sl, off, w_router, dx, ws, s);
-  if (st != MOE_OK) return st;
-  if (dw_router || db_router) return run_router_wgrad(cfg, L, x, dw_router, db_router, ws, s);
+  if (!cfg->use_residual) return MOE_ERR_INVALID_ARG;
+  const int d = cfg->hidden_size, h = cfg->ffn_hidden;
+  const bool tok = cfg->num_tokens > 0;
+  if (tok && (!x || !out || (!logits_in && !w_router))) return MOE_ERR_INVALID_ARG;
+  if (!w1 || !mlp_w1 || !gate_loss || !expert_count || !ws) return MOE_ERR_INVALID_ARG;
+  if ((h > 0) != (w2 != nullptr) || (h > 0) != (mlp_w2 != nullptr)) return MOE_ERR_INVALID_ARG;
+  if (coef_b && !coef_w) return MOE_ERR_INVALID_ARG;
+  const Layout L = layout_of(cfg);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t* idx = expert_idx ? expert_idx : at<int32_t>(ws, L.idx);
+  int32_t* sl = slot ? slot : at<int32_t>(ws, L.slot);
+  float* wt = weight ? weight : at<float>(ws, L.weight);
+  int32_t* off = at<int32_t>(ws, L.offset);
+  // the MoE branch: gate, dispatch, experts (the combine is fused below)
+  st = forward_experts(cfg, L, x, w_router, b_router, logits_in, w1, b1, w2, b2, gate_loss, expert_count,
+                       logits_out, idx, sl, wt, off, ws, s);
+  if (st != MOE_OK || L.T == 0) return st;
+  // the dense branch: the grouped GEMM with one "expert" holding all T rows
+  int32_t* roff = at<int32_t>(ws, L.r_off);
+  MOE_TRY_HIP(launch_residual_offsets(roff, L.T, s));
+  GemmArgs g;
+  g.offset = roff;
+  g.max_rows = L.T;
+  g.E = 1;
+  g.X = x;
+  g.W = mlp_w1;
+  g.bias = mlp_b1;
+  if (h > 0) {
+    g.Y = at<void>(ws, L.r_h);
+    g.Apre = cfg->save_preact ? at<void>(ws, L.r_a) : nullptr;
+    g.N = h;
+    g.K = d;
+    g.act = cfg->activation;
+    MOE_TRY_HIP(launch_grouped_gemm(g, cfg->dtype, s));
+    g.X = at<void>(ws, L.r_h);
+    g.W = mlp_w2;
+    g.bias = mlp_b2;
+    g.Y = at<void>(ws, L.r_y);
+    g.Apre = nullptr;
+    g.N = d;
+    g.K = h;
+    g.act = ACT_NONE;
+  } else {
+    g.Y = at<void>(ws, L.r_y);
+    g.Apre = nullptr;
+    g.N = d;
+    g.K = d;
+    g.act = cfg->activation;
+  }
+  MOE_TRY_HIP(launch_grouped_gemm(g, cfg->dtype, s));
+  // the coefficients and the mix, with the combine of the MoE branch
+  ResidualArgs r{};
+  r.x = static_cast<const bf16*>(x);
+  r.coef_w = static_cast<const bf16*>(coef_w);
+  r.coef_b = coef_b;
+  r.y_disp = at<bf16>(ws, L.y_disp);
+  r.mlp_y = at<bf16>(ws, L.r_y);
+  r.expert_idx = idx;
+  r.slot = sl;
+  r.weight = wt;
+  r.offset = off;
+  r.out = static_cast<bf16*>(out);
+  r.coef = at<float>(ws, L.r_coef);
+  r.T = L.T;
+  r.d = d;
+  r.k = cfg->k;
+  r.coef_out = coef_out;
+  MOE_TRY_HIP(launch_residual_combine(r, s));
   return MOE_OK;
 }
 
+moe_status moe_residual_layer_backward(const moe_config* cfg, const void* x, const void* w_router,
+                                       const void* w1, const void* w2, const void* mlp_w1,
+                                       const void* mlp_w2, const void* coef_w, const float* logits,
+                                       const int32_t* expert_idx, const int32_t* slot, const float* weight,
+                                       const void* dout, const float* dloss, void* dx, float* dlogits,
+                                       float* dw_router, float* db_router, void* dw1, float* db1, void* dw2,
+                                       float* db2, void* mlp_dw1, float* mlp_db1, void* mlp_dw2,
+                                       float* mlp_db2, float* dcoef_w, float* dcoef_b, void* ws,
+                                       size_t ws_bytes, void* stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (!cfg->use_residual) return MOE_ERR_INVALID_ARG;
+  if (cfg->ffn_hidden <= 0 || !ws || !w1 || !w2 || !dw1 || !dw2) return MOE_ERR_INVALID_ARG;
+  if (!mlp_w1 || !mlp_w2 || !mlp_dw1 || !mlp_dw2) return MOE_ERR_INVALID_ARG;
+  if (!w_router && (dw_router || db_router)) return MOE_ERR_INVALID_ARG;
+  if (!coef_w && (dcoef_w || dcoef_b)) return MOE_ERR_INVALID_ARG;
+  const bool router_w = w_router && dw_router;
+  if ((st = check_backward(cfg, router_w)) != MOE_OK) return st;
+  if (cfg->ffn_hidden % 16) return MOE_ERR_UNSUPPORTED;
+  const bool tok = cfg->num_tokens > 0;
+  if (tok && (!x || !dout || !dx || (!w_router && !dlogits))) return MOE_ERR_INVALID_ARG;
+  const Layout L = layout_of(cfg);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int32_t* idx = expert_idx ? expert_idx : at<int32_t>(ws, L.idx);
+  const int32_t* sl = slot ? slot : at<int32_t>(ws, L.slot);
+  const float* wt = weight ? weight : at<float>(ws, L.weight);
+  const float* lg = logits ? logits : at<float>(ws, L.logits);
+  float* dl = dlogits ? dlogits : at<float>(ws, L.dlg);
+  const int32_t* off = at<int32_t>(ws, L.offset);
+  // the mix's backward: dY_disp over y_disp, the MLP's upstream over its
+  // output, the gate-weight and coefficient-logit gradients
+  ResidualArgs r{};
+  r.x = static_cast<const bf16*>(x);
+  r.coef_w = static_cast<const bf16*>(coef_w);
+  r.y_disp = at<bf16>(ws, L.y_disp);
+  r.mlp_y = at<bf16>(ws, L.r_y);
+  r.expert_idx = idx;
+  r.slot = sl;
+  r.weight = wt;
+  r.offset = off;
+  r.coef = at<float>(ws, L.r_coef);
+  r.dout = static_cast<const bf16*>(dout);
+  r.dw = at<float>(ws, L.dwg);
+  r.dlc = coef_w ? at<float>(ws, L.r_dlc) : nullptr;
+  r.cw_part = at<float>(ws, L.r_cwpart);
+  r.cb_part = at<float>(ws, L.r_cbpart);
+  r.dcoef_w = dcoef_w;
+  r.dcoef_b = dcoef_b;
+  r.T = L.T;
+  r.d = cfg->hidden_size;
+  r.k = cfg->k;
+  MOE_TRY_HIP(launch_residual_combine_backward(r, s));
+  // the dense branch's backward (one expert of all T rows); its input
+  // gradient is added to dx below
+  GemmBwdArgs b;
+  b.X = x;
+  b.W1 = mlp_w1;
+  b.W2 = mlp_w2;
+  b.A = at<void>(ws, L.r_a);
+  b.H = at<void>(ws, L.r_h);
+  b.dY = at<void>(ws, L.r_y);
+  b.dA = at<void>(ws, L.r_dact);
+  b.dX = at<void>(ws, L.r_dx);
+  b.dW1 = mlp_dw1;
+  b.dW2 = mlp_dw2;
+  b.db1 = mlp_db1;
+  b.db2 = mlp_db2;
+  b.offset = at<int32_t>(ws, L.r_off);
+  b.max_rows = L.T;
+  b.E = 1;
+  b.d = cfg->hidden_size;
+  b.h = cfg->ffn_hidden;
+  b.act = cfg->activation;
+  MOE_TRY_HIP(launch_ffn_backward(b, cfg->dtype, s));   // no tokens: zero weight gradients
+  // the MoE branch and dx with the dense branch's and the coefficients' terms
+  st = backward_experts(cfg, L, x, w_router, w1, w2, lg, idx, sl, wt, off, dloss, dx, dl, dw_router, db_router, dw1,
+                        db1, dw2, db2, ws, s, at<void>(ws, L.r_dx), r.dlc, coef_w);
+  if (st != MOE_OK) return st;
+  if (coef_w && (dcoef_w || dcoef_b)) MOE_TRY_HIP(launch_coef_wgrad(r, s));
+  return MOE_OK;
+}
 }  // extern "C"

@@ -206,6 +206,9 @@ struct InputGradArgs {
   int32_t d, k, Ep;
   int32_t jitter;           // the router read x * factor: its term is scaled by the factor
   uint32_t seed_lo, seed_hi;
+  const bf16* dx_add;       // [T, d] added to dx, or null (the residual MLP's input gradient)
+  const float* dlc;         // [T, 2] coefficient logit gradient, or null
+  const bf16* coef_w;       // [2, d]: with dlc, dx += dlc[t] · coef_w
 };
 hipError_t launch_router_pack(const void* w_router, uint16_t* wfrag, int E, int d, int Ep, hipStream_t s);
 hipError_t launch_input_grad(const InputGradArgs& a, hipStream_t s);
@@ -231,6 +234,37 @@ hipError_t launch_router_wgrad(const RouterWgradArgs& a, hipStream_t s);
 // The chunked product on the large-tile GEMM: part[c] = dl_hl[chunk c]^T x[chunk c].
 hipError_t launch_router_partials(const uint16_t* dl_hl, const void* x, const int32_t* choff, float* part,
                                   int64_t T, int S, int d, int Ep, hipStream_t s);
+
+// ---------------------------------------------------------------- residual MoE
+// Per-token parts of the residual (PR-MoE) layer, see residual.hip.
+struct ResidualArgs {
+  const bf16* x;             // [T, d]
+  const bf16* coef_w;        // [2, d] or null: then the coefficients are (1, 1)
+  const float* coef_b;       // [2] or null
+  bf16* y_disp;              // [rows, d]; the backward writes dY_disp over it
+  bf16* mlp_y;               // [T, d]; the backward writes the MLP's upstream over it
+  const int32_t* expert_idx; // [T, k]
+  const int32_t* slot;       // [T, k]
+  const float* weight;       // [T, k]
+  const int32_t* offset;     // [E+1]
+  bf16* out;                 // [T, d] forward output
+  float* coef;               // [T, 2] coefficients (forward out, backward in)
+  float* coef_out;           // [T, 2] the caller's copy (forward), or null
+  const bf16* dout;          // [T, d] backward upstream
+  float* dw;                 // [T, k] gate-weight gradient
+  float* dlc;                // [T, 2] coefficient logit gradient, or null (no coef_w)
+  float* cw_part;            // [chunks, 2, d] partial dW_c
+  float* cb_part;            // [chunks, 2] partial db_c
+  float* dcoef_w;            // [2, d] or null
+  float* dcoef_b;            // [2] or null
+  int64_t T;
+  int32_t d, k;
+};
+int residual_coef_chunks(int64_t T);
+hipError_t launch_residual_offsets(int32_t* off, int64_t T, hipStream_t s);
+hipError_t launch_residual_combine(const ResidualArgs& a, hipStream_t s);
+hipError_t launch_residual_combine_backward(const ResidualArgs& a, hipStream_t s);
+hipError_t launch_coef_wgrad(const ResidualArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------- small-batch forward
 // The whole forward in one persistent kernel for up to kDecodeMaxTokens

@@ -18,6 +18,10 @@ Workloads (shapes from the five benchmark configurations of the layer):
               plus an N(0,1) upstream gradient for the expert backward
   nodrop_e128_layer  the same layer with an N(0,1) upstream gradient of the
               layer output [T, d] for the whole layer's backward
+  residual_e64 the top2_e64 layer as a residual MoE (PR-MoE): after the
+              layer's tensors, a dense MLP of the expert's shape (W1 [h, d],
+              b1, W2 [d, h], b2) and the mixing coefficient Linear (W_c [2, d]
+              ~ N(0, 0.02), b_c [2] fp32 ~ N(0, 1))
 Activations and upstream gradients ~ N(0,1); weights and biases ~ N(0, 0.02)
 unless stated.
 """
@@ -45,6 +49,9 @@ WORKLOADS = {
     "nodrop_e128": dict(T=65536, d=4096, E=128, k=2, h=1536, act=ACT_GELU, dtype="bf16",
                         cf=1.0, min_cap=4, drop=False, wstd=0.02, logits_given=False,
                         zipf=None, seed=1005, backward=True),
+    "residual_e64": dict(T=16384, d=2048, E=64, k=2, h=5120, act=ACT_GELU, dtype="bf16",
+                         cf=1.25, min_cap=4, drop=True, wstd=0.02, logits_given=False,
+                         zipf=None, seed=1006, residual=True),
     "nodrop_e128_layer": dict(T=65536, d=4096, E=128, k=2, h=1536, act=ACT_GELU, dtype="bf16",
                               cf=1.0, min_cap=4, drop=False, wstd=0.02, logits_given=False,
                               zipf=None, seed=1005, backward="layer"),
@@ -105,4 +112,11 @@ def make_inputs(sp, device="cpu", seed=None, n_rows_grad=None):
     if sp.get("backward"):
         n = (T if sp["backward"] == "layer" else sp["k"] * T) if n_rows_grad is None else n_rows_grad
         out["dy"] = _draw(g, (n, d), 1.0, dev).to(dt)
+    if sp.get("residual"):
+        out["mlp_w1"] = _draw(g, (hid, d), std, dev).to(dt)
+        out["mlp_b1"] = _draw(g, (hid,), std, dev).to(dt)
+        out["mlp_w2"] = _draw(g, (d, h), std, dev).to(dt) if h > 0 else None
+        out["mlp_b2"] = _draw(g, (d,), std, dev).to(dt) if h > 0 else None
+        out["coef_w"] = _draw(g, (2, d), std, dev).to(dt)
+        out["coef_b"] = _draw(g, (2,), 1.0, dev)
     return out

@@ -45,7 +45,7 @@ int main(void) {
 #define F(n) printf(" %zu", offsetof(moe_config, n));
   F(num_tokens) F(capacity_factor) F(hidden_size) F(num_experts) F(k) F(min_capacity) F(drop_tokens)
   F(ffn_hidden) F(activation) F(dtype) F(normalize_topk) F(loss_kind) F(save_preact)
-  F(small_batch) F(noisy_gate_policy) F(use_rts) F(second_expert_sampling) F(seed)
+  F(small_batch) F(noisy_gate_policy) F(use_rts) F(second_expert_sampling) F(use_residual) F(seed)
   return 0;
 }'''
     with tempfile.TemporaryDirectory() as d:
@@ -129,6 +129,7 @@ def test_workspace_size_grows_with_problem():
     (dict(second_expert_sampling=True, k=1), B.MOE_ERR_INVALID_ARG),
     (dict(noisy_gate_policy=B.MOE_NOISE_JITTER, dtype=B.MOE_F32), B.MOE_ERR_UNSUPPORTED),
     (dict(small_batch=-2), B.MOE_ERR_INVALID_ARG),
+    (dict(use_residual=True, dtype=B.MOE_F32), B.MOE_ERR_UNSUPPORTED),
     (dict(hidden_size=500), B.MOE_ERR_UNSUPPORTED),
     (dict(ffn_hidden=100, activation=B.MOE_ACT_GELU), B.MOE_ERR_UNSUPPORTED),
     (dict(hidden_size=34, dtype=B.MOE_F32), B.MOE_ERR_UNSUPPORTED),
@@ -280,6 +281,36 @@ def test_backward_entry_points_validate_before_launch():
     assert L.moe_layer_backward(c, *args, FAKE, ws - 1, None) == B.MOE_ERR_WORKSPACE
     one = _cfg(hidden_size=256, ffn_hidden=0, save_preact=True)
     assert L.moe_layer_backward(ctypes.byref(one), *args, FAKE, 1 << 40, None) == B.MOE_ERR_INVALID_ARG
+
+
+def test_residual_entry_points_validate_before_launch():
+    L = B.lib()
+    res = _cfg(hidden_size=256, ffn_hidden=512, activation=B.MOE_ACT_GELU, use_residual=True, save_preact=True)
+    plain = _cfg(hidden_size=256, ffn_hidden=512, activation=B.MOE_ACT_GELU, save_preact=True)
+    r, p = ctypes.byref(res), ctypes.byref(plain)
+    ws = B.moe_workspace_size(res)
+    # the residual layer's dense branch and coefficients take workspace
+    assert ws > B.moe_workspace_size(plain)
+    fwd = [FAKE] * 22
+    assert L.moe_residual_layer_forward(p, *fwd, FAKE, 1 << 40, None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_residual_layer_forward(r, *fwd, FAKE, ws - 1, None) == B.MOE_ERR_WORKSPACE
+    no_mlp = list(fwd)
+    no_mlp[8] = None   # mlp_w1
+    assert L.moe_residual_layer_forward(r, *no_mlp, FAKE, ws, None) == B.MOE_ERR_INVALID_ARG
+    bias_only = list(fwd)
+    bias_only[12] = None   # coef_w NULL with coef_b given
+    assert L.moe_residual_layer_forward(r, *bias_only, FAKE, ws, None) == B.MOE_ERR_INVALID_ARG
+    # the plain entry points refuse a residual configuration
+    assert L.moe_layer_forward(r, *([FAKE] * 15), FAKE, 1 << 40, None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_layer_backward(r, *([FAKE] * 18), FAKE, 1 << 40, None) == B.MOE_ERR_INVALID_ARG
+    bwd = [FAKE] * 27
+    assert L.moe_residual_layer_backward(p, *bwd, FAKE, 1 << 40, None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_residual_layer_backward(r, *bwd, FAKE, ws - 1, None) == B.MOE_ERR_WORKSPACE
+    no_coef = list(bwd)
+    no_coef[6] = None   # coef_w NULL with dcoef_w given
+    assert L.moe_residual_layer_backward(r, *no_coef, FAKE, ws, None) == B.MOE_ERR_INVALID_ARG
+    inf = _cfg(hidden_size=256, ffn_hidden=512, activation=B.MOE_ACT_GELU, use_residual=True)
+    assert L.moe_residual_layer_backward(ctypes.byref(inf), *bwd, FAKE, 1 << 40, None) == B.MOE_ERR_INVALID_ARG
 
 
 def test_workspace_views_are_inside_workspace():
