@@ -122,20 +122,23 @@ def gumbel(u):
     return -np.log(-np.log(u))
 
 
-def jitter_factors(seed, T, d, eps=JITTER_EPS):
-    """fp32 factors (1 - eps) + (2 eps) * u for every element of x [T, d]:
-    the product and the sum are each rounded to fp32 (no fused step)."""
-    n = np.arange(T * d, dtype=np.int64).reshape(T, d)
+def jitter_factors(seed, T, d, eps=JITTER_EPS, rows=None):
+    """fp32 factors (1 - eps) + (2 eps) * u for every element of x [T, d]
+    (or of the given token rows only): the product and the sum are each
+    rounded to fp32 (no fused step)."""
+    t = np.arange(T, dtype=np.int64) if rows is None else np.asarray(rows, np.int64)
+    n = t[:, None] * d + np.arange(d, dtype=np.int64)[None, :]
     u = uniform01(draws(seed, STREAM_JITTER, n))
     return np.float32(1.0 - eps) + np.float32(2.0 * eps) * u
 
 
-def jittered_input(x, seed, eps=JITTER_EPS):
+def jittered_input(x, seed, eps=JITTER_EPS, rows=None):
     """The router's input under Jitter: x * factor in fp32, stored as bf16
-    (round to nearest even), as the router product reads it."""
+    (round to nearest even), as the router product reads it.  With ``rows``,
+    x holds those token rows only."""
     x = np.asarray(x, np.float32)
     T, d = x.shape
-    return O.round_bf16((x * jitter_factors(seed, T, d, eps)).astype(np.float64))
+    return O.round_bf16((x * jitter_factors(seed, T, d, eps, rows)).astype(np.float64))
 
 
 def noisy_keys(logits, seed, stream):

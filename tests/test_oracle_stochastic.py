@@ -209,6 +209,10 @@ def test_jitter_factors_and_input():
     # the factor is (1 - eps) + (2 eps) * u with two fp32 roundings
     u = S.uniform01(S.draws(17, S.STREAM_JITTER, np.arange(T * d))).reshape(T, d)
     assert np.array_equal(f, (np.float32(0.99) + (np.float32(0.02) * u).astype(np.float32)).astype(np.float32))
+    # selected rows give the same factors as the whole matrix
+    rows = np.array([5, 0, 63, 17])
+    assert np.array_equal(S.jitter_factors(17, T, d, rows=rows), f[rows])
+    assert np.array_equal(S.jittered_input(x[rows], 17, rows=rows), S.jittered_input(x, 17)[rows])
     # jitter leaves |x_j / x - 1| <= eps plus the bf16 rounding
     xj = S.jittered_input(x, 17)
     nz = x != 0
