@@ -227,3 +227,32 @@ def test_residual_full_size_sampled():
                 moe += r["weight"][t, j] * y[0]
         want[i] = c[i, 0] * moe + c[i, 1] * ym[i]
     close(f64(out[sel]), O.store(want, "bf16"), 2e-2)
+
+
+def test_residual_no_tokens():
+    """T = 0: the forward returns zero counts and loss; the backward zero
+    weight, bias and coefficient gradients."""
+    d, E, h = 256, 4, 128
+    inp = _inputs(1, d, E, h, seed=9)
+    cfg = B.make_config(0, d, E, 2, 1.0, 1, True, h, B.MOE_ACT_GELU, B.MOE_BF16, use_residual=True,
+                        save_preact=True)
+    ws = workspace(cfg, DEV)
+    f32 = dict(dtype=torch.float32, device=DEV)
+    loss, cnt = torch.full((1,), 5.0, **f32), torch.full((E,), 5, dtype=torch.int32, device=DEV)
+    out = torch.empty(0, d, dtype=torch.bfloat16, device=DEV)
+    B.moe_residual_layer_forward(cfg, None, inp["w_router"], None, None, inp["w1"], inp["b1"], inp["w2"], inp["b2"],
+                                 inp["m_w1"], inp["m_b1"], inp["m_w2"], inp["m_b2"], inp["c_w"], inp["c_b"], out,
+                                 loss, cnt, ws=ws)
+    g = {n: torch.full(s, 7.0, dtype=dt, device=DEV) for n, s, dt in
+         (("dw1", (E, h, d), torch.bfloat16), ("dw2", (E, d, h), torch.bfloat16), ("db1", (E, h), torch.float32),
+          ("db2", (E, d), torch.float32), ("mdw1", (h, d), torch.bfloat16), ("mdw2", (d, h), torch.bfloat16),
+          ("mdb1", (h,), torch.float32), ("mdb2", (d,), torch.float32), ("dwr", (E, d), torch.float32),
+          ("dbr", (E,), torch.float32), ("dcw", (2, d), torch.float32), ("dcb", (2,), torch.float32))}
+    B.moe_residual_layer_backward(cfg, None, inp["w_router"], inp["w1"], inp["w2"], inp["m_w1"], inp["m_w2"],
+                                  inp["c_w"], None, None, None, g["dw1"], g["dw2"], g["mdw1"], g["mdw2"],
+                                  dw_router=g["dwr"], db_router=g["dbr"], db1=g["db1"], db2=g["db2"],
+                                  mlp_db1=g["mdb1"], mlp_db2=g["mdb2"], dcoef_w=g["dcw"], dcoef_b=g["dcb"], ws=ws)
+    torch.cuda.synchronize()
+    assert float(loss[0]) == 0.0 and int(cnt.abs().sum()) == 0
+    for n, t in g.items():
+        assert not t.float().abs().sum().item(), n

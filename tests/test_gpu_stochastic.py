@@ -325,3 +325,19 @@ def test_full_size_jitter_and_second_expert_sampling():
     np.testing.assert_array_equal(idx[:, 0], O.top_k(L, 1)[:, 0])
     _check_choice(idx[:, 1], S.noisy_keys(L, seed, S.STREAM_SECOND), exclude=idx[:, 0])
     _downstream(g, L, 2, sp["cf"], sp["min_cap"], True, seed, rts=False)
+
+
+def test_random_gate_no_tokens_and_no_overflow():
+    """T = 0 with every option on runs nothing and returns zeros; RTS with
+    room for every claim keeps the first-come slots."""
+    cfg = B.make_config(0, 128, 4, 1, 1.0, 4, True, 0, B.MOE_ACT_NONE, B.MOE_BF16, use_rts=True,
+                        noisy_gate_policy=B.MOE_NOISE_RSAMPLE, seed=3)
+    g = _gate(cfg, logits=torch.zeros(0, 4, device=DEV))
+    assert int(g["count"].abs().sum()) == 0 and float(g["loss"][0]) == 0.0
+    T, E = 500, 8
+    lg = torch.randn(T, E, generator=torch.Generator(device=DEV).manual_seed(4), device=DEV)
+    cfg = B.make_config(T, 128, E, 1, 8.0, 4, True, 0, B.MOE_ACT_NONE, B.MOE_BF16, use_rts=True, seed=3)
+    g = _gate(cfg, logits=lg)
+    L = f64(lg)
+    r = O.route(L, 1, 8.0, 4, True)
+    np.testing.assert_array_equal(i64(g["slot"]), r["slot"])
