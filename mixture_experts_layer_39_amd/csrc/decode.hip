@@ -16,7 +16,7 @@
 // runtime's cooperative grid sync took 30-60 us per barrier here, and its
 // launch about 20 us more than a plain one):
 //  1. Router products: items of 16 experts x 16 tokens x one of ks slices of
-//     K (ks grows while the items fit the grid, so a few tokens still spread
+//     K (ks grows while there are at most 16 items, so a few tokens still spread
 //     the router weight over many CUs), the four wavefronts splitting the
 //     slice (v_mfma_f32_16x16x32_bf16), fp32 partials.
 //  2. Routing: a wavefront per token adds the slices in order (+ bias), then
@@ -670,11 +670,13 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   const int grid = cus;
   DecodeArgs args = a;
   // K slices of the router product: the largest divisor of d / 128 (at most
-  // kDecodeMaxSlices) that keeps the item count within the grid
+  // kDecodeMaxSlices) that keeps the items at 16 or fewer (more slices spread
+  // the router weight wider but give the routing phase more partial sums to
+  // gather; 16 items measured best at 1 and 16 tokens)
   const int ntile = ((a.E + 15) / 16) * ((a.T + 15) / 16);
   args.ks = 1;
   for (int c = 2; c <= kDecodeMaxSlices; ++c)
-    if ((a.d / 128) % c == 0 && ntile * c <= grid) args.ks = c;
+    if ((a.d / 128) % c == 0 && ntile * c <= 16) args.ks = c;
   hipLaunchKernelGGL(decode_init_kernel, dim3(1), dim3(256), 0, s, a.bar);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // a plain launch: the cooperative launch API waits for the device to drain
