@@ -68,6 +68,8 @@ def load_traffic(workload):
 
 def bwd_label(sp):
     b = sp.get("backward")
+    if sp.get("random_gate"):
+        return ", seeded random gate (router input jitter, sampled second expert)"
     if sp.get("residual"):
         return ", residual MoE (dense MLP mixed by softmax coefficients)"
     return "" if not b else (", layer backward" if b == "layer" else ", expert FFN backward")
@@ -92,6 +94,15 @@ def cpu_baseline(sp, inp, target_s=15.0):
     def run(ts):
         t0 = time.perf_counter()
         logits = lg_given[:ts] if lg_given is not None else O.router_logits(x[:ts], wr, br)
+        if sp.get("random_gate"):
+            from oracle import stochastic_gate as S
+            xj = S.jittered_input(x[:ts], 12345, rows=np.arange(ts))
+            rr = S.route(O.router_logits(xj, wr, br), sp["k"], sp["cf"], sp["min_cap"], sp["drop"], seed=12345,
+                         second_sampling=True)
+            xd = O.dispatch(x[:ts], rr["expert_idx"], rr["slot"], rr["expert_offset"])
+            _, _, y = O.expert_ffn(xd, rr["expert_offset"], w1, b1, w2, b2, sp["act"], sp["dtype"])
+            O.combine(y, rr["expert_idx"], rr["slot"], rr["weight"], rr["expert_offset"], ts, sp["dtype"])
+            return time.perf_counter() - t0
         if sp.get("residual"):
             from oracle import residual_moe as R
             mlp = (f(inp["mlp_w1"]), f(inp["mlp_b1"]), f(inp["mlp_w2"]), f(inp["mlp_b2"]))
@@ -211,8 +222,10 @@ def main(argv=None):
     T, d, E, k, h = sp["T"], sp["d"], sp["E"], sp["k"], sp["h"]
     dt = B.MOE_BF16 if sp["dtype"] == "bf16" else B.MOE_F32
     esz = 2 if dt == B.MOE_BF16 else 4
+    rnd = dict(noisy_gate_policy=B.MOE_NOISE_JITTER, second_expert_sampling=True, seed=12345) \
+        if sp.get("random_gate") else {}
     cfg = B.make_config(T, d, E, k, sp["cf"], sp["min_cap"], sp["drop"], h, sp["act"], dt,
-                        save_preact=bool(sp.get("backward")), use_residual=bool(sp.get("residual")))
+                        save_preact=bool(sp.get("backward")), use_residual=bool(sp.get("residual")), **rnd)
     ws = torch.empty(B.moe_workspace_size(cfg), dtype=torch.uint8, device=dev)
     out = torch.empty_like(inp["x"])
     loss = torch.empty(1, dtype=torch.float32, device=dev)
@@ -405,7 +418,7 @@ def main(argv=None):
             "config": {"workload": describe(sp) + bwd_label(sp).replace(",", " +"),
                        "tokens_per_step": T, "rows_kept": N},
             "roofline": roofline, "stages": stages}
-    if not a.no_small_batch and not bwd and not res and sp["h"] and dt == B.MOE_BF16:
+    if not a.no_small_batch and not bwd and not res and not sp.get("random_gate") and sp["h"] and dt == B.MOE_BF16:
         line["small_batch"] = small_batch_latency(B, torch, sp, inp, dt, stream)
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(sp, inp)

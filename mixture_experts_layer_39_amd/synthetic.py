@@ -18,6 +18,9 @@ Workloads (shapes from the five benchmark configurations of the layer):
               plus an N(0,1) upstream gradient for the expert backward
   nodrop_e128_layer  the same layer with an N(0,1) upstream gradient of the
               layer output [T, d] for the whole layer's backward
+  random_e64  the top2_e64 layer and inputs with the seeded random gate
+              options of a training step on (router input jitter, sampled
+              second expert)
   residual_e64 the top2_e64 layer as a residual MoE (PR-MoE): after the
               layer's tensors, a dense MLP of the expert's shape (W1 [h, d],
               b1, W2 [d, h], b2) and the mixing coefficient Linear (W_c [2, d]
@@ -49,6 +52,9 @@ WORKLOADS = {
     "nodrop_e128": dict(T=65536, d=4096, E=128, k=2, h=1536, act=ACT_GELU, dtype="bf16",
                         cf=1.0, min_cap=4, drop=False, wstd=0.02, logits_given=False,
                         zipf=None, seed=1005, backward=True),
+    "random_e64": dict(T=16384, d=2048, E=64, k=2, h=5120, act=ACT_GELU, dtype="bf16",
+                       cf=1.25, min_cap=4, drop=True, wstd=0.02, logits_given=False,
+                       zipf=None, seed=1003, random_gate=True),
     "residual_e64": dict(T=16384, d=2048, E=64, k=2, h=5120, act=ACT_GELU, dtype="bf16",
                          cf=1.25, min_cap=4, drop=True, wstd=0.02, logits_given=False,
                          zipf=None, seed=1006, residual=True),
