@@ -293,6 +293,7 @@ def main(argv=None):
              weight=torch.empty(T, k, dtype=torch.float32, device=dev),
              offset=torch.empty(E + 1, dtype=torch.int32, device=dev))
     xd, a_p, hd_p, yd_p, _ = B.moe_workspace_views(cfg, ws)
+    h_ld = B.moe_workspace_h_ld(cfg)   # the pitch the fused forward keeps h_disp at
     nst = 9 if layer else 5
     if res:
         # the dense branch on its own: the expert FFN entry point with one
@@ -313,7 +314,7 @@ def main(argv=None):
         B.moe_dispatch(cfg, inp["x"], g["idx"], g["slot"], g["offset"], xd, stream=stream)
         ev[2].record(stream)
         B.moe_expert_ffn(cfg, xd, g["offset"], inp["w1"], inp["b1"], inp["w2"], inp["b2"], a_p if bwd else None,
-                         hd_p, yd_p, ws, stream=stream)
+                         hd_p, yd_p, ws, stream=stream, h_ld=h_ld)
         ev[3].record(stream)
         B.moe_combine(cfg, yd_p, g["idx"], g["slot"], g["weight"], g["offset"], out, stream=stream)
         ev[4].record(stream)

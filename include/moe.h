@@ -206,10 +206,15 @@ moe_status moe_dispatch(const moe_config* cfg, const void* x, const int32_t* exp
  * a, h and y are stored as dtype.  b1/b2 nullable (no bias).
  *   x_disp device [rows, d]; h_disp device [rows, h]; y_disp device [rows, d]
  *   a_save device [rows, h], nullable: the pre-activation for the backward
- * where rows >= expert_offset[E] (moe_max_rows suffices). */
+ * where rows >= expert_offset[E] (moe_max_rows suffices).  h_ld is the row
+ * pitch of h_disp and a_save in elements: 0 or h for contiguous rows, or
+ * h + 64 (only for bf16 with d and h multiples of 64, else
+ * MOE_ERR_UNSUPPORTED; MOE_ERR_INVALID_ARG for any other value).  An odd
+ * number of 128-byte lines per row lets the second Linear read h_disp
+ * faster; moe_workspace_h_ld gives the pitch moe_layer_forward uses. */
 moe_status moe_expert_ffn(const moe_config* cfg, const void* x_disp, const int32_t* expert_offset,
                           const void* w1, const void* b1, const void* w2, const void* b2,
-                          void* a_save, void* h_disp, void* y_disp,
+                          void* a_save, void* h_disp, int64_t h_ld, void* y_disp,
                           void* ws, size_t ws_bytes, void* stream);
 
 /* Backward of the expert FFNs for an upstream gradient dy_disp [rows, d]
@@ -394,10 +399,19 @@ moe_status moe_residual_layer_backward(const moe_config* cfg, const void* x, con
 /* Device addresses, inside a workspace ws, of the intermediates that
  * moe_layer_forward leaves there (valid until the next call that uses ws):
  * packed x_disp [rows, d], a_save [rows, h] (only with cfg->save_preact),
- * h_disp [rows, h], y_disp [rows, d] and expert_offset [E+1] int32.  Any
+ * h_disp [rows, h], y_disp [rows, d] and expert_offset [E+1] int32.  The
+ * rows of h_disp are contiguous with cfg->save_preact; without it the
+ * forward may keep them at a pitch of h + 64 elements, in a region sized
+ * for that pitch.  Any
  * output pointer may be NULL.  Host only; computes addresses, reads nothing. */
 moe_status moe_workspace_views(const moe_config* cfg, void* ws, void** x_disp, void** a_save,
                                void** h_disp, void** y_disp, int32_t** expert_offset);
+
+/* The row pitch (elements) at which moe_layer_forward keeps h_disp in the
+ * workspace for this cfg (h, or h + 64 without save_preact as described at
+ * moe_workspace_views; 0 when ffn_hidden == 0).  Host only;
+ * MOE_ERR_INVALID_ARG for an invalid cfg or a NULL h_ld. */
+moe_status moe_workspace_h_ld(const moe_config* cfg, int64_t* h_ld);
 
 #ifdef __cplusplus
 }

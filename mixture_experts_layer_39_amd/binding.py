@@ -25,7 +25,7 @@ EXPORTED = ("moe_status_string", "moe_capacity", "moe_max_rows", "moe_workspace_
             "moe_dispatch", "moe_expert_ffn", "moe_expert_ffn_backward", "moe_combine",
             "moe_layer_forward", "moe_workspace_views", "moe_combine_backward", "moe_gate_backward",
             "moe_dispatch_backward", "moe_router_backward", "moe_layer_backward", "moe_residual_layer_forward",
-            "moe_residual_layer_backward")
+            "moe_residual_layer_backward", "moe_workspace_h_ld")
 
 
 class MoeConfig(ctypes.Structure):
@@ -88,11 +88,12 @@ def lib():
         L.moe_workspace_size.argtypes = [CFG, ctypes.POINTER(ctypes.c_size_t)]
         L.moe_gate.argtypes = [CFG] + [P] * 11 + [P, S, P]
         L.moe_dispatch.argtypes = [CFG] + [P] * 5 + [P]
-        L.moe_expert_ffn.argtypes = [CFG] + [P] * 9 + [P, S, P]
+        L.moe_expert_ffn.argtypes = [CFG] + [P] * 8 + [ctypes.c_int64, P, P, S, P]
         L.moe_expert_ffn_backward.argtypes = [CFG] + [P] * 12 + [P, S, P]
         L.moe_combine.argtypes = [CFG] + [P] * 6 + [P]
         L.moe_layer_forward.argtypes = [CFG] + [P] * 15 + [P, S, P]
         L.moe_workspace_views.argtypes = [CFG, P] + [ctypes.POINTER(P)] * 5
+        L.moe_workspace_h_ld.argtypes = [CFG, ctypes.POINTER(ctypes.c_int64)]
         L.moe_combine_backward.argtypes = [CFG] + [P] * 8 + [P]
         L.moe_gate_backward.argtypes = [CFG] + [P] * 5 + [P, S, P]
         L.moe_dispatch_backward.argtypes = [CFG] + [P] * 7 + [P, S, P]
@@ -153,6 +154,13 @@ def moe_workspace_size(cfg):
     return c.value
 
 
+def moe_workspace_h_ld(cfg):
+    """Row pitch (elements) of h_disp in the workspace after moe_layer_forward."""
+    v = ctypes.c_int64()
+    _check(lib().moe_workspace_h_ld(ctypes.byref(cfg), ctypes.byref(v)))
+    return v.value
+
+
 def moe_workspace_views(cfg, ws):
     outs = [ctypes.c_void_p() for _ in range(5)]
     _check(lib().moe_workspace_views(ctypes.byref(cfg), _ptr(ws), *[ctypes.byref(o) for o in outs]))
@@ -173,11 +181,12 @@ def moe_dispatch(cfg, x, expert_idx, slot, expert_offset, x_disp, stream=None):
                               _ptr(x_disp), _stream(stream)))
 
 
-def moe_expert_ffn(cfg, x_disp, expert_offset, w1, b1, w2, b2, a_save, h_disp, y_disp, ws=None, stream=None):
+def moe_expert_ffn(cfg, x_disp, expert_offset, w1, b1, w2, b2, a_save, h_disp, y_disp, ws=None, stream=None,
+                   h_ld=0):
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().moe_expert_ffn(ctypes.byref(cfg), _ptr(x_disp), _ptr(expert_offset), _ptr(w1), _ptr(b1),
-                                _ptr(w2), _ptr(b2), _ptr(a_save), _ptr(h_disp), _ptr(y_disp), _ptr(ws), nbytes,
-                                _stream(stream)))
+                                _ptr(w2), _ptr(b2), _ptr(a_save), _ptr(h_disp), int(h_ld), _ptr(y_disp), _ptr(ws),
+                                nbytes, _stream(stream)))
 
 
 def moe_expert_ffn_backward(cfg, x_disp, expert_offset, w1, w2, a_save, h_disp, dy_disp, dx_disp, dw1, db1, dw2,

@@ -618,11 +618,12 @@ __device__ __forceinline__ void big_tile(const BigArgs& a, const BigCtx& c, cons
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  // Fragment registers: two sets, so that sub-step i+1's fragments are read
-  // while sub-step i's MFMAs run (sub-step i uses set i & 1).  Sub-step i of
-  // a 64-wide K step covers, for lane half h, the 8 K values of chunk h*4+i
-  // (the same order on both operands, which leaves the dot product alone).
-  bf16x8 fa[2][4], fb[2][NB > 0 ? NB : 1];
+  // Fragment registers: four sets, so that sub-step i+2's fragments are read
+  // while sub-step i's MFMAs run (sub-step i uses set i), two sub-steps
+  // (about 1000 cycles) ahead of their use.  Sub-step i of a 64-wide K step
+  // covers, for lane half h, the 8 K values of chunk h*4+i (the same order
+  // on both operands, which leaves the dot product alone).
+  bf16x8 fa[4][4], fb[4][NB > 0 ? NB : 1];
   constexpr int NM = 4 * NB;       // MFMAs per sub-step
   constexpr int NR = 4 + NB;       // fragment reads per sub-step
   // transposed-read source columns of this lane within a 32-wide block: the
@@ -658,11 +659,12 @@ __device__ __forceinline__ void big_tile(const BigArgs& a, const BigCtx& c, cons
     acc[ff][tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][ff], fb[set][tt], acc[ff][tt], 0, 0, 0);
   };
   // One sub-step in a fixed issue order: each MFMA is followed by its share
-  // of the next sub-step's fragment reads (one after each of the first NR
-  // MFMAs) and, when loading, of the 16 global->LDS loads, so that the memory
-  // instructions issue in the shadow of the MFMAs instead of in a bubble.
+  // of the fragment reads of the sub-step two ahead (one after each of the
+  // first NR MFMAs) and, when loading, of half (lhalf) of the 16
+  // global->LDS loads, so that the memory instructions issue in the shadow
+  // of the MFMAs instead of in a bubble.
   auto substep = [&](auto loads, int mset, int rstage, int ri, int rset, __amdgpu_buffer_rsrc_t llr, int lstage,
-                     int lkstep) {
+                     int lkstep, int lhalf) {
     constexpr bool LOADS = decltype(loads)::value;
     constexpr int NJ = NM > NR ? NM : NR;
 #pragma unroll
@@ -671,9 +673,13 @@ __device__ __forceinline__ void big_tile(const BigArgs& a, const BigCtx& c, cons
       if constexpr (LOADS) {
         if constexpr (NM > 0) {
 #pragma unroll
-          for (int q = j * 16 / NM; q < (j + 1) * 16 / NM && j < NM; ++q) big_issue_one(c, llr, lstage, lkstep, q);
+          for (int q = j * 8 / NM; q < (j + 1) * 8 / NM && j < NM; ++q)
+            big_issue_one(c, llr, lstage, lkstep, lhalf * 8 + q);
         } else {
-          if (j == 0) big_issue(c, llr, lstage, lkstep);
+          if (j == 0) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) big_issue_one(c, llr, lstage, lkstep, lhalf * 8 + q);
+          }
         }
       }
       if (j < NR && ri >= 0) read1(rstage, ri, rset, j);
@@ -684,14 +690,15 @@ __device__ __forceinline__ void big_tile(const BigArgs& a, const BigCtx& c, cons
   using Loads = std::integral_constant<bool, true>;
   const __amdgpu_buffer_rsrc_t no_lr = make_rsrc(a.tok, 0);
   // Stage s holds K step s (mod 2, offset by sb).  The one barrier per step
-  // sits before sub-step 3: by then every wave has read all of the current
-  // stage (so the loads two steps ahead may overwrite it) and the next stage
-  // has landed (so its first fragments can be read while sub-step 3
-  // computes).  The last step is peeled off so that in the loop sub-step 3's
-  // operands are known to have arrived at the barrier's wait.  What sub-step
-  // 3 of step kt loads into the stage it has just finished: step kt+2 of this
-  // tile, else step 0 of the next tile, else nothing (a descriptor with no
-  // records: the loads return zeros and touch no memory).
+  // sits before sub-step 2: by then every wave has read all of the current
+  // stage (sub-steps 2 and 3 were read during 0 and 1, so the loads two
+  // steps ahead may overwrite it) and the next stage has landed (so its
+  // first two sub-steps can be read while sub-steps 2 and 3 compute).  The
+  // last step is peeled off so that in the loop the operands read after the
+  // barrier are known to have arrived at its wait.  What sub-steps 2 and 3
+  // of step kt load into the stage they have just finished: step kt+2 of
+  // this tile, else step 0 of the next tile, else nothing (a descriptor with
+  // no records: the loads return zeros and touch no memory).
   const __amdgpu_buffer_rsrc_t tail_lr = has_next ? next_lr : no_lr;
   __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_s_barrier();
@@ -700,22 +707,26 @@ __device__ __forceinline__ void big_tile(const BigArgs& a, const BigCtx& c, cons
 #pragma unroll
   for (int r = 0; r < NR; ++r) read1(sb, 0, 0, r);
   __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int r = 0; r < NR; ++r) read1(sb, 1, 1, r);
+  __builtin_amdgcn_sched_barrier(0);
   for (int kt = 0; kt + 1 < nk; ++kt) {
     const int cur = (kt + sb) & 1;
-    substep(NoLoads{}, 0, cur, 1, 1, no_lr, 0, 0);
-    substep(NoLoads{}, 1, cur, 2, 0, no_lr, 0, 0);
-    substep(NoLoads{}, 0, cur, 3, 1, no_lr, 0, 0);
+    substep(NoLoads{}, 0, cur, 2, 2, no_lr, 0, 0, 0);
+    substep(NoLoads{}, 1, cur, 3, 3, no_lr, 0, 0, 0);
     __builtin_amdgcn_s_waitcnt(0);  // own loads of the next stage and own reads of this one
     __builtin_amdgcn_s_barrier();
     const bool more = kt + 2 < nk;
-    substep(Loads{}, 1, cur ^ 1, 0, 0, more ? t.lr : tail_lr, cur, more ? kt + 2 : 0);
+    const __amdgpu_buffer_rsrc_t llr = more ? t.lr : tail_lr;
+    substep(Loads{}, 2, cur ^ 1, 0, 0, llr, cur, more ? kt + 2 : 0, 0);
+    substep(Loads{}, 3, cur ^ 1, 1, 1, llr, cur, more ? kt + 2 : 0, 1);
   }
   {
     const int cur = (nk - 1 + sb) & 1;
-    substep(NoLoads{}, 0, cur, 1, 1, no_lr, 0, 0);
-    substep(NoLoads{}, 1, cur, 2, 0, no_lr, 0, 0);
-    substep(NoLoads{}, 0, cur, 3, 1, no_lr, 0, 0);
-    substep(NoLoads{}, 1, cur, -1, 0, no_lr, 0, 0);
+    substep(NoLoads{}, 0, cur, 2, 2, no_lr, 0, 0, 0);
+    substep(NoLoads{}, 1, cur, 3, 3, no_lr, 0, 0, 0);
+    substep(NoLoads{}, 2, cur, -1, 0, no_lr, 0, 0, 0);
+    substep(NoLoads{}, 3, cur, -1, 0, no_lr, 0, 0, 0);
   }
 
   // one compact loop over the accumulator blocks keeps the epilogue small
@@ -918,10 +929,10 @@ hipError_t launch_bf16_big(const GemmArgs& g, hipStream_t s) {
   a.Apre = static_cast<bf16*>(g.Apre);
   a.offset = g.offset;
   a.max_rows = g.max_rows;
-  a.tok_ld = g.K;
+  a.tok_ld = g.x_ld ? g.x_ld : g.K;
   a.feat_ld = g.K;
   a.feat_estride = (int64_t)g.N * g.K;
-  a.y_ld = g.N;
+  a.y_ld = g.y_ld ? g.y_ld : g.N;
   a.y_estride = 0;
   a.E = g.E;
   a.N = g.N;
@@ -1015,13 +1026,19 @@ hipError_t launch_router_partials(const uint16_t* dl_hl, const void* x, const in
   return launch_big<BE_F32, ACT_NONE, OP_TR, OP_TR, BM_WGRAD>(a, s);
 }
 
+// The large-tile kernel needs whole 64-wide K steps, whole 16-feature output
+// groups, and byte offsets of one operand tile below 2^31 (buffer offsets are
+// 32-bit).
+bool grouped_gemm_is_big(int64_t K, int64_t N, int dtype) {
+  return dtype == DT_BF16 && K > 0 && K % 64 == 0 && N % 16 == 0 && (int64_t)256 * (K + 64) * 2 < (int64_t(1) << 31);
+}
+
 hipError_t launch_grouped_gemm(const GemmArgs& a, int dtype, hipStream_t s) {
   if (a.max_rows <= 0) return hipSuccess;
-  // the large-tile kernel needs whole 64-wide K steps, whole 16-feature
-  // output groups, and byte offsets of one operand tile below 2^31 (buffer
-  // offsets are 32-bit)
-  if (dtype == DT_BF16 && a.K % 64 == 0 && a.N % 16 == 0 && (int64_t)256 * a.K * 2 < (int64_t(1) << 31))
-    return launch_bf16_big(a, s);
+  const bool pitched = (a.x_ld && a.x_ld != a.K) || (a.y_ld && a.y_ld != a.N);
+  if (pitched && (a.x_ld && a.x_ld < a.K || a.y_ld && a.y_ld < a.N || a.x_ld > a.K + 64)) return hipErrorInvalidValue;
+  if (grouped_gemm_is_big(a.K, a.N, dtype)) return launch_bf16_big(a, s);
+  if (pitched) return hipErrorNotSupported;
   if (dtype == DT_BF16) return launch_bf16<128, 128, 2, 2>(a, s);
   dim3 grid((a.N + 63) / 64, (unsigned)((a.max_rows + 3) / 4));
   hipLaunchKernelGGL(gemm_f32_kernel, grid, dim3(256), 0, s, a);

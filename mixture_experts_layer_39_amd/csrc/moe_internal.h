@@ -113,8 +113,12 @@ struct GemmArgs {
   const int32_t* offset;     // [E+1]
   int64_t max_rows;          // upper bound on offset[E] (sizes the grid)
   int32_t E, N, K, act;
+  int64_t x_ld = 0, y_ld = 0;  // row pitches of X and Y (and Apre) in elements; 0: K and N.
+                               // Other pitches only where grouped_gemm_is_big holds.
 };
 hipError_t launch_grouped_gemm(const GemmArgs& a, int dtype, hipStream_t s);
+// Whether launch_grouped_gemm runs this shape on the large-tile kernel.
+bool grouped_gemm_is_big(int64_t K, int64_t N, int dtype);
 
 // Backward pieces (see gemm_bwd.hip).
 struct GemmBwdArgs {

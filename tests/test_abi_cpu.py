@@ -215,15 +215,23 @@ def test_device_entry_points_validate_before_launch():
     assert L.moe_dispatch(c, FAKE, FAKE, None, FAKE, FAKE, None) == B.MOE_ERR_INVALID_ARG
     assert L.moe_combine(c, FAKE, FAKE, FAKE, None, FAKE, FAKE, None) == B.MOE_ERR_INVALID_ARG
     # single-Linear expert must not get w2
-    assert L.moe_expert_ffn(c, FAKE, FAKE, FAKE, None, FAKE, None, None, None, FAKE, None, 0, None) \
+    assert L.moe_expert_ffn(c, FAKE, FAKE, FAKE, None, FAKE, None, None, None, 0, FAKE, None, 0, None) \
         == B.MOE_ERR_INVALID_ARG
     cfg2 = _cfg(ffn_hidden=1024, activation=B.MOE_ACT_GELU)
     c2 = ctypes.byref(cfg2)
     # two-Linear expert needs w2 and h_disp
-    assert L.moe_expert_ffn(c2, FAKE, FAKE, FAKE, None, None, None, None, FAKE, FAKE, None, 0, None) \
+    assert L.moe_expert_ffn(c2, FAKE, FAKE, FAKE, None, None, None, None, FAKE, 0, FAKE, None, 0, None) \
         == B.MOE_ERR_INVALID_ARG
-    assert L.moe_expert_ffn(c2, FAKE, FAKE, FAKE, None, FAKE, None, None, None, FAKE, None, 0, None) \
+    assert L.moe_expert_ffn(c2, FAKE, FAKE, FAKE, None, FAKE, None, None, None, 0, FAKE, None, 0, None) \
         == B.MOE_ERR_INVALID_ARG
+    # h_disp's row pitch: h or h + 64 only
+    for bad in (1023, 1025, 1024 + 32, 1024 + 128, -1):
+        assert L.moe_expert_ffn(c2, FAKE, FAKE, FAKE, None, FAKE, None, None, FAKE, bad, FAKE, None, 0, None) \
+            == B.MOE_ERR_INVALID_ARG, bad
+    # a padded pitch needs the bf16 large-tile path (d and h multiples of 64)
+    cfg3 = _cfg(hidden_size=96, ffn_hidden=1024, activation=B.MOE_ACT_GELU)
+    assert L.moe_expert_ffn(ctypes.byref(cfg3), FAKE, FAKE, FAKE, None, FAKE, None, None, FAKE, 1088, FAKE, None, 0,
+                            None) == B.MOE_ERR_UNSUPPORTED
     # backward needs a hidden layer and every gradient output
     assert L.moe_expert_ffn_backward(c, *([FAKE] * 12), FAKE, 1 << 40, None) == B.MOE_ERR_INVALID_ARG
     assert L.moe_expert_ffn_backward(c2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, None,
@@ -328,6 +336,30 @@ def test_workspace_views_are_inside_workspace():
         assert p0 + s0 <= p1
     cfg.save_preact = 0
     assert B.moe_workspace_views(cfg, base)[1] is None
+
+
+def test_workspace_h_ld():
+    """The forward pads h_disp's rows to an odd number of 128-byte lines only
+    without save_preact and only on the bf16 large-tile path; the padded rows
+    fit in the h_disp region, before the next one."""
+    gelu = dict(ffn_hidden=1024, activation=B.MOE_ACT_GELU)
+    assert B.moe_workspace_h_ld(_cfg(**gelu)) == 1088                       # 16 lines -> 17
+    assert B.moe_workspace_h_ld(_cfg(save_preact=True, **gelu)) == 1024
+    assert B.moe_workspace_h_ld(_cfg(ffn_hidden=1088, activation=B.MOE_ACT_GELU)) == 1088   # 17 lines already
+    assert B.moe_workspace_h_ld(_cfg(dtype=B.MOE_F32, **gelu)) == 1024
+    assert B.moe_workspace_h_ld(_cfg(hidden_size=96, **gelu)) == 1024          # d not a multiple of 64
+    assert B.moe_workspace_h_ld(_cfg()) == 0
+    cfg = _cfg(**gelu)
+    n = B.moe_workspace_size(cfg)
+    base = 1 << 20
+    xd, _, h, y, _ = B.moe_workspace_views(cfg, base)
+    rows = B.moe_max_rows(cfg)
+    spans = sorted([(xd, rows * 512 * 2), (h, rows * 1088 * 2), (y, rows * 512 * 2)])
+    for (p0, s0), (p1, _) in zip(spans, spans[1:]):
+        assert p0 + s0 <= p1
+    assert spans[-1][0] + spans[-1][1] <= base + n
+    L = B.lib()
+    assert L.moe_workspace_h_ld(ctypes.byref(cfg), None) == B.MOE_ERR_INVALID_ARG
 
 
 def test_status_strings():

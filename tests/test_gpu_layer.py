@@ -110,6 +110,41 @@ def test_layer_parity_small(name, T):
     assert torch.equal(g2["offset"], off)
 
 
+@pytest.mark.parametrize("name,T", [("top2_e64", 1000), ("nodrop_e128", 700), ("skew_e16", 549)], ids=str)
+def test_layer_padded_intermediate(name, T):
+    """Without save_preact the forward keeps h_disp at a row pitch of h + 64
+    (an odd number of 128-byte lines for these h): same output bits as the
+    contiguous layout that save_preact uses, and the same intermediate."""
+    sp = spec(name, T=T, logits_given=True)
+    inp = with_given_logits(make_inputs(sp, DEV))
+    h = sp["h"]
+    assert h % 128 == 0
+    g0, out0, ws0, v0 = run_fused(sp, inp, cfg_of(sp, save_preact=0))
+    out0 = out0.clone()
+    g1, out1, ws1, v1 = run_fused(sp, inp, cfg_of(sp, save_preact=1))
+    torch.cuda.synchronize()
+    assert torch.equal(out0, out1)
+    assert torch.equal(g0["slot"], g1["slot"]) and torch.equal(g0["loss"], g1["loss"])
+    n = int(g1["count"].sum())
+    tdt = inp["x"].dtype
+    assert B.moe_workspace_h_ld(cfg_of(sp, save_preact=0)) == h + 64
+    padded = view(v0["h"], n, h + 64, tdt, ws0)[:, :h]
+    assert torch.equal(padded, view(v1["h"], n, h, tdt, ws1))
+    # the expert FFN entry point with the same pitch: the same bits
+    cfg = cfg_of(sp, save_preact=0)
+    rows = max(B.moe_max_rows(cfg), 1)
+    xd = view(v1["x_disp"], rows, sp["d"], tdt, ws1)
+    off = torch.empty(sp["E"] + 1, dtype=torch.int32, device=DEV)
+    off.copy_(view(v1["offset"], 1, sp["E"] + 1, torch.int32, ws1)[0])
+    hp = torch.full((rows, h + 64), 7.0, dtype=tdt, device=DEV)
+    yd = torch.empty(rows, sp["d"], dtype=tdt, device=DEV)
+    B.moe_expert_ffn(cfg, xd, off, inp["w1"], inp["b1"], inp["w2"], inp["b2"], None, hp, yd, h_ld=h + 64)
+    torch.cuda.synchronize()
+    assert torch.equal(hp[:n, :h], view(v1["h"], n, h, tdt, ws1))
+    assert torch.equal(yd[:n], view(v1["y"], n, sp["d"], tdt, ws1))
+    assert bool((hp[:, h:] == 7.0).all())    # the pad columns are not written
+
+
 def test_layer_is_deterministic():
     sp = spec("top2_e64", T=4000)
     inp = make_inputs(sp, DEV)
