@@ -37,13 +37,38 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
 
+# Kernels that must not use scratch memory.  decode_kernel separates its
+# phases with grid barriers, so every workgroup must be resident at once, and
+# scratch allocation can limit how many are; a variant of it that spilled to
+# scratch also computed its second Linear wrongly (with every barrier met).
+NO_SCRATCH = {"decode.hip": ("decode_kernel",)}
+
+
+def _scratch_sizes(remarks):
+    """Kernel name -> ScratchSize from hipcc's kernel-resource-usage remarks."""
+    sizes, name = {}, None
+    for line in remarks.splitlines():
+        if "Function Name:" in line:
+            name = line.split("Function Name:", 1)[1].split()[0]
+        elif name and "ScratchSize [bytes/lane]:" in line:
+            sizes[name] = int(line.split("ScratchSize [bytes/lane]:", 1)[1].split()[0])
+    return sizes
+
+
 def _compile(src):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc()] + FLAGS + ["-c", src, "-o", obj]
+    guarded = NO_SCRATCH.get(os.path.basename(src), ())
+    extra = ["-Rpass-analysis=kernel-resource-usage"] if guarded else []
+    cmd = [hipcc()] + FLAGS + extra + ["-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
-    msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in l)
+    out = r.stdout + r.stderr
+    msgs = "\n".join(l for l in out.splitlines() if "packed-fp32-ops" not in l and "remark:" not in l
+                     and not l.lstrip().startswith(("|", "^")) and l.strip())
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{msgs}")
+    for kern, size in _scratch_sizes(out).items():
+        if any(g in kern for g in guarded) and size > 0:
+            raise RuntimeError(f"{kern} in {src} uses {size} bytes of scratch per lane; it must use none")
     return obj, msgs
 
 

@@ -365,3 +365,18 @@ def test_workspace_h_ld():
 def test_status_strings():
     for s in range(5):
         assert B.status_string(s).startswith("MOE_")
+
+
+def test_build_scratch_guard_reads_resource_remarks():
+    """The build refuses a decode kernel that spills: its grid barriers need
+    every workgroup resident, which scratch allocation can prevent."""
+    from mixture_experts_layer_39_amd import build
+    remarks = ("x.hip:1:1: remark: Function Name: _ZN3moe12_GLOBAL__N_113decode_kernelENS_10DecodeArgsE [-Rpass]\n"
+               "x.hip:1:1: remark:     VGPRs: 172 [-Rpass]\n"
+               "x.hip:1:1: remark:     ScratchSize [bytes/lane]: 240 [-Rpass]\n"
+               "x.hip:9:1: remark: Function Name: _ZN3moe12_GLOBAL__N_118decode_init_kernelEPj [-Rpass]\n"
+               "x.hip:9:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass]\n")
+    sizes = build._scratch_sizes(remarks)
+    assert sizes == {"_ZN3moe12_GLOBAL__N_113decode_kernelENS_10DecodeArgsE": 240,
+                     "_ZN3moe12_GLOBAL__N_118decode_init_kernelEPj": 0}
+    assert build.NO_SCRATCH["decode.hip"] == ("decode_kernel",)

@@ -30,6 +30,9 @@ CASES = [
     (33, 128, 256, 1, 256, O.ACT_GELU, 1.0, 1, True, False, O.LOSS_BALANCE),
     (17, 384, 37, 2, 128, O.ACT_GELU, 2.0, 2, True, False, O.LOSS_BALANCE),
     (2, 128, 4, 1, 0, O.ACT_RELU, 1.0, 0, True, False, O.LOSS_USAGE_STD),
+    # up to 4 tokens every workgroup routes them all itself: more experts per lane, drops, both losses
+    (4, 256, 200, 2, 128, O.ACT_GELU, 1.0, 1, True, False, O.LOSS_BALANCE),
+    (3, 512, 96, 1, 256, O.ACT_RELU, 0.5, 1, True, True, O.LOSS_BALANCE),
 ]
 
 
