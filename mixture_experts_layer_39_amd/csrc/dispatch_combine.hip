@@ -28,6 +28,57 @@ __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u 
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 
 
+// The packed rows of token t's claims (-1 when dropped) and their weights.
+// Every index load of the token is issued before the first wait: slot,
+// expert and weight of each choice, then the kept claims' expert offsets, so
+// a token costs two memory latencies before its rows move instead of one per
+// dependent load.
+struct Claims {
+  int64_t r0, r1;
+  float w0, w1;
+};
+
+template <bool W>
+__device__ __forceinline__ Claims token_claims(const int32_t* __restrict__ expert_idx,
+                                               const int32_t* __restrict__ slot,
+                                               const float* __restrict__ weight,
+                                               const int32_t* __restrict__ offset, int64_t t, int k) {
+  const int s0 = slot[t * k], e0 = expert_idx[t * k];
+  const int s1 = k == 2 ? slot[t * k + 1] : -1, e1 = k == 2 ? expert_idx[t * k + 1] : 0;
+  Claims c;
+  c.w0 = W ? weight[t * k] : 0.f;
+  c.w1 = (W && k == 2) ? weight[t * k + 1] : 0.f;
+  c.r0 = s0 >= 0 ? (int64_t)offset[e0] + s0 : -1;
+  c.r1 = s1 >= 0 ? (int64_t)offset[e1] + s1 : -1;
+  return c;
+}
+
+// Each lane moves up to kUnroll 16-byte vectors of a row per pass, all
+// loads of a pass issued before the first use.
+constexpr int kUnroll = 4;
+
+// One token row to ND packed rows, kUnroll vectors per lane and pass.
+template <int ND>
+__device__ __forceinline__ void copy_row(const u32x4* __restrict__ src, u32x4* __restrict__ d0,
+                                         u32x4* __restrict__ d1, int lane, int nvec) {
+  int v0 = lane;
+  for (; v0 + (kUnroll - 1) * 64 < nvec; v0 += kUnroll * 64) {
+    u32x4 val[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) val[u] = __builtin_nontemporal_load(src + v0 + u * 64);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      d0[v0 + u * 64] = val[u];
+      if constexpr (ND == 2) d1[v0 + u * 64] = val[u];
+    }
+  }
+  for (; v0 < nvec; v0 += 64) {
+    const u32x4 val = __builtin_nontemporal_load(src + v0);
+    d0[v0] = val;
+    if constexpr (ND == 2) d1[v0] = val;
+  }
+}
+
 __global__ __launch_bounds__(256) void dispatch_kernel(const u32x4* __restrict__ x,
                                                        const int32_t* __restrict__ expert_idx,
                                                        const int32_t* __restrict__ slot,
@@ -38,22 +89,13 @@ __global__ __launch_bounds__(256) void dispatch_kernel(const u32x4* __restrict__
   const int64_t wave_id = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
   for (int64_t t = wave_id; t < T; t += nwaves) {
-    int64_t r0 = -1, r1 = -1;
-    {
-      const int s0 = slot[t * k];
-      if (s0 >= 0) r0 = (int64_t)offset[expert_idx[t * k]] + s0;
-      if (k == 2) {
-        const int s1 = slot[t * k + 1];
-        if (s1 >= 0) r1 = (int64_t)offset[expert_idx[t * k + 1]] + s1;
-      }
-    }
-    if (r0 < 0 && r1 < 0) continue;
+    const Claims c = token_claims<false>(expert_idx, slot, nullptr, offset, t, k);
+    if (c.r0 < 0 && c.r1 < 0) continue;
     const u32x4* src = x + t * nvec;
-    for (int v = lane; v < nvec; v += 64) {
-      const u32x4 val = __builtin_nontemporal_load(src + v);
-      if (r0 >= 0) x_disp[r0 * nvec + v] = val;
-      if (r1 >= 0) x_disp[r1 * nvec + v] = val;
-    }
+    // one branch per token, outside the copy, so that the stores of a pass
+    // issue back to back
+    if (c.r0 >= 0 && c.r1 >= 0) copy_row<2>(src, x_disp + c.r0 * nvec, x_disp + c.r1 * nvec, lane, nvec);
+    else copy_row<1>(src, x_disp + (c.r0 >= 0 ? c.r0 : c.r1) * nvec, nullptr, lane, nvec);
   }
 }
 
@@ -68,69 +110,54 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ 
   const int lane = threadIdx.x & 63;
   const int64_t wave_id = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
   for (int64_t t = wave_id; t < T; t += nwaves) {
-    int64_t r0 = -1, r1 = -1;
-    float w0 = 0.f, w1 = 0.f;
-    {
-      const int s0 = slot[t * k];
-      if (s0 >= 0) {
-        r0 = (int64_t)offset[expert_idx[t * k]] + s0;
-        w0 = weight[t * k];
-      }
-      if (k == 2) {
-        const int s1 = slot[t * k + 1];
-        if (s1 >= 0) {
-          r1 = (int64_t)offset[expert_idx[t * k + 1]] + s1;
-          w1 = weight[t * k + 1];
-        }
-      }
-    }
+    const Claims c = token_claims<true>(expert_idx, slot, weight, offset, t, k);
     u32x4* dst = out + t * nvec;
-    for (int v = lane; v < nvec; v += 64) {
-      if constexpr (DT == DT_BF16) {
-        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        if (r0 >= 0) {
-          const u32x4 a = __builtin_nontemporal_load(y + r0 * nvec + v);
-          const uint32_t u[4] = {a.x, a.y, a.z, a.w};
+    for (int v0 = lane; v0 < nvec; v0 += kUnroll * 64) {
+      u32x4 a[kUnroll], b[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int v = v0 + u * 64;
+        a[u] = (v < nvec && c.r0 >= 0) ? __builtin_nontemporal_load(y + c.r0 * nvec + v) : zero;
+        b[u] = (v < nvec && c.r1 >= 0) ? __builtin_nontemporal_load(y + c.r1 * nvec + v) : zero;
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int v = v0 + u * 64;
+        if (v >= nvec) continue;
+        // fp32 sum in choice order; a dropped claim adds nothing
+        if constexpr (DT == DT_BF16) {
+          const uint32_t ua[4] = {a[u].x, a[u].y, a[u].z, a[u].w};
+          const uint32_t ub[4] = {b[u].x, b[u].y, b[u].z, b[u].w};
+          float acc[8];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            acc[2 * i] = w0 * bf16_lo(u[i]);
-            acc[2 * i + 1] = w0 * bf16_hi(u[i]);
+            acc[2 * i] = c.r0 >= 0 ? c.w0 * bf16_lo(ua[i]) : 0.f;
+            acc[2 * i + 1] = c.r0 >= 0 ? c.w0 * bf16_hi(ua[i]) : 0.f;
+            if (c.r1 >= 0) {
+              acc[2 * i] = fmaf(c.w1, bf16_lo(ub[i]), acc[2 * i]);
+              acc[2 * i + 1] = fmaf(c.w1, bf16_hi(ub[i]), acc[2 * i + 1]);
+            }
           }
-        }
-        if (r1 >= 0) {
-          const u32x4 b = __builtin_nontemporal_load(y + r1 * nvec + v);
-          const uint32_t u[4] = {b.x, b.y, b.z, b.w};
+          u32x4 o;
+          o.x = pack_bf16x2(acc[0], acc[1]);
+          o.y = pack_bf16x2(acc[2], acc[3]);
+          o.z = pack_bf16x2(acc[4], acc[5]);
+          o.w = pack_bf16x2(acc[6], acc[7]);
+          dst[v] = o;
+        } else {
+          const uint32_t ua[4] = {a[u].x, a[u].y, a[u].z, a[u].w};
+          const uint32_t ub[4] = {b[u].x, b[u].y, b[u].z, b[u].w};
+          float acc[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            acc[2 * i] = fmaf(w1, bf16_lo(u[i]), acc[2 * i]);
-            acc[2 * i + 1] = fmaf(w1, bf16_hi(u[i]), acc[2 * i + 1]);
+            acc[i] = c.r0 >= 0 ? c.w0 * __uint_as_float(ua[i]) : 0.f;
+            if (c.r1 >= 0) acc[i] = fmaf(c.w1, __uint_as_float(ub[i]), acc[i]);
           }
+          dst[v] = u32x4{__float_as_uint(acc[0]), __float_as_uint(acc[1]), __float_as_uint(acc[2]),
+                         __float_as_uint(acc[3])};
         }
-        u32x4 o;
-        o.x = pack_bf16x2(acc[0], acc[1]);
-        o.y = pack_bf16x2(acc[2], acc[3]);
-        o.z = pack_bf16x2(acc[4], acc[5]);
-        o.w = pack_bf16x2(acc[6], acc[7]);
-        dst[v] = o;
-      } else {
-        float acc[4] = {0.f, 0.f, 0.f, 0.f};
-        if (r0 >= 0) {
-          const u32x4 a = y[r0 * nvec + v];
-          acc[0] = w0 * __uint_as_float(a.x);
-          acc[1] = w0 * __uint_as_float(a.y);
-          acc[2] = w0 * __uint_as_float(a.z);
-          acc[3] = w0 * __uint_as_float(a.w);
-        }
-        if (r1 >= 0) {
-          const u32x4 b = y[r1 * nvec + v];
-          acc[0] = fmaf(w1, __uint_as_float(b.x), acc[0]);
-          acc[1] = fmaf(w1, __uint_as_float(b.y), acc[1]);
-          acc[2] = fmaf(w1, __uint_as_float(b.z), acc[2]);
-          acc[3] = fmaf(w1, __uint_as_float(b.w), acc[3]);
-        }
-        dst[v] = u32x4{__float_as_uint(acc[0]), __float_as_uint(acc[1]), __float_as_uint(acc[2]),
-                       __float_as_uint(acc[3])};
       }
     }
   }
