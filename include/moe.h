@@ -227,7 +227,9 @@ moe_status moe_expert_ffn(const moe_config* cfg, const void* x_disp, const int32
  * Needs ffn_hidden > 0; MOE_ERR_UNSUPPORTED unless dtype is MOE_BF16 and d
  * and h are multiples of 16.  dx_disp device [rows, d] bf16; dw1 [E, h, d]
  * and dw2 [E, d, h] bf16 (fp32 accumulation; experts with no rows get
- * zeros); db1 [E, h], db2 [E, d] fp32.  ws as above (it also holds dA). */
+ * zeros); db1 [E, h], db2 [E, d] fp32.  ws as above (it also holds dA).
+ * a_save and h_disp are read with contiguous rows (pitch h), as the forward
+ * writes them with h_ld = 0 or with cfg->save_preact. */
 moe_status moe_expert_ffn_backward(const moe_config* cfg, const void* x_disp,
                                    const int32_t* expert_offset, const void* w1, const void* w2,
                                    const void* a_save, const void* h_disp, const void* dy_disp,
