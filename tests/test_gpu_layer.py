@@ -137,12 +137,14 @@ def test_layer_padded_intermediate(name, T):
     off = torch.empty(sp["E"] + 1, dtype=torch.int32, device=DEV)
     off.copy_(view(v1["offset"], 1, sp["E"] + 1, torch.int32, ws1)[0])
     hp = torch.full((rows, h + 64), 7.0, dtype=tdt, device=DEV)
+    ap = torch.full((rows, h + 64), 7.0, dtype=tdt, device=DEV)
     yd = torch.empty(rows, sp["d"], dtype=tdt, device=DEV)
-    B.moe_expert_ffn(cfg, xd, off, inp["w1"], inp["b1"], inp["w2"], inp["b2"], None, hp, yd, h_ld=h + 64)
+    B.moe_expert_ffn(cfg, xd, off, inp["w1"], inp["b1"], inp["w2"], inp["b2"], ap, hp, yd, h_ld=h + 64)
     torch.cuda.synchronize()
     assert torch.equal(hp[:n, :h], view(v1["h"], n, h, tdt, ws1))
+    assert torch.equal(ap[:n, :h], view(v1["a"], n, h, tdt, ws1))   # a_save at the same pitch
     assert torch.equal(yd[:n], view(v1["y"], n, sp["d"], tdt, ws1))
-    assert bool((hp[:, h:] == 7.0).all())    # the pad columns are not written
+    assert bool((hp[:, h:] == 7.0).all()) and bool((ap[:, h:] == 7.0).all())   # pad columns not written
 
 
 def test_layer_is_deterministic():
