@@ -104,22 +104,14 @@ __global__ __launch_bounds__(256) void combine_backward_kernel(const u32x4* __re
   const int64_t wave_id = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * kWaves;
   for (int64_t t = wave_id; t < T; t += nwaves) {
-    int64_t r0 = -1, r1 = -1;
-    float w0 = 0.f, w1 = 0.f;
-    {
-      const int s0 = slot[t * k];
-      if (s0 >= 0) {
-        r0 = (int64_t)offset[expert_idx[t * k]] + s0;
-        w0 = weight[t * k];
-      }
-      if (k == 2) {
-        const int s1 = slot[t * k + 1];
-        if (s1 >= 0) {
-          r1 = (int64_t)offset[expert_idx[t * k + 1]] + s1;
-          w1 = weight[t * k + 1];
-        }
-      }
-    }
+    // every index load of the token before the first wait: slot, expert and
+    // weight of each choice, then the kept claims' offsets
+    const int s0 = slot[t * k], e0 = expert_idx[t * k];
+    const int s1 = k == 2 ? slot[t * k + 1] : -1, e1 = k == 2 ? expert_idx[t * k + 1] : 0;
+    const float wt0 = weight[t * k], wt1 = k == 2 ? weight[t * k + 1] : 0.f;
+    const int64_t r0 = s0 >= 0 ? (int64_t)offset[e0] + s0 : -1;
+    const int64_t r1 = s1 >= 0 ? (int64_t)offset[e1] + s1 : -1;
+    const float w0 = r0 >= 0 ? wt0 : 0.f, w1 = r1 >= 0 ? wt1 : 0.f;
     float dot0 = 0.f, dot1 = 0.f;
     if (r0 >= 0 || r1 >= 0) {
       const u32x4* src = dout + t * nvec;
