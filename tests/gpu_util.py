@@ -76,16 +76,22 @@ def gate_np(g):
                 count=i64(g["count"]), offset=i64(g["offset"]), loss=float(g["loss"][0].item()))
 
 
-def close(got, want, rtol):
+def close(got, want, rtol, scale=None):
     """Elementwise |g - o| <= rtol*|o| + rtol*rms(o): relative error with a
-    floor at the tensor's rms so near-zero entries are not over-weighted."""
+    floor at the tensor's rms so near-zero entries are not over-weighted.
+
+    ``scale`` (>= |o| elementwise) replaces |o| in the relative term for a
+    value formed as a difference of larger terms: it is the sum of those
+    terms' magnitudes, to which a relative error of the inputs applies
+    before the cancellation."""
     got = np.asarray(got, np.float64)
     want = np.asarray(want, np.float64)
     assert got.shape == want.shape, (got.shape, want.shape)
     if want.size == 0:
         return
     rms = float(np.sqrt(np.mean(want * want)))
-    bound = rtol * np.abs(want) + rtol * rms
+    rel = np.abs(want) if scale is None else np.maximum(np.abs(want), np.asarray(scale, np.float64))
+    bound = rtol * rel + rtol * rms
     err = np.abs(got - want)
     bad = err > bound
     if bad.any():

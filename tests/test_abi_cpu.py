@@ -362,6 +362,21 @@ def test_workspace_h_ld():
     assert L.moe_workspace_h_ld(ctypes.byref(cfg), None) == B.MOE_ERR_INVALID_ARG
 
 
+def test_workspace_status_word():
+    """The small-batch status word lies inside the workspace (4-byte aligned)
+    for batches the one-launch path takes, and there is none past them."""
+    for T in (1, 64, 256):
+        cfg = _cfg(num_tokens=T, ffn_hidden=1024, activation=B.MOE_ACT_GELU)
+        n = B.moe_workspace_size(cfg)
+        base = 1 << 20
+        p = B.moe_workspace_status(cfg, base)
+        assert base <= p and p + 4 <= base + n and p % 4 == 0
+    assert B.moe_workspace_status(_cfg(num_tokens=257), 1 << 20) is None
+    L = B.lib()
+    cfg = _cfg(num_tokens=8)
+    assert L.moe_workspace_status(ctypes.byref(cfg), None, None) == B.MOE_ERR_INVALID_ARG
+
+
 def test_status_strings():
     for s in range(5):
         assert B.status_string(s).startswith("MOE_")

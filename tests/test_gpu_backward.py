@@ -95,57 +95,71 @@ def test_backward_is_deterministic():
         assert torch.equal(g1[key], g2[key]), key
 
 
-def test_backward_full_size_sampled():
-    """The no-drop workload at full size: sampled rows of dX, sampled entries
-    of dW1 and dW2, each computed one by one by the oracle's formulas."""
+@pytest.mark.timeout(900)
+def test_backward_full_size():
+    """The no-drop workload at full size (T=65536, d=4096, E=128, h=1536):
+    every element of dX, dW1, dW2, db1 and db2 against the oracle's whole
+    forward and expert backward."""
     sp = spec("nodrop_e128", logits_given=True)
     inp = make_inputs(sp, DEV)
     cfg, g, gr = forward_backward(sp, inp)
-    T, d, h, E = sp["T"], sp["d"], sp["h"], sp["E"]
-    logits = f64(inp["logits"])
-    r = O.route(logits, 2, 1.0, 0, False)
+    x, w1, b1, w2, b2 = f64(inp["x"]), experts(inp["w1"]), experts(inp["b1"]), experts(inp["w2"]), experts(inp["b2"])
+    r = O.layer_forward(x, f64(inp["logits"]), w1, b1, w2, b2, k=2, capacity_factor=1.0, min_capacity=0,
+                        drop_tokens=False, act=O.ACT_GELU, dtype="bf16")
     np.testing.assert_array_equal(i64(g["slot"]), r["slot"])
-    off = r["expert_offset"]
-    # the packed row -> token map from the (bit-exact) routing
-    tok = np.empty(int(off[-1]), np.int64)
-    for t in range(T):
-        for j in range(2):
-            tok[off[r["expert_idx"][t, j]] + r["slot"][t, j]] = t
-    rng = np.random.default_rng(5)
-    w1, w2, b1 = experts(inp["w1"]), experts(inp["w2"]), experts(inp["b1"])
-    x_rows = lambda rows: f64(inp["x"][torch.from_numpy(tok[rows]).to(DEV)])
-    dy_rows = lambda rows: f64(inp["dy"][torch.from_numpy(np.asarray(rows)).to(DEV)])
+    np.testing.assert_array_equal(i64(g["count"]), r["expert_count"])
+    del x
+    dx, dw1, db1, dw2, db2 = O.expert_ffn_backward(r["x_disp"], r["expert_offset"], w1, w2, r["a"], r["h"],
+                                                   f64(inp["dy"]), O.ACT_GELU, "bf16")
+    r.clear()
+    close(f64(gr["dx"]), dx, 2e-2)
+    del dx
+    close(f64(gr["dw1"]), dw1, 2e-2)
+    del dw1
+    close(f64(gr["dw2"]), dw2, 2e-2)
+    del dw2
+    close(f64(gr["db1"]), db1, 2e-2)
+    close(f64(gr["db2"]), db2, 2e-2)
 
-    def expert_of(row):
-        return int(np.searchsorted(off, row, side="right") - 1)
 
-    def dA_rows(rows, e):
-        X = x_rows(rows)
-        a = O.store(X @ np.asarray(w1[e], np.float64).T + np.asarray(b1[e], np.float64), "bf16")
-        dH = dy_rows(rows) @ np.asarray(w2[e], np.float64)
-        return O.store(dH * O.gelu_grad(a), "bf16"), a
+# Shapes the large-tile backward does not take (d or h a multiple of 16 but
+# not of 64): the four backward GEMMs then run on the 128 x 128 fallback
+# kernel (dA with act', dW2, dX, dW1), the bias gradients on the column sums.
+FALLBACK = [  # E, T, d, h, cf, drop, empty expert
+    (5, 400, 96, 176, 0.8, True, 2),
+    (4, 300, 128, 80, 1.0, False, None),
+    (3, 260, 80, 128, 1.0, False, 1),
+    (6, 517, 208, 112, 0.9, True, None),
+]
 
-    # dX on sampled rows
-    rows = rng.choice(int(off[-1]), 24, replace=False)
-    got = f64(gr["dx"][torch.from_numpy(rows).to(DEV)])
-    want = []
-    for row in rows:
-        e = expert_of(row)
-        dA, _ = dA_rows([row], e)
-        want.append(O.store(dA[0] @ np.asarray(w1[e], np.float64), "bf16"))
-    close(got, np.stack(want), 2e-2)
-    # dW2 and dW1 entries of sampled experts, over all of each expert's rows
-    for e in rng.choice(E, 3, replace=False):
-        rs = np.arange(off[e], off[e + 1])
-        dA, a = dA_rows(rs, e)
-        H = O.store(O.gelu(a), "bf16")
-        dY = dy_rows(rs)
-        X = x_rows(rs)
-        ii = rng.integers(0, d, 40)
-        jj = rng.integers(0, h, 40)
-        got2 = f64(gr["dw2"][int(e)])[ii, jj]
-        close(got2, O.store(np.einsum("mi,mi->i", dY[:, ii], H[:, jj]), "bf16"), 2e-2)
-        kk = rng.integers(0, h, 40)
-        ll = rng.integers(0, d, 40)
-        got1 = f64(gr["dw1"][int(e)])[kk, ll]
-        close(got1, O.store(np.einsum("mi,mi->i", dA[:, kk], X[:, ll]), "bf16"), 2e-2)
+
+@pytest.mark.parametrize("E,T,d,h,cf,drop,empty", FALLBACK)
+def test_backward_fallback_shapes(E, T, d, h, cf, drop, empty):
+    assert d % 64 or h % 64   # not a large-tile shape
+    sp = spec("nodrop_e128", T=T, E=E, d=d, h=h, cf=cf, min_cap=1, drop=drop, logits_given=True,
+              seed=900 + E + d + h)
+    inp = make_inputs(sp, DEV)
+    L = inp["logits"].clone()
+    if empty is not None:
+        L[:, empty] -= 100.0   # never chosen: zero weight and bias gradients
+    cfg, g, gr = forward_backward(sp, inp, logits_in=L)
+    x, w1, b1, w2, b2 = f64(inp["x"]), experts(inp["w1"]), experts(inp["b1"]), experts(inp["w2"]), experts(inp["b2"])
+    r = O.layer_forward(x, f64(L), w1, b1, w2, b2, k=2, capacity_factor=cf, min_capacity=1, drop_tokens=drop,
+                        act=O.ACT_GELU, dtype="bf16")
+    np.testing.assert_array_equal(i64(g["slot"]), r["slot"])
+    np.testing.assert_array_equal(i64(g["count"]), r["expert_count"])
+    if drop:
+        assert (r["slot"] < 0).any()
+    if empty is not None:
+        assert r["expert_count"][empty] == 0
+    n = int(r["expert_offset"][-1])
+    dx, dw1, db1, dw2, db2 = O.expert_ffn_backward(r["x_disp"], r["expert_offset"], w1, w2, r["a"], r["h"],
+                                                   f64(inp["dy"])[:n], O.ACT_GELU, "bf16")
+    close(f64(gr["dx"])[:n], dx, 2e-2)
+    close(f64(gr["dw1"]), dw1, 2e-2)
+    close(f64(gr["dw2"]), dw2, 2e-2)
+    close(f64(gr["db1"]), db1, 2e-2)
+    close(f64(gr["db2"]), db2, 2e-2)
+    if empty is not None:
+        for t in (gr["dw1"][empty], gr["dw2"][empty], gr["db1"][empty], gr["db2"][empty]):
+            assert not t.float().abs().sum().item()

@@ -30,7 +30,7 @@ CASES = [
     (33, 128, 256, 1, 256, O.ACT_GELU, 1.0, 1, True, False, O.LOSS_BALANCE),
     (17, 384, 37, 2, 128, O.ACT_GELU, 2.0, 2, True, False, O.LOSS_BALANCE),
     (2, 128, 4, 1, 0, O.ACT_RELU, 1.0, 0, True, False, O.LOSS_USAGE_STD),
-    # up to 4 tokens every workgroup routes them all itself: more experts per lane, drops, both losses
+    # a few tokens with many experts (up to four 64-expert groups per lane), drops, both losses
     (4, 256, 200, 2, 128, O.ACT_GELU, 1.0, 1, True, False, O.LOSS_BALANCE),
     (3, 512, 96, 1, 256, O.ACT_RELU, 0.5, 1, True, True, O.LOSS_BALANCE),
 ]
@@ -60,6 +60,11 @@ def _forward(cfg, inp, T, d, E, given=True, ws=None):
                         logits_out=gate["logits"], expert_idx=gate["idx"], slot=gate["slot"], weight=gate["weight"],
                         ws=ws)
     torch.cuda.synchronize()
+    st = B.moe_workspace_status(cfg, ws)
+    one_launch = cfg.small_batch == 1 or (cfg.small_batch == 0 and T <= B.MOE_SMALL_BATCH_AUTO)
+    if st is not None and one_launch:
+        # every grid barrier of the one-launch kernel completed (all cases here fit that kernel)
+        assert int(ws[st - ws.data_ptr():st - ws.data_ptr() + 4].view(torch.int32)[0]) == 0
     return gate, out, ws
 
 
