@@ -415,6 +415,16 @@ moe_status moe_workspace_views(const moe_config* cfg, void* ws, void** x_disp, v
  * MOE_ERR_INVALID_ARG for an invalid cfg or a NULL h_ld. */
 moe_status moe_workspace_h_ld(const moe_config* cfg, int64_t* h_ld);
 
+/* Device address, inside a workspace ws, of the status word of the
+ * one-launch small-batch forward (see moe_layer_forward): a uint32 that the
+ * launch zeroes first and sets to 1 if one of its grid barriers stopped
+ * waiting (its other outputs are then undefined, and *gate_loss is NaN).
+ * It holds the last small-batch launch's status until the next one on ws;
+ * the caller reads it after synchronising the stream.  *status = NULL when
+ * cfg->num_tokens exceeds MOE_SMALL_BATCH_MAX (no such launch for cfg).
+ * Host only; computes an address, reads nothing. */
+moe_status moe_workspace_status(const moe_config* cfg, void* ws, uint32_t** status);
+
 #ifdef __cplusplus
 }
 #endif

@@ -20,12 +20,13 @@ MOE_ACT_NONE, MOE_ACT_RELU, MOE_ACT_GELU = 0, 1, 2
 MOE_LOSS_BALANCE, MOE_LOSS_USAGE_STD = 0, 1
 MOE_NOISE_NONE, MOE_NOISE_JITTER, MOE_NOISE_RSAMPLE = 0, 1, 2
 MOE_MAX_EXPERTS = 256
+MOE_SMALL_BATCH_MAX, MOE_SMALL_BATCH_AUTO = 256, 64
 
 EXPORTED = ("moe_status_string", "moe_capacity", "moe_max_rows", "moe_workspace_size", "moe_gate",
             "moe_dispatch", "moe_expert_ffn", "moe_expert_ffn_backward", "moe_combine",
             "moe_layer_forward", "moe_workspace_views", "moe_combine_backward", "moe_gate_backward",
             "moe_dispatch_backward", "moe_router_backward", "moe_layer_backward", "moe_residual_layer_forward",
-            "moe_residual_layer_backward", "moe_workspace_h_ld")
+            "moe_residual_layer_backward", "moe_workspace_h_ld", "moe_workspace_status")
 
 
 class MoeConfig(ctypes.Structure):
@@ -94,6 +95,7 @@ def lib():
         L.moe_layer_forward.argtypes = [CFG] + [P] * 15 + [P, S, P]
         L.moe_workspace_views.argtypes = [CFG, P] + [ctypes.POINTER(P)] * 5
         L.moe_workspace_h_ld.argtypes = [CFG, ctypes.POINTER(ctypes.c_int64)]
+        L.moe_workspace_status.argtypes = [CFG, P, ctypes.POINTER(P)]
         L.moe_combine_backward.argtypes = [CFG] + [P] * 8 + [P]
         L.moe_gate_backward.argtypes = [CFG] + [P] * 5 + [P, S, P]
         L.moe_dispatch_backward.argtypes = [CFG] + [P] * 7 + [P, S, P]
@@ -165,6 +167,14 @@ def moe_workspace_views(cfg, ws):
     outs = [ctypes.c_void_p() for _ in range(5)]
     _check(lib().moe_workspace_views(ctypes.byref(cfg), _ptr(ws), *[ctypes.byref(o) for o in outs]))
     return tuple(o.value for o in outs)
+
+
+def moe_workspace_status(cfg, ws):
+    """Device address of the small-batch forward's status word in ws (None
+    when cfg's batch is too large for that path)."""
+    out = ctypes.c_void_p()
+    _check(lib().moe_workspace_status(ctypes.byref(cfg), _ptr(ws), ctypes.byref(out)))
+    return out.value
 
 
 # ---------------------------------------------------------------- device calls

@@ -125,20 +125,34 @@ __device__ __forceinline__ float act_rt(float v, int act) {
 // workgroup is resident and every wait ends.  The spin is bounded all the
 // same: a wait that gives up records it in the status word and returns
 // false, and the workgroup then stops (its reads would see data that was
-// never written) after setting gate_loss to NaN, the signal the caller sees.
+// never written) after setting gate_loss to NaN and the status word (which
+// the host can read through moe_workspace_status) to 1.
+//
+// Publishing: every wavefront releases its own stores at agent scope before
+// the workgroup barrier.  A workgroup barrier orders the waves' execution but
+// does not wait for their outstanding global stores (on gfx950 __syncthreads
+// compiles to a bare s_barrier), and a release fence waits only for the
+// issuing wave's own memory operations before it writes this XCD's L2 back.
+// A release by thread 0 alone therefore does not cover a store of another
+// wave that is still on its way to the L2 when the write-back runs, and a
+// workgroup on another XCD (own L2) can then read the old value.  Stores by
+// several waves that other workgroups read after a barrier happen here in
+// the routing phase (a wave per token) and in the row copy.
 constexpr int kBarGroups = 16, kBarLine = 32;   // 32 words = 128 bytes
 constexpr int kBarTop = kBarGroups * kBarLine, kBarStatus = kBarTop + kBarLine;
 constexpr int kBarWords = kBarStatus + 1;
+static_assert(kBarStatus == kDecodeStatusWord, "status word index");
 
 __device__ __forceinline__ bool grid_barrier(unsigned* bar, unsigned phase, int* ok) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");   // each wave: its stores reach memory
   __syncthreads();
   if (threadIdx.x == 0) {
     const unsigned nwg = gridDim.x;
     const unsigned g = blockIdx.x % kBarGroups;
     const unsigned groups = nwg < (unsigned)kBarGroups ? nwg : (unsigned)kBarGroups;
     const unsigned gsize = (nwg - g + kBarGroups - 1) / kBarGroups;   // workgroups in group g
-    // one release (this workgroup's writes reach memory before it arrives),
-    // relaxed arrivals and polls (an acquire per poll would invalidate the
+    // the release that pairs with the arrival (the waves' own releases above
+    // made every store of the workgroup visible), relaxed arrivals and polls (an acquire per poll would invalidate the
     // XCD's L2 on every read), then one acquire
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     const unsigned old = __hip_atomic_fetch_add(&bar[g * kBarLine], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -343,6 +343,15 @@ moe_status moe_workspace_views(const moe_config* cfg, void* ws, void** x_disp, v
   return MOE_OK;
 }
 
+moe_status moe_workspace_status(const moe_config* cfg, void* ws, uint32_t** status) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (!ws || !status) return MOE_ERR_INVALID_ARG;
+  const Layout L = layout_of(cfg);
+  *status = cfg->num_tokens <= kDecodeMaxTokens ? at<uint32_t>(ws, L.dec_bar) + kDecodeStatusWord : nullptr;
+  return MOE_OK;
+}
+
 moe_status moe_gate(const moe_config* cfg, const void* x, const void* w_router, const float* b_router,
                     const float* logits_in, float* logits_out, int32_t* expert_idx, int32_t* slot,
                     float* weight, int32_t* expert_count, int32_t* expert_offset, float* gate_loss, void* ws,

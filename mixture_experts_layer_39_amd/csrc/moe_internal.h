@@ -275,6 +275,10 @@ hipError_t launch_coef_wgrad(const ResidualArgs& a, hipStream_t s);
 // tokens (bf16, d and h multiples of 128, inference: no pre-activation kept).
 constexpr int kDecodeMaxTokens = 256;
 constexpr int kDecodeMaxSlices = 16;
+// Index (32-bit words) of the status word in the small-batch kernel's barrier
+// region: 0 after a launch whose grid barriers all completed, 1 if a wait ran
+// out.
+constexpr int kDecodeStatusWord = 16 * 32 + 32;
 struct DecodeArgs {
   const bf16* x;            // [T, d]
   const bf16* w_router;     // [E, d] (unused with logits_in)
