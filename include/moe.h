@@ -190,6 +190,24 @@ moe_status moe_gate(const moe_config* cfg, const void* x, const void* w_router,
                     int32_t* expert_count, int32_t* expert_offset, float* gate_loss,
                     void* ws, size_t ws_bytes, void* stream);
 
+/* The gate of moe_gate without a workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  Same arguments, kernels and
+ * results as moe_gate; the gate's scratch (per-tile counts and probability
+ * sums, about T/64 * E * (4k + 4) bytes) lives in a library-owned device
+ * array of MOE_GATE_NOALLOC_SCRATCH_BYTES per GPU, held until the process
+ * ends.  MOE_ERR_WORKSPACE when cfg needs more than that (with E = 256,
+ * k = 2: beyond about T = 174000 tokens).  Nothing is allocated or freed.  Every
+ * call on one GPU shares that GPU's array: calls that overlap on one GPU
+ * (concurrent streams, or host threads) race and must be serialised by
+ * the caller (one stream, or events). */
+#define MOE_GATE_NOALLOC_SCRATCH_BYTES (8u << 20)
+moe_status moe_gate_noalloc(const moe_config* cfg, const void* x, const void* w_router,
+                            const float* b_router, const float* logits_in, float* logits_out,
+                            int32_t* expert_idx, int32_t* slot, float* weight,
+                            int32_t* expert_count, int32_t* expert_offset, float* gate_loss,
+                            void* stream);
+
 /* Dispatch ([MoE-sched] §3.1 Step 3; [ds.moe] §3.1 step 2 on one GPU):
  * for every kept claim (t, j): x_disp[expert_offset[e] + slot[t,j]] = x[t],
  * e = expert_idx[t,j].  x_disp is the packed expert-major buffer, device,

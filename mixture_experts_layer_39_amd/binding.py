@@ -26,7 +26,7 @@ EXPORTED = ("moe_status_string", "moe_capacity", "moe_max_rows", "moe_workspace_
             "moe_dispatch", "moe_expert_ffn", "moe_expert_ffn_backward", "moe_combine",
             "moe_layer_forward", "moe_workspace_views", "moe_combine_backward", "moe_gate_backward",
             "moe_dispatch_backward", "moe_router_backward", "moe_layer_backward", "moe_residual_layer_forward",
-            "moe_residual_layer_backward", "moe_workspace_h_ld", "moe_workspace_status")
+            "moe_residual_layer_backward", "moe_workspace_h_ld", "moe_workspace_status", "moe_gate_noalloc")
 
 
 class MoeConfig(ctypes.Structure):
@@ -88,6 +88,7 @@ def lib():
             getattr(L, name).argtypes = [CFG, I64P]
         L.moe_workspace_size.argtypes = [CFG, ctypes.POINTER(ctypes.c_size_t)]
         L.moe_gate.argtypes = [CFG] + [P] * 11 + [P, S, P]
+        L.moe_gate_noalloc.argtypes = [CFG] + [P] * 11 + [P]
         L.moe_dispatch.argtypes = [CFG] + [P] * 5 + [P]
         L.moe_expert_ffn.argtypes = [CFG] + [P] * 8 + [ctypes.c_int64, P, P, S, P]
         L.moe_expert_ffn_backward.argtypes = [CFG] + [P] * 12 + [P, S, P]
@@ -184,6 +185,13 @@ def moe_gate(cfg, x, w_router, b_router, logits_in, logits_out, expert_idx, slot
                           _ptr(logits_out), _ptr(expert_idx), _ptr(slot), _ptr(weight), _ptr(expert_count),
                           _ptr(expert_offset), _ptr(gate_loss), _ptr(ws), ws.numel() * ws.element_size(),
                           _stream(stream)))
+
+
+def moe_gate_noalloc(cfg, x, w_router, b_router, logits_in, logits_out, expert_idx, slot, weight, expert_count,
+                     expert_offset, gate_loss, stream=None):
+    _check(lib().moe_gate_noalloc(ctypes.byref(cfg), _ptr(x), _ptr(w_router), _ptr(b_router), _ptr(logits_in),
+                                  _ptr(logits_out), _ptr(expert_idx), _ptr(slot), _ptr(weight),
+                                  _ptr(expert_count), _ptr(expert_offset), _ptr(gate_loss), _stream(stream)))
 
 
 def moe_dispatch(cfg, x, expert_idx, slot, expert_offset, x_disp, stream=None):

@@ -4,6 +4,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "moe.h"
 #include "moe_internal.h"
 
@@ -75,7 +77,7 @@ int64_t max_rows_of(const moe_config* c) {
 struct Layout {
   int64_t T, C, rows;
   int tiles, tile_tokens;
-  size_t tile_cnt, me_tile, me_sum, demand, idx, slot, weight, offset;
+  size_t tile_cnt, me_tile, me_sum, demand, gate_end, idx, slot, weight, offset;
   size_t x_disp, a_save, h_disp, y_disp, d_act;
   int64_t h_ld;   // row pitch (elements) of h_disp in the layer forward
   size_t dec_logits, dec_prob, dec_part, dec_bar;   // small-batch forward: logits, probabilities, partial logits, barrier
@@ -107,6 +109,7 @@ Layout layout_of(const moe_config* c) {
   L.me_tile = take((size_t)L.tiles * E * 4);
   L.me_sum = take((size_t)E * 8);
   L.demand = take((size_t)2 * E * 4);
+  L.gate_end = off;   // the gate's own scratch ends here (moe_gate_noalloc)
   L.idx = take((size_t)L.T * k * 4);
   L.slot = take((size_t)L.T * k * 4);
   L.weight = take((size_t)L.T * k * 4);
@@ -282,6 +285,53 @@ moe_status forward_experts(const moe_config* cfg, const Layout& L, const void* x
   return run_ffn(cfg, L, xd, off, w1, b1, w2, b2, as, hd, yd, L.h_ld, s);
 }
 
+moe_status check_gate_args(const moe_config* cfg, const void* x, const void* w_router, const float* logits_in,
+                           const int32_t* expert_idx, const int32_t* slot, const float* weight,
+                           const int32_t* expert_count, const int32_t* expert_offset, const float* gate_loss) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  // per-token arrays may be NULL only when there are no tokens
+  const bool tok = cfg->num_tokens > 0;
+  if (tok && !logits_in && (!x || !w_router)) return MOE_ERR_INVALID_ARG;
+  if (tok && (!expert_idx || !slot || !weight)) return MOE_ERR_INVALID_ARG;
+  if (!expert_count || !expert_offset || !gate_loss) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------- library-owned gate scratch
+// moe_gate_noalloc keeps the gate's per-tile counts, per-tile probability
+// sums, their totals and the demand (the first regions of the workspace
+// layout, which every gate kernel writes before it reads them, so nothing
+// needs clearing) in this array instead of a caller workspace.  Each device
+// holds its own copy for the life of the process.  In host code the name is
+// a host-side stand-in, never a device address: the kernels get the address
+// that hipGetSymbolAddress returns for the current device.
+constexpr size_t kGateScratchBytes = (size_t)MOE_GATE_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kGateScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The device address of `scratch` on the current device, looked up on the
+// first call made with that device current and kept for later calls.
+hipError_t gate_scratch_of_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -356,15 +406,28 @@ moe_status moe_gate(const moe_config* cfg, const void* x, const void* w_router, 
                     const float* logits_in, float* logits_out, int32_t* expert_idx, int32_t* slot,
                     float* weight, int32_t* expert_count, int32_t* expert_offset, float* gate_loss, void* ws,
                     size_t ws_bytes, void* stream) {
-  moe_status st = check_config(cfg);
+  moe_status st = check_gate_args(cfg, x, w_router, logits_in, expert_idx, slot, weight, expert_count,
+                                  expert_offset, gate_loss);
   if (st != MOE_OK) return st;
-  // per-token arrays may be NULL only when there are no tokens
-  const bool tok = cfg->num_tokens > 0;
-  if (tok && !logits_in && (!x || !w_router)) return MOE_ERR_INVALID_ARG;
-  if (tok && (!expert_idx || !slot || !weight)) return MOE_ERR_INVALID_ARG;
-  if (!expert_count || !expert_offset || !gate_loss || !ws) return MOE_ERR_INVALID_ARG;
+  if (!ws) return MOE_ERR_INVALID_ARG;
   const Layout L = layout_of(cfg);
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  return run_gate(cfg, L, x, w_router, b_router, logits_in, logits_out, expert_idx, slot, weight, expert_count,
+                  expert_offset, gate_loss, ws, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_gate_noalloc(const moe_config* cfg, const void* x, const void* w_router, const float* b_router,
+                            const float* logits_in, float* logits_out, int32_t* expert_idx, int32_t* slot,
+                            float* weight, int32_t* expert_count, int32_t* expert_offset, float* gate_loss,
+                            void* stream) {
+  moe_status st = check_gate_args(cfg, x, w_router, logits_in, expert_idx, slot, weight, expert_count,
+                                  expert_offset, gate_loss);
+  if (st != MOE_OK) return st;
+  const Layout L = layout_of(cfg);
+  if (L.gate_end > kGateScratchBytes) return MOE_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (gate_scratch_of_current_device(&ws) != hipSuccess) return MOE_ERR_HIP;
+  // run_gate reads and writes only the gate's regions, [0, L.gate_end)
   return run_gate(cfg, L, x, w_router, b_router, logits_in, logits_out, expert_idx, slot, weight, expert_count,
                   expert_offset, gate_loss, ws, static_cast<hipStream_t>(stream));
 }

@@ -377,6 +377,17 @@ def test_workspace_status_word():
     assert L.moe_workspace_status(ctypes.byref(cfg), None, None) == B.MOE_ERR_INVALID_ARG
 
 
+def test_gate_noalloc_rejects_what_its_scratch_cannot_hold():
+    """The no-allocation gate refuses, before any device call, a config whose
+    gate scratch exceeds its fixed array (the pointers are never read)."""
+    L = B.lib()
+    big = _cfg(num_tokens=1 << 20, num_experts=256)
+    dummy = [ctypes.c_void_p(4096)] * 11
+    assert L.moe_gate_noalloc(ctypes.byref(big), *dummy, None) == B.MOE_ERR_WORKSPACE
+    assert L.moe_gate_noalloc(ctypes.byref(_cfg()), None, None, None, None, None, None, None, None, None, None,
+                              None, None) == B.MOE_ERR_INVALID_ARG
+
+
 def test_status_strings():
     for s in range(5):
         assert B.status_string(s).startswith("MOE_")
