@@ -128,31 +128,36 @@ __device__ __forceinline__ float act_rt(float v, int act) {
 // never written) after setting gate_loss to NaN and the status word (which
 // the host can read through moe_workspace_status) to 1.
 //
-// Publishing: every wavefront releases its own stores at agent scope before
-// the workgroup barrier.  A workgroup barrier orders the waves' execution but
-// does not wait for their outstanding global stores (on gfx950 __syncthreads
-// compiles to a bare s_barrier), and a release fence waits only for the
-// issuing wave's own memory operations before it writes this XCD's L2 back.
-// A release by thread 0 alone therefore does not cover a store of another
-// wave that is still on its way to the L2 when the write-back runs, and a
-// workgroup on another XCD (own L2) can then read the old value.  Stores by
-// several waves that other workgroups read after a barrier happen here in
-// the routing phase (a wave per token) and in the row copy.
+// Publishing: every wavefront first waits until its own stores have been
+// acknowledged by the L2 (s_waitcnt vmcnt(0)), then the workgroup barrier,
+// then thread 0's agent-scope release writes this XCD's L2 back before it
+// arrives.  A workgroup barrier orders the waves' execution but does not
+// wait for their outstanding global stores (on gfx950 __syncthreads compiles
+// to a bare s_barrier), and a release fence waits only for the issuing
+// wave's own memory operations before the write-back (buffer_wbl2).  Without
+// the per-wave wait, a store of another wave still on its way to the L2 when
+// the write-back runs stays in this XCD's L2, and a workgroup on another XCD
+// (own L2) can read the old value.  Stores by several waves that other
+// workgroups read after a barrier happen here in the routing phase (a wave
+// per token) and in the row copy.  (A full release in every wave does the
+// same but repeats the L2 write-back four times per workgroup: about 7 us
+// more per barrier, measured.)
 constexpr int kBarGroups = 16, kBarLine = 32;   // 32 words = 128 bytes
 constexpr int kBarTop = kBarGroups * kBarLine, kBarStatus = kBarTop + kBarLine;
 constexpr int kBarWords = kBarStatus + 1;
 static_assert(kBarStatus == kDecodeStatusWord, "status word index");
 
 __device__ __forceinline__ bool grid_barrier(unsigned* bar, unsigned phase, int* ok) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");   // each wave: its stores reach memory
+  // each wave: its stores have reached the L2 (vmcnt(0); expcnt, lgkmcnt not waited on)
+  __builtin_amdgcn_s_waitcnt(0x0f70);
   __syncthreads();
   if (threadIdx.x == 0) {
     const unsigned nwg = gridDim.x;
     const unsigned g = blockIdx.x % kBarGroups;
     const unsigned groups = nwg < (unsigned)kBarGroups ? nwg : (unsigned)kBarGroups;
     const unsigned gsize = (nwg - g + kBarGroups - 1) / kBarGroups;   // workgroups in group g
-    // the release that pairs with the arrival (the waves' own releases above
-    // made every store of the workgroup visible), relaxed arrivals and polls (an acquire per poll would invalidate the
+    // one release (with every wave's stores in the L2, its write-back
+    // publishes all of the workgroup's), relaxed arrivals and polls (an acquire per poll would invalidate the
     // XCD's L2 on every read), then one acquire
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     const unsigned old = __hip_atomic_fetch_add(&bar[g * kBarLine], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -99,6 +99,44 @@ __global__ __launch_bounds__(256) void dispatch_kernel(const u32x4* __restrict__
   }
 }
 
+// Dispatch fused with the gate's slot fix-up (the layer forward): the gate
+// left in slot each claim's rank among the claims of its (choice, expert)
+// column inside its token tile; the final slot is that rank plus the
+// column's prefix over earlier tiles (plus, for choice 1, the expert's whole
+// choice-0 demand), dropped at or past the capacity.  It is written back for
+// the later steps and used at once for the copy.  Every index load of a token
+// is issued before the first wait on them: expert and rank of each choice,
+// then the prefixes, the demand and the offsets.
+__global__ __launch_bounds__(256) void dispatch_finalize_kernel(const u32x4* __restrict__ x, GateArgs g,
+                                                                u32x4* __restrict__ x_disp, int nvec) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave_id = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
+  const int k = g.k, E = g.E;
+  const int64_t T = g.T, C = g.C;
+  for (int64_t t = wave_id; t < T; t += nwaves) {
+    const int64_t tile = t / g.tile_tokens;
+    const int e0 = g.expert_idx[t * k], q0 = g.slot[t * k];
+    const int e1 = k == 2 ? g.expert_idx[t * k + 1] : 0, q1 = k == 2 ? g.slot[t * k + 1] : 0;
+    int64_t s0 = (int64_t)q0 + g.tile_cnt[(int64_t)e0 * g.num_tiles + tile];
+    int64_t s1 = k == 2 ? (int64_t)q1 + g.tile_cnt[(int64_t)(E + e1) * g.num_tiles + tile] + g.demand[e1] : -1;
+    const int64_t o0 = g.expert_offset[e0];
+    const int64_t o1 = k == 2 ? g.expert_offset[e1] : 0;
+    if (C >= 0 && s0 >= C) s0 = -1;
+    if (C >= 0 && s1 >= C) s1 = -1;
+    if (lane == 0) {
+      g.slot[t * k] = (int32_t)s0;
+      if (k == 2) g.slot[t * k + 1] = (int32_t)s1;
+    }
+    const int64_t r0 = s0 >= 0 ? o0 + s0 : -1;
+    const int64_t r1 = s1 >= 0 ? o1 + s1 : -1;
+    if (r0 < 0 && r1 < 0) continue;
+    const u32x4* src = x + t * nvec;
+    if (r0 >= 0 && r1 >= 0) copy_row<2>(src, x_disp + r0 * nvec, x_disp + r1 * nvec, lane, nvec);
+    else copy_row<1>(src, x_disp + (r0 >= 0 ? r0 : r1) * nvec, nullptr, lane, nvec);
+  }
+}
+
 template <int DT>
 __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ y,
                                                       const int32_t* __restrict__ expert_idx,
@@ -179,6 +217,13 @@ hipError_t launch_dispatch(const void* x, const int32_t* expert_idx, const int32
   if (T == 0) return hipSuccess;
   hipLaunchKernelGGL(dispatch_kernel, dim3(row_grid(T)), dim3(256), 0, s, static_cast<const u32x4*>(x),
                      expert_idx, slot, expert_offset, static_cast<u32x4*>(x_disp), T, k, row_bytes / 16);
+  return hipGetLastError();
+}
+
+hipError_t launch_dispatch_finalize(const void* x, const GateArgs& g, void* x_disp, int row_bytes, hipStream_t s) {
+  if (g.T == 0) return hipSuccess;
+  hipLaunchKernelGGL(dispatch_finalize_kernel, dim3(row_grid(g.T)), dim3(256), 0, s, static_cast<const u32x4*>(x), g,
+                     static_cast<u32x4*>(x_disp), row_bytes / 16);
   return hipGetLastError();
 }
 

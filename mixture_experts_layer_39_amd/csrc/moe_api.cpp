@@ -77,7 +77,7 @@ int64_t max_rows_of(const moe_config* c) {
 struct Layout {
   int64_t T, C, rows;
   int tiles, tile_tokens;
-  size_t tile_cnt, me_tile, me_sum, demand, gate_end, idx, slot, weight, offset;
+  size_t tile_cnt, me_tile, me_sum, demand, gate_sync, gate_end, idx, slot, weight, offset;
   size_t x_disp, a_save, h_disp, y_disp, d_act;
   int64_t h_ld;   // row pitch (elements) of h_disp in the layer forward
   size_t dec_logits, dec_prob, dec_part, dec_bar;   // small-batch forward: logits, probabilities, partial logits, barrier
@@ -109,6 +109,7 @@ Layout layout_of(const moe_config* c) {
   L.me_tile = take((size_t)L.tiles * E * 4);
   L.me_sum = take((size_t)E * 8);
   L.demand = take((size_t)2 * E * 4);
+  L.gate_sync = take(4);
   L.gate_end = off;   // the gate's own scratch ends here (moe_gate_noalloc)
   L.idx = take((size_t)L.T * k * 4);
   L.slot = take((size_t)L.T * k * 4);
@@ -178,10 +179,13 @@ moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_
     if (_e != hipSuccess) return MOE_ERR_HIP;    \
   } while (0)
 
+// The gate.  With defer (set only when no Random Token Selection follows),
+// the slot fix-up is left to the caller's dispatch (launch_dispatch_finalize
+// with *args): slot then holds the in-tile ranks until that dispatch runs.
 moe_status run_gate(const moe_config* c, const Layout& L, const void* x, const void* w_router,
                     const float* b_router, const float* logits_in, float* logits_out, int32_t* expert_idx,
                     int32_t* slot, float* weight, int32_t* expert_count, int32_t* expert_offset,
-                    float* gate_loss, void* ws, hipStream_t s) {
+                    float* gate_loss, void* ws, hipStream_t s, GateArgs* defer = nullptr) {
   if (L.T == 0) return hip_status(launch_gate_empty(expert_count, expert_offset, gate_loss, c->num_experts, s));
   GateArgs a;
   a.x = x;
@@ -199,6 +203,7 @@ moe_status run_gate(const moe_config* c, const Layout& L, const void* x, const v
   a.me_tile = at<float>(ws, L.me_tile);
   a.me_sum = at<double>(ws, L.me_sum);
   a.demand = at<int32_t>(ws, L.demand);
+  a.sync = at<uint32_t>(ws, L.gate_sync);
   a.T = L.T;
   a.C = L.C;
   a.d = c->hidden_size;
@@ -206,7 +211,9 @@ moe_status run_gate(const moe_config* c, const Layout& L, const void* x, const v
   a.k = c->k;
   a.normalize = c->normalize_topk;
   a.loss_kind = c->loss_kind;
-  a.num_tiles = L.tiles;
+  const bool rnd = c->noisy_gate_policy != MOE_NOISE_NONE || c->second_expert_sampling;
+  a.tile_tokens = gate_tile_tokens_for(c->num_experts, c->hidden_size, c->dtype, logits_in != nullptr, rnd);
+  a.num_tiles = (int32_t)((L.T + a.tile_tokens - 1) / a.tile_tokens);   // <= L.tiles (64-token tiles)
   a.jitter = c->noisy_gate_policy == MOE_NOISE_JITTER;
   a.rsample = c->noisy_gate_policy == MOE_NOISE_RSAMPLE;
   a.second = c->second_expert_sampling;
@@ -215,8 +222,14 @@ moe_status run_gate(const moe_config* c, const Layout& L, const void* x, const v
   // jitter acts on the router's input: there is none when the logits are given
   if (a.jitter && logits_in) return MOE_ERR_INVALID_ARG;
   MOE_TRY_HIP(launch_gate(a, c->dtype, s));
-  MOE_TRY_HIP(launch_slot_finalize(a, L.tile_tokens, s));
-  if (c->use_rts && L.C >= 0) MOE_TRY_HIP(launch_rts_select(a, s));
+  const bool rts = c->use_rts && L.C >= 0;
+  if (defer && !rts) {
+    *defer = a;
+    return MOE_OK;
+  }
+  if (defer) defer->T = -1;   // slots are final: a plain dispatch follows
+  MOE_TRY_HIP(launch_slot_finalize(a, s));
+  if (rts) MOE_TRY_HIP(launch_rts_select(a, s));
   return MOE_OK;
 }
 
@@ -274,14 +287,18 @@ moe_status forward_experts(const moe_config* cfg, const Layout& L, const void* x
                            hipStream_t s) {
   // training: the backward needs the logits, so keep them when the caller does not
   float* lg = (logits_out || !cfg->save_preact) ? logits_out : at<float>(ws, L.logits);
+  GateArgs ga;
   moe_status st =
-      run_gate(cfg, L, x, w_router, b_router, logits_in, lg, idx, sl, wt, expert_count, off, gate_loss, ws, s);
+      run_gate(cfg, L, x, w_router, b_router, logits_in, lg, idx, sl, wt, expert_count, off, gate_loss, ws, s, &ga);
   if (st != MOE_OK || L.T == 0) return st;
   void* xd = at<void>(ws, L.x_disp);
   void* hd = cfg->ffn_hidden > 0 ? at<void>(ws, L.h_disp) : nullptr;
   void* as = (cfg->save_preact && cfg->ffn_hidden > 0) ? at<void>(ws, L.a_save) : nullptr;
   void* yd = at<void>(ws, L.y_disp);
-  MOE_TRY_HIP(launch_dispatch(x, idx, sl, off, xd, L.T, cfg->k, cfg->hidden_size * esize(cfg), s));
+  if (ga.T >= 0)
+    MOE_TRY_HIP(launch_dispatch_finalize(x, ga, xd, cfg->hidden_size * esize(cfg), s));
+  else
+    MOE_TRY_HIP(launch_dispatch(x, idx, sl, off, xd, L.T, cfg->k, cfg->hidden_size * esize(cfg), s));
   return run_ffn(cfg, L, xd, off, w1, b1, w2, b2, as, hd, yd, L.h_ld, s);
 }
 

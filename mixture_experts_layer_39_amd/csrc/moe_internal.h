@@ -56,8 +56,11 @@ __device__ __forceinline__ float act_fixed(float v) {
 
 
 // ---------------------------------------------------------------- gate
-// Tokens per gate tile: 64, four groups of 16, one per wavefront.
+// Tokens per gate tile: at most 64 (four groups of 16, one per wavefront),
+// which sizes the per-tile workspace; gate_tile_tokens_for gives the tile a
+// launch uses (256 for the deterministic 65..128-expert bf16 router).
 inline int gate_tile_tokens(int) { return 64; }
+int gate_tile_tokens_for(int E, int d, int dtype, bool logits_in, bool random_options);
 
 struct GateArgs {
   const void* x;            // [T, d] dtype (router GEMM modes)
@@ -76,11 +79,13 @@ struct GateArgs {
   float* me_tile;           // [tiles, E] per-tile sums of the softmax probabilities
   double* me_sum;           // [E] their totals
   int32_t* demand;          // [k, E] total claims per (choice, expert)
+  uint32_t* sync;           // arrival counter of the scan kernel (zeroed by the gate kernel)
   int64_t T;
   int64_t C;                // capacity, < 0 = none
   int32_t d, E, k;
   int32_t normalize, loss_kind;
   int32_t num_tiles;
+  int32_t tile_tokens;      // tokens per tile (64, or 256 for the 65..128-expert router)
   int32_t jitter, rsample, second;   // random gate options (router input jitter,
                                      // Gumbel top-1, Gumbel second expert)
   uint32_t seed_lo, seed_hi;         // Philox4x32-10 key
@@ -90,7 +95,7 @@ hipError_t launch_gate(const GateArgs& a, int dtype, hipStream_t s);
 // Random Token Selection (k = 1, with a capacity): after the slot fix-up,
 // every expert whose demand exceeds C keeps its C claims of largest priority.
 hipError_t launch_rts_select(const GateArgs& a, hipStream_t s);
-hipError_t launch_slot_finalize(const GateArgs& a, int tile_tokens, hipStream_t s);
+hipError_t launch_slot_finalize(const GateArgs& a, hipStream_t s);
 hipError_t launch_gate_empty(int32_t* expert_count, int32_t* expert_offset, float* gate_loss,
                              int E, hipStream_t s);
 
@@ -98,6 +103,9 @@ hipError_t launch_gate_empty(int32_t* expert_count, int32_t* expert_offset, floa
 hipError_t launch_dispatch(const void* x, const int32_t* expert_idx, const int32_t* slot,
                            const int32_t* expert_offset, void* x_disp, int64_t T, int k,
                            int row_bytes, hipStream_t s);
+// Dispatch with the gate's slot fix-up fused in (g as the gate ran it, its
+// slots still the in-tile ranks): writes the final slots and the packed rows.
+hipError_t launch_dispatch_finalize(const void* x, const GateArgs& g, void* x_disp, int row_bytes, hipStream_t s);
 hipError_t launch_combine(const void* y_disp, const int32_t* expert_idx, const int32_t* slot,
                           const float* weight, const int32_t* expert_offset, void* out,
                           int64_t T, int k, int d, int dtype, hipStream_t s);
