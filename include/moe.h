@@ -143,6 +143,18 @@ typedef struct moe_config {
                               refuse it) and the workspace holds the dense
                               branch's buffers                               */
   uint64_t seed;                  /* Philox key                             */
+  int32_t packed_weights;         /* 1: the expert weights w1 and w2 given to
+                              the forward calls (moe_expert_ffn,
+                              moe_layer_forward, moe_residual_layer_forward)
+                              are in the packed layout that
+                              moe_pack_expert_weight writes; needs bf16 and
+                              both Linears on the large-tile path (K a
+                              multiple of 64, N of 16, see
+                              moe_pack_expert_weight).  The backward calls
+                              refuse it (MOE_ERR_INVALID_ARG): they read the
+                              nn.Linear layout.  The dense branch of the
+                              residual MoE is never packed.  0: nn.Linear
+                              layout [E, out, in].                           */
 } moe_config;
 
 /* Static text for a status code. */
@@ -207,6 +219,31 @@ moe_status moe_gate_noalloc(const moe_config* cfg, const void* x, const void* w_
                             int32_t* expert_idx, int32_t* slot, float* weight,
                             int32_t* expert_count, int32_t* expert_offset, float* gate_loss,
                             void* stream);
+
+/* Packed expert weights (the layout of the expert weights in device
+ * memory, not a step of the layer: [MoE-sched] §3.1 Step 4 multiplies each
+ * expert's token rows by its weight whatever the layout).  An expert weight
+ * in the nn.Linear layout w[E, N, K] (N outputs, K inputs; w1: N = h,
+ * K = d; w2: N = d, K = h; ffn_hidden == 0: N = K = d) is rewritten as
+ * blocks of 256 output rows x 64 inputs, each block contiguous (32 KB in
+ * bf16):
+ *   packed[((e * ceil(N/256) + n / 256) * (K/64) + k / 64) * 16384
+ *          + (n % 256) * 64 + k % 64] = w[e, n, k]
+ * with zeros in the rows n >= N of the last block.  A 64-wide K step of a
+ * 256-feature tile of the grouped GEMM is then one contiguous 32 KB read
+ * instead of 256 rows of 128 bytes K elements apart, which spread over few
+ * memory channels; a caller that keeps its inference weights packed (once,
+ * after loading or after each update) runs the forward's GEMMs faster.
+ * Needs dtype bf16, K a positive multiple of 64, N a positive multiple of
+ * 16 (MOE_ERR_UNSUPPORTED otherwise, MOE_ERR_INVALID_ARG for non-positive
+ * sizes or E outside 1..MOE_MAX_EXPERTS).
+ *   moe_packed_weight_bytes: the packed size, E * ceil(N/256) * 256 * K * 2.
+ *   moe_pack_expert_weight: w device [E, N, K]; w_packed device, that many
+ *   bytes, must not overlap w; enqueued on stream. */
+moe_status moe_packed_weight_bytes(int32_t num_experts, int64_t n, int64_t k, int32_t dtype,
+                                   size_t* bytes);
+moe_status moe_pack_expert_weight(int32_t num_experts, int64_t n, int64_t k, int32_t dtype,
+                                  const void* w, void* w_packed, void* stream);
 
 /* Dispatch ([MoE-sched] §3.1 Step 3; [ds.moe] §3.1 step 2 on one GPU):
  * for every kept claim (t, j): x_disp[expert_offset[e] + slot[t,j]] = x[t],

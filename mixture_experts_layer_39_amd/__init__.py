@@ -33,6 +33,11 @@ class MoE:
     the one-launch forward for a few tokens (0 automatic, 1 always when it
     applies, -1 never).
 
+    ``pack_weights()`` keeps copies of the expert weights in the packed
+    layout (moe_pack_expert_weight), which the inference forward (after
+    ``eval()``) then reads; call it again after the weights change.  Training
+    forwards read the nn.Linear weights.
+
     The random gate options noisy_gate_policy ("Jitter" or "RSample"),
     use_rts and top2_2nd_expert_sampling act in training mode only and, as
     in the gate they come from, each where it applies: RSample and RTS with
@@ -67,6 +72,17 @@ class MoE:
         self.w1, self.b1, self.w2, self.b2 = w1, b1, w2, b2
         self.dtype = MOE_BF16 if w1.dtype == torch.bfloat16 else MOE_F32
         self._ws = None
+        self._packed = None   # (w1, w2) in the packed layout, or None
+
+    def pack_weights(self):
+        """Packed copies of w1 and w2 for the inference forward (raises
+        MoeError where the packed layout does not apply)."""
+        probe = make_config(1, self.hidden_size, self.num_experts, self.k, 1.0, self.min_capacity, self.drop_tokens,
+                            self.ffn_hidden, self.activation, self.dtype, packed_weights=True)
+        moe_workspace_size(probe)   # validates the configuration
+        w2 = binding.pack_expert_weight(self.w2) if self.w2 is not None else None
+        self._packed = (binding.pack_expert_weight(self.w1), w2)
+        return self
 
     def train(self, mode=True):
         self.training = bool(mode)
@@ -88,7 +104,7 @@ class MoE:
         return make_config(num_tokens, self.hidden_size, self.num_experts, self.k, cf, self.min_capacity,
                            self.drop_tokens, self.ffn_hidden, self.activation, self.dtype, self.normalize_topk,
                            self.loss_kind, small_batch=self.small_batch, use_residual=self.residual is not None,
-                           **rnd)
+                           packed_weights=self._packed is not None and not self.training, **rnd)
 
     def forward(self, x, logits=None):
         import torch
@@ -101,12 +117,13 @@ class MoE:
         out = torch.empty_like(x2)
         loss = torch.empty(1, dtype=torch.float32, device=x.device)
         count = torch.empty(self.num_experts, dtype=torch.int32, device=x.device)
+        w1, w2 = self._packed if cfg.packed_weights else (self.w1, self.w2)
         if self.residual is None:
-            moe_layer_forward(cfg, x2, self.w_router, self.b_router, logits, self.w1, self.b1, self.w2, self.b2,
+            moe_layer_forward(cfg, x2, self.w_router, self.b_router, logits, w1, self.b1, w2, self.b2,
                               out, loss, count, ws=self._ws)
         else:
-            binding.moe_residual_layer_forward(cfg, x2, self.w_router, self.b_router, logits, self.w1, self.b1,
-                                               self.w2, self.b2, *self.residual, out, loss, count, ws=self._ws)
+            binding.moe_residual_layer_forward(cfg, x2, self.w_router, self.b_router, logits, w1, self.b1,
+                                               w2, self.b2, *self.residual, out, loss, count, ws=self._ws)
         if self.training:
             self.steps += 1
         return out.reshape(shape), loss[0], count

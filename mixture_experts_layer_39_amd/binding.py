@@ -26,7 +26,8 @@ EXPORTED = ("moe_status_string", "moe_capacity", "moe_max_rows", "moe_workspace_
             "moe_dispatch", "moe_expert_ffn", "moe_expert_ffn_backward", "moe_combine",
             "moe_layer_forward", "moe_workspace_views", "moe_combine_backward", "moe_gate_backward",
             "moe_dispatch_backward", "moe_router_backward", "moe_layer_backward", "moe_residual_layer_forward",
-            "moe_residual_layer_backward", "moe_workspace_h_ld", "moe_workspace_status", "moe_gate_noalloc")
+            "moe_residual_layer_backward", "moe_workspace_h_ld", "moe_workspace_status", "moe_gate_noalloc",
+            "moe_packed_weight_bytes", "moe_pack_expert_weight")
 
 
 class MoeConfig(ctypes.Structure):
@@ -50,18 +51,20 @@ class MoeConfig(ctypes.Structure):
         ("second_expert_sampling", ctypes.c_int32),
         ("use_residual", ctypes.c_int32),
         ("seed", ctypes.c_uint64),
+        ("packed_weights", ctypes.c_int32),
     ]
 
 
 def make_config(num_tokens, hidden_size, num_experts, k=1, capacity_factor=1.0, min_capacity=4,
                 drop_tokens=True, ffn_hidden=0, activation=MOE_ACT_NONE, dtype=MOE_BF16,
                 normalize_topk=False, loss_kind=MOE_LOSS_BALANCE, save_preact=False, small_batch=0,
-                noisy_gate_policy=0, use_rts=False, second_expert_sampling=False, seed=0, use_residual=False):
+                noisy_gate_policy=0, use_rts=False, second_expert_sampling=False, seed=0, use_residual=False,
+                packed_weights=False):
     return MoeConfig(int(num_tokens), float(capacity_factor), int(hidden_size), int(num_experts), int(k),
                      int(min_capacity), int(bool(drop_tokens)), int(ffn_hidden), int(activation), int(dtype),
                      int(bool(normalize_topk)), int(loss_kind), int(bool(save_preact)), int(small_batch),
                      int(noisy_gate_policy), int(bool(use_rts)), int(bool(second_expert_sampling)),
-                     int(bool(use_residual)), int(seed) & (2 ** 64 - 1))
+                     int(bool(use_residual)), int(seed) & (2 ** 64 - 1), int(bool(packed_weights)))
 
 
 class MoeError(RuntimeError):
@@ -104,6 +107,9 @@ def lib():
         L.moe_layer_backward.argtypes = [CFG] + [P] * 18 + [P, S, P]
         L.moe_residual_layer_forward.argtypes = [CFG] + [P] * 22 + [P, S, P]
         L.moe_residual_layer_backward.argtypes = [CFG] + [P] * 27 + [P, S, P]
+        L.moe_packed_weight_bytes.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                                              ctypes.POINTER(ctypes.c_size_t)]
+        L.moe_pack_expert_weight.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, P, P, P]
         for name in EXPORTED:
             if name != "moe_status_string":
                 getattr(L, name).restype = ctypes.c_int
@@ -155,6 +161,29 @@ def moe_workspace_size(cfg):
     c = ctypes.c_size_t()
     _check(lib().moe_workspace_size(ctypes.byref(cfg), ctypes.byref(c)))
     return c.value
+
+
+def moe_packed_weight_bytes(num_experts, n, k, dtype=MOE_BF16):
+    """Bytes of an expert weight [E, n, k] in the packed layout."""
+    v = ctypes.c_size_t()
+    _check(lib().moe_packed_weight_bytes(int(num_experts), int(n), int(k), int(dtype), ctypes.byref(v)))
+    return v.value
+
+
+def moe_pack_expert_weight(w, w_packed, dtype=MOE_BF16, stream=None):
+    """Repack w [E, n, k] (device) into w_packed (moe_packed_weight_bytes(E, n, k) bytes)."""
+    E, n, k = w.shape
+    _check(lib().moe_pack_expert_weight(int(E), int(n), int(k), int(dtype), _ptr(w), _ptr(w_packed),
+                                        _stream(stream)))
+
+
+def pack_expert_weight(w, stream=None):
+    """A new packed copy of the bf16 expert weight w [E, n, k] (a flat uint8 device tensor)."""
+    import torch
+    E, n, k = w.shape
+    out = torch.empty(moe_packed_weight_bytes(E, n, k), dtype=torch.uint8, device=w.device)
+    moe_pack_expert_weight(w, out, stream=stream)
+    return out
 
 
 def moe_workspace_h_ld(cfg):

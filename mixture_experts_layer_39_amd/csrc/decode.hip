@@ -435,7 +435,7 @@ __device__ __forceinline__ f32x4 block_product(const bf16* wrow, const bf16* bro
 // Per-lane view of one work unit of an expert Linear: 16 output features of
 // one expert times one block of (up to) 16 of its rows.
 struct LinUnit {
-  const bf16* w;   // lane's weight row (feature f0 + lane % 16) at its K start
+  const bf16* w;   // start of the lane's weight row (feature f0 + lane % 16)
   const bf16* b;   // lane's input row at the same K offset (a valid row when past the block's end)
   int e, f0, rb;   // expert, first output feature, first row of the block
 };
@@ -469,6 +469,18 @@ __device__ void decode_linear(const DecodeArgs& a, DecShared& S, int phase) {
   bf16* Y = (phase == 1 && h > 0) ? a.h_disp : a.y_disp;
   const bool act = phase == 1;
   const int nwg = gridDim.x;
+  // Weight element k of a row sits at (k / 64) * kb + k % 64 from the row's
+  // start: kb = 64 in the row-major layout [E, nout, K]; with packed weights
+  // row n of expert e starts block (e * ntf + n / 256) * (K / 64) at
+  // (n % 256) * 64 and its K step k / 64 is the block kb = 16384 elements on.
+  const bool packed = a.w_packed != 0;
+  const int ntf = (nout + 255) / 256;
+  const int kb = packed ? 16384 : 64;
+  auto wrow = [&](int e, int n) -> const bf16* {
+    return packed ? W + (((int64_t)e * ntf + n / 256) * (K / 64)) * 16384 + (n % 256) * 64
+                  : W + ((int64_t)e * nout + n) * K;
+  };
+  auto wat = [&](const bf16* row, int k) -> const bf16* { return row + (k >> 6) * kb + (k & 63); };
 
   auto unit = [&](int it, int rb) {
     const int key = phase == 1 ? it : (it / nfb) * nfb1;   // the expert's first phase-1 item
@@ -481,7 +493,7 @@ __device__ void decode_linear(const DecodeArgs& a, DecShared& S, int phase) {
     u.e = lo;
     u.f0 = (phase == 1 ? it - S.ipre[lo] : it % nfb) * kFB;
     u.rb = rb;
-    u.w = W + ((int64_t)lo * nout + u.f0 + n16) * K + kw;
+    u.w = wrow(lo, u.f0 + n16);
     const int rr = rb + n16;
     const int r = S.off[lo] + (rr < S.cnt[lo] ? rr : 0);
     u.b = X + (int64_t)(phase == 1 ? S.rowtok[r] : r) * K + kw;
@@ -495,7 +507,7 @@ __device__ void decode_linear(const DecodeArgs& a, DecShared& S, int phase) {
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
     const int s = j < nst ? j : nst - 1;
-    av[j] = ldv(cur.w + 32 * s);
+    av[j] = ldv(wat(cur.w, kw + 32 * s));
     bv[j] = ldv(cur.b + 32 * s);
   }
   for (;;) {
@@ -527,7 +539,7 @@ __device__ void decode_linear(const DecodeArgs& a, DecShared& S, int phase) {
         const bool here = s2 < npad;
         int ss = here ? s2 : s2 - npad;
         ss = ss < nst ? ss : nst - 1;
-        av[jj] = ldv((here ? cur.w : nxt.w) + 32 * ss);
+        av[jj] = ldv(wat(here ? cur.w : nxt.w, kw + 32 * ss));
         bv[jj] = ldv((here ? cur.b : nxt.b) + 32 * ss);
       }
     }

@@ -330,6 +330,7 @@ struct BigArgs {
   int64_t feat_estride;     // elements between experts' feature operands (0: packed rows)
   int64_t y_ld, y_estride;  // output row pitch; per-expert output stride (weight gradients)
   int32_t E, N, K, M, act;  // K: contraction (token-row tiles); M: output rows (weight gradients)
+  int32_t feat_packed;      // K-contiguous feature operand in packed blocks of 256 rows x 64 K
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -385,6 +386,7 @@ struct BigCtx {
   bool tr;                      // this wave's operand is transposed
   uint32_t vbase_e, vbase_o;    // per-lane load offsets for even / odd instructions
   uint32_t sbase, ld_bytes;     // per-wave row base; bytes between operand rows
+  uint32_t kstride;             // K-contiguous: bytes between consecutive 64-wide K steps
 };
 
 template <int TOK, int FEAT, int MODE>
@@ -416,7 +418,9 @@ __device__ __forceinline__ BigTile big_tile_desc(const BigArgs& a, const BigCtx&
     const int ncols = min(BF, a.N - t.n0);
     if constexpr (FEAT == OP_KC) {
       const bf16* p = a.feat + (int64_t)tc.e * a.feat_estride + (int64_t)t.n0 * a.feat_ld;
-      t.lr = make_rsrc(p, (uint32_t)ncols * c.ld_bytes);
+      // packed: the tile's K steps are consecutive 32 KB blocks whose rows
+      // past N are zero, so the descriptor covers all of them
+      t.lr = make_rsrc(p, a.feat_packed ? (uint32_t)(a.K / 64) * (256u * 128u) : (uint32_t)ncols * c.ld_bytes);
     } else {
       const int krows = MODE == BM_WGRAD ? rows : a.K;
       const bf16* p = a.feat + (int64_t)tc.e * a.feat_estride + (MODE == BM_WGRAD ? (int64_t)t.row0 * a.feat_ld : 0) +
@@ -440,7 +444,8 @@ __device__ __forceinline__ BigTile big_tile_desc(const BigArgs& a, const BigCtx&
 // tile, waves 2-3 the feature tile (feature rows permuted so the MFMA row
 // m = lane&31 reads feature ((m>>2)&1)*16 + (m>>3)*4 + (m&3)); the row goes
 // in the per-lane offset, which the buffer range check always covers, and
-// only the position along K (inside a valid row) in the scalar offset.
+// only the position along K (inside a valid row, or, for packed weights,
+// the K step's 32 KB block of the tile) in the scalar offset.
 // Transposed: K rows 2i, 2i+1 of this wave's 32, 512 bytes each; the K row
 // goes in the per-lane offset (K rows past the end read as zero).
 __device__ __forceinline__ void big_issue_one(const BigCtx& c, __amdgpu_buffer_rsrc_t lr, int stage, int kstep, int i) {
@@ -453,7 +458,7 @@ __device__ __forceinline__ void big_issue_one(const BigCtx& c, __amdgpu_buffer_r
   const uint32_t kc_row = c.sbase + g * c.ld_bytes;
   const uint32_t tr_row = (uint32_t)(kstep * 64 + (c.wave & 1) * 32 + 2 * i) * c.ld_bytes;
   const uint32_t vrow = c.tr ? tr_row : kc_row;
-  const uint32_t soff = c.tr ? 0u : (uint32_t)kstep * 128;
+  const uint32_t soff = c.tr ? 0u : (uint32_t)kstep * c.kstride;
   __builtin_amdgcn_raw_ptr_buffer_load_lds(lr, (__attribute__((address_space(3))) void*)dst, 16,
                                            ((i & 1) ? c.vbase_o : c.vbase_e) + vrow, soff, 0, 0);
 }
@@ -780,6 +785,12 @@ void gemm_bf16_big_kernel(BigArgs a) {
   c.lds_op = wave >= 2 ? TILE_BYTES : 0;
   c.tr = wave >= 2 ? FEAT == OP_TR : TOK == OP_TR;
   c.ld_bytes = (uint32_t)((wave >= 2 ? a.feat_ld : a.tok_ld) * 2);
+  c.kstride = 128;
+  if (wave >= 2 && FEAT == OP_KC && a.feat_packed) {
+    // packed weights: a K step of the tile is one block of 256 rows x 128 B
+    c.ld_bytes = 128;
+    c.kstride = 256 * 128;
+  }
   if (!c.tr) {
     // K-contiguous: this lane's source row / chunk for each of its 16 load
     // instructions.  Chunk c of tile row r sits in slot c ^ ((r >> 1) & 7).
@@ -931,7 +942,10 @@ hipError_t launch_bf16_big(const GemmArgs& g, hipStream_t s) {
   a.max_rows = g.max_rows;
   a.tok_ld = g.x_ld ? g.x_ld : g.K;
   a.feat_ld = g.K;
-  a.feat_estride = (int64_t)g.N * g.K;
+  // packed: an expert's blocks cover ceil(N/256) * 256 rows; tile nf still
+  // starts nf * 256 * K elements into them
+  a.feat_estride = (int64_t)(g.w_packed ? (g.N + big::BF - 1) / big::BF * big::BF : g.N) * g.K;
+  a.feat_packed = g.w_packed;
   a.y_ld = g.y_ld ? g.y_ld : g.N;
   a.y_estride = 0;
   a.E = g.E;
@@ -1033,8 +1047,38 @@ bool grouped_gemm_is_big(int64_t K, int64_t N, int dtype) {
   return dtype == DT_BF16 && K > 0 && K % 64 == 0 && N % 16 == 0 && (int64_t)256 * (K + 64) * 2 < (int64_t(1) << 31);
 }
 
+// Packed expert weight: one thread per 16-byte chunk of the packed tensor,
+// [E][ceil(N/256)][K/64][256][64], reading row n = nf*256 + r of expert e
+// (zeros past N).
+__global__ __launch_bounds__(256) void pack_expert_weight_kernel(const uint4* __restrict__ w, uint4* __restrict__ wp,
+                                                                 int64_t N, int64_t K, int64_t ntf, int64_t chunks) {
+  const int64_t nk = K / 64;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < chunks; i += (int64_t)gridDim.x * 256) {
+    const int64_t c8 = i & 7;             // 16-byte chunk within the 128-byte row of the block
+    const int64_t r = (i >> 3) & 255;     // row within the block
+    int64_t b = i >> 11;                  // block: ((e * ntf + nf) * nk + ks)
+    const int64_t ks = b % nk;
+    b /= nk;
+    const int64_t nf = b % ntf;
+    const int64_t e = b / ntf;
+    const int64_t n = nf * 256 + r;
+    wp[i] = n < N ? w[((e * N + n) * K + ks * 64) / 8 + c8] : make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+
+hipError_t launch_pack_expert_weight(const void* w, void* wp, int E, int64_t N, int64_t K, hipStream_t s) {
+  const int64_t ntf = (N + 255) / 256;
+  const int64_t chunks = (int64_t)E * ntf * 256 * K / 8;
+  if (chunks <= 0) return hipSuccess;
+  const int64_t grid = std::min<int64_t>((chunks + 255) / 256, 8192);
+  hipLaunchKernelGGL(pack_expert_weight_kernel, dim3((unsigned)grid), dim3(256), 0, s, static_cast<const uint4*>(w),
+                     static_cast<uint4*>(wp), N, K, ntf, chunks);
+  return hipGetLastError();
+}
+
 hipError_t launch_grouped_gemm(const GemmArgs& a, int dtype, hipStream_t s) {
   if (a.max_rows <= 0) return hipSuccess;
+  if (a.w_packed && !grouped_gemm_is_big(a.K, a.N, dtype)) return hipErrorNotSupported;
   const bool pitched = (a.x_ld && a.x_ld != a.K) || (a.y_ld && a.y_ld != a.N);
   if (pitched && (a.x_ld && a.x_ld < a.K || a.y_ld && a.y_ld < a.N || a.x_ld > a.K + 64)) return hipErrorInvalidValue;
   if (grouped_gemm_is_big(a.K, a.N, dtype)) return launch_bf16_big(a, s);

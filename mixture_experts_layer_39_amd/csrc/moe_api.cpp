@@ -49,6 +49,15 @@ moe_status check_config(const moe_config* c) {
   if (c->noisy_gate_policy == MOE_NOISE_JITTER && c->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (c->use_residual != 0 && c->use_residual != 1) return MOE_ERR_INVALID_ARG;
   if (c->use_residual && c->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (c->packed_weights != 0 && c->packed_weights != 1) return MOE_ERR_INVALID_ARG;
+  if (c->packed_weights) {
+    // only the large-tile GEMM (and the one-launch small-batch kernel) read
+    // the packed layout: bf16, both expert Linears on that path
+    const int d = c->hidden_size, h = c->ffn_hidden;
+    const bool big = h > 0 ? grouped_gemm_is_big(d, h, c->dtype) && grouped_gemm_is_big(h, d, c->dtype)
+                           : grouped_gemm_is_big(d, d, c->dtype);
+    if (c->dtype != MOE_BF16 || !big) return MOE_ERR_UNSUPPORTED;
+  }
   // kernels move rows as 16-byte vectors
   const int vec = c->dtype == MOE_BF16 ? 8 : 4;
   if (c->hidden_size % vec) return MOE_ERR_UNSUPPORTED;
@@ -242,6 +251,7 @@ moe_status run_ffn(const moe_config* c, const Layout& L, const void* x_disp, con
   g.offset = offset;
   g.max_rows = L.rows;
   g.E = c->num_experts;
+  g.w_packed = c->packed_weights;
   if (h > 0) {
     g.X = x_disp;
     g.W = w1;
@@ -362,6 +372,31 @@ const char* moe_status_string(moe_status s) {
     case MOE_ERR_HIP: return "MOE_ERR_HIP: HIP runtime or launch error";
   }
   return "unknown moe_status";
+}
+
+moe_status moe_packed_weight_bytes(int32_t num_experts, int64_t n, int64_t k, int32_t dtype, size_t* bytes) {
+  if (!bytes || num_experts < 1 || num_experts > MOE_MAX_EXPERTS || n <= 0 || k <= 0) return MOE_ERR_INVALID_ARG;
+  if (dtype != MOE_BF16 && dtype != MOE_F32) return MOE_ERR_INVALID_ARG;
+  if (n >= (int64_t(1) << 31) || k >= (int64_t(1) << 31)) return MOE_ERR_INVALID_ARG;
+  if (dtype != MOE_BF16 || !grouped_gemm_is_big(k, n, dtype)) return MOE_ERR_UNSUPPORTED;
+  *bytes = (size_t)num_experts * (size_t)((n + 255) / 256 * 256) * (size_t)k * 2;
+  return MOE_OK;
+}
+
+moe_status moe_pack_expert_weight(int32_t num_experts, int64_t n, int64_t k, int32_t dtype, const void* w,
+                                  void* w_packed, void* stream) {
+  size_t bytes = 0;
+  const moe_status st = moe_packed_weight_bytes(num_experts, n, k, dtype, &bytes);
+  if (st != MOE_OK) return st;
+  if (!w || !w_packed) return MOE_ERR_INVALID_ARG;
+  // the kernel reads and writes 16-byte chunks
+  if (reinterpret_cast<uintptr_t>(w) % 16 || reinterpret_cast<uintptr_t>(w_packed) % 16) return MOE_ERR_INVALID_ARG;
+  const char* a = static_cast<const char*>(w);
+  const char* b = static_cast<const char*>(w_packed);
+  const size_t in_bytes = (size_t)num_experts * (size_t)n * (size_t)k * 2;
+  if (a < b + bytes && b < a + in_bytes) return MOE_ERR_INVALID_ARG;   // overlap
+  MOE_TRY_HIP(launch_pack_expert_weight(w, w_packed, num_experts, n, k, static_cast<hipStream_t>(stream)));
+  return MOE_OK;
 }
 
 moe_status moe_capacity(const moe_config* cfg, int64_t* C) {
@@ -485,7 +520,7 @@ moe_status moe_expert_ffn_backward(const moe_config* cfg, const void* x_disp, co
                                    float* db2, void* ws, size_t ws_bytes, void* stream) {
   moe_status st = check_config(cfg);
   if (st != MOE_OK) return st;
-  if (cfg->ffn_hidden <= 0) return MOE_ERR_INVALID_ARG;
+  if (cfg->ffn_hidden <= 0 || cfg->packed_weights) return MOE_ERR_INVALID_ARG;   // the backward reads nn.Linear weights
   if (!x_disp || !expert_offset || !w1 || !w2 || !a_save || !h_disp || !dy_disp || !dx_disp || !dw1 || !dw2 ||
       !ws)
     return MOE_ERR_INVALID_ARG;
@@ -559,6 +594,7 @@ moe_status moe_layer_forward(const moe_config* cfg, const void* x, const void* w
     da.w1 = static_cast<const bf16*>(w1);
     da.b1 = static_cast<const bf16*>(b1);
     da.w2 = static_cast<const bf16*>(w2);
+    da.w_packed = cfg->packed_weights;
     da.b2 = static_cast<const bf16*>(b2);
     da.out = static_cast<bf16*>(out);
     da.gate_loss = gate_loss;
@@ -709,7 +745,7 @@ moe_status run_router_wgrad(const moe_config* c, const Layout& L, const void* x,
 // Shapes the router and dispatch backward kernels take: bf16, d a multiple
 // of 32 (64 for the router weight gradient), the backward workspace regions.
 moe_status check_backward(const moe_config* c, bool router_weights) {
-  if (!c->save_preact) return MOE_ERR_INVALID_ARG;
+  if (!c->save_preact || c->packed_weights) return MOE_ERR_INVALID_ARG;   // nn.Linear weights only
   if (c->dtype != MOE_BF16 || c->hidden_size % 32) return MOE_ERR_UNSUPPORTED;
   if (router_weights && c->hidden_size % 64) return MOE_ERR_UNSUPPORTED;
   const Layout L = layout_of(c);

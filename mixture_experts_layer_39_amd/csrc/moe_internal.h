@@ -123,10 +123,14 @@ struct GemmArgs {
   int32_t E, N, K, act;
   int64_t x_ld = 0, y_ld = 0;  // row pitches of X and Y (and Apre) in elements; 0: K and N.
                                // Other pitches only where grouped_gemm_is_big holds.
+  int32_t w_packed = 0;        // W in the packed layout (moe_pack_expert_weight); big path only
 };
 hipError_t launch_grouped_gemm(const GemmArgs& a, int dtype, hipStream_t s);
 // Whether launch_grouped_gemm runs this shape on the large-tile kernel.
 bool grouped_gemm_is_big(int64_t K, int64_t N, int dtype);
+// Expert weight [E, N, K] (bf16) into the packed layout: blocks of 256 rows
+// x 64 K values, each contiguous, rows past N zero.
+hipError_t launch_pack_expert_weight(const void* w, void* wp, int E, int64_t N, int64_t K, hipStream_t s);
 
 // Backward pieces (see gemm_bwd.hip).
 struct GemmBwdArgs {
@@ -296,6 +300,7 @@ struct DecodeArgs {
   const bf16* w1;           // [E, n1, d], n1 = h (or d for a single Linear)
   const bf16* b1;           // [E, n1] or null
   const bf16* w2;           // [E, d, h] or null
+  int32_t w_packed;         // w1 and w2 in the packed layout
   const bf16* b2;           // [E, d] or null
   bf16* out;                // [T, d]
   float* gate_loss;

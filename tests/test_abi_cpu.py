@@ -46,6 +46,7 @@ int main(void) {
   F(num_tokens) F(capacity_factor) F(hidden_size) F(num_experts) F(k) F(min_capacity) F(drop_tokens)
   F(ffn_hidden) F(activation) F(dtype) F(normalize_topk) F(loss_kind) F(save_preact)
   F(small_batch) F(noisy_gate_policy) F(use_rts) F(second_expert_sampling) F(use_residual) F(seed)
+  F(packed_weights)
   return 0;
 }'''
     with tempfile.TemporaryDirectory() as d:
@@ -133,6 +134,9 @@ def test_workspace_size_grows_with_problem():
     (dict(hidden_size=500), B.MOE_ERR_UNSUPPORTED),
     (dict(ffn_hidden=100, activation=B.MOE_ACT_GELU), B.MOE_ERR_UNSUPPORTED),
     (dict(hidden_size=34, dtype=B.MOE_F32), B.MOE_ERR_UNSUPPORTED),
+    (dict(packed_weights=True, dtype=B.MOE_F32), B.MOE_ERR_UNSUPPORTED),
+    (dict(packed_weights=True, hidden_size=96), B.MOE_ERR_UNSUPPORTED),              # d % 64
+    (dict(packed_weights=True, ffn_hidden=520, activation=B.MOE_ACT_GELU), B.MOE_ERR_UNSUPPORTED),  # h % 64
 ])
 def test_invalid_configs_are_rejected(kw, status):
     cfg = _cfg(**kw)
@@ -289,6 +293,56 @@ def test_backward_entry_points_validate_before_launch():
     assert L.moe_layer_backward(c, *args, FAKE, ws - 1, None) == B.MOE_ERR_WORKSPACE
     one = _cfg(hidden_size=256, ffn_hidden=0, save_preact=True)
     assert L.moe_layer_backward(ctypes.byref(one), *args, FAKE, 1 << 40, None) == B.MOE_ERR_INVALID_ARG
+
+
+def test_packed_weights_config_and_sizes():
+    # accepted where both Linears take the large-tile path
+    for kw in (dict(), dict(ffn_hidden=1024, activation=B.MOE_ACT_GELU), dict(hidden_size=128, ffn_hidden=192,
+                                                                             activation=B.MOE_ACT_RELU)):
+        assert B.moe_workspace_size(_cfg(packed_weights=True, **kw)) == B.moe_workspace_size(_cfg(**kw))
+    cfg = _cfg(packed_weights=True)
+    cfg.packed_weights = 2
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_workspace_size(cfg)
+    assert ei.value.status == B.MOE_ERR_INVALID_ARG
+    # E * ceil(N / 256) * 256 * K * 2 bytes
+    assert B.moe_packed_weight_bytes(64, 5120, 2048) == 64 * 5120 * 2048 * 2
+    assert B.moe_packed_weight_bytes(3, 80, 128) == 3 * 256 * 128 * 2
+    assert B.moe_packed_weight_bytes(1, 272, 64) == 512 * 64 * 2
+    for args, st in (((0, 256, 64), B.MOE_ERR_INVALID_ARG), ((257, 256, 64), B.MOE_ERR_INVALID_ARG),
+                     ((1, 0, 64), B.MOE_ERR_INVALID_ARG), ((1, 256, -64), B.MOE_ERR_INVALID_ARG),
+                     ((1, 256, 96), B.MOE_ERR_UNSUPPORTED), ((1, 24, 64), B.MOE_ERR_UNSUPPORTED)):
+        with pytest.raises(B.MoeError) as ei:
+            B.moe_packed_weight_bytes(*args)
+        assert ei.value.status == st, args
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_packed_weight_bytes(1, 256, 64, B.MOE_F32)
+    assert ei.value.status == B.MOE_ERR_UNSUPPORTED
+
+
+def test_pack_expert_weight_validates_before_launch():
+    L = B.lib()
+    n = 2 * 256 * 128 * 2   # E = 2, N = 256, K = 128
+    # missing pointers, misalignment, overlap of input and output
+    assert L.moe_pack_expert_weight(2, 256, 128, B.MOE_BF16, None, FAKE, None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_expert_weight(2, 256, 128, B.MOE_BF16, FAKE, None, None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_expert_weight(2, 256, 128, B.MOE_BF16, FAKE + 8, FAKE + 2 * n, None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_expert_weight(2, 256, 128, B.MOE_BF16, FAKE, FAKE + n - 16, None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_expert_weight(2, 256, 128, B.MOE_BF16, FAKE + n - 16, FAKE, None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_expert_weight(2, 256, 96, B.MOE_BF16, FAKE, FAKE + 2 * n, None) == B.MOE_ERR_UNSUPPORTED
+    assert L.moe_pack_expert_weight(2, 256, 128, B.MOE_F32, FAKE, FAKE + 2 * n, None) == B.MOE_ERR_UNSUPPORTED
+
+
+def test_backward_refuses_packed_weights():
+    L = B.lib()
+    tr = _cfg(hidden_size=256, ffn_hidden=512, activation=B.MOE_ACT_GELU, save_preact=True, packed_weights=True)
+    c = ctypes.byref(tr)
+    assert L.moe_expert_ffn_backward(c, *([FAKE] * 12), FAKE, 1 << 40, None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_layer_backward(c, *([FAKE] * 18), FAKE, 1 << 40, None) == B.MOE_ERR_INVALID_ARG
+    res = _cfg(hidden_size=256, ffn_hidden=512, activation=B.MOE_ACT_GELU, save_preact=True, packed_weights=True,
+               use_residual=True)
+    assert L.moe_residual_layer_backward(ctypes.byref(res), *([FAKE] * 27), FAKE, 1 << 40, None) \
+        == B.MOE_ERR_INVALID_ARG
 
 
 def test_residual_entry_points_validate_before_launch():
