@@ -141,7 +141,7 @@ def cpu_baseline(sp, inp, target_s=15.0):
                       f"{bwd_label(sp)}; {el:.1f} s"}
 
 
-def small_batch_latency(B, torch, sp, inp, dt, stream, sizes=(1, 16, 64), iters=50):
+def small_batch_latency(B, torch, sp, inp, dt, stream, sizes=(1, 16, 64), iters=50, packed=None):
     """Latency of moe_layer_forward for a few tokens with the workload's
     weights, through the one-launch small-batch kernel and through the
     multi-kernel path, with the bytes the fused kernel must read (the chosen
@@ -156,7 +156,8 @@ def small_batch_latency(B, torch, sp, inp, dt, stream, sizes=(1, 16, 64), iters=
                  hold (a call's two experts at one token are 84 MB at the
                  headline shape; the last three calls' fill the cache).
     The HBM fraction is taken from the cold time, with the mean bytes of the
-    calls (each call's own experts)."""
+    calls (each call's own experts).  packed: (w1, w2) in the packed layout,
+    which the calls then read (as the timed forward does)."""
     dev = inp["x"].device
     T0, d, E, k, h = sp["T"], sp["d"], sp["E"], sp["k"], sp["h"]
     esz = 2 if dt == B.MOE_BF16 else 4
@@ -168,7 +169,9 @@ def small_batch_latency(B, torch, sp, inp, dt, stream, sizes=(1, 16, 64), iters=
         row = {}
         touched_sum = 0
         for mode, name in ((1, "fused"), (-1, "multi_kernel")):
-            cfg = B.make_config(T, d, E, k, sp["cf"], sp["min_cap"], sp["drop"], h, sp["act"], dt, small_batch=mode)
+            cfg = B.make_config(T, d, E, k, sp["cf"], sp["min_cap"], sp["drop"], h, sp["act"], dt, small_batch=mode,
+                                packed_weights=packed is not None)
+            w1, w2 = packed if packed is not None else (inp["w1"], inp["w2"])
             ws = torch.empty(B.moe_workspace_size(cfg), dtype=torch.uint8, device=dev)
             out = torch.empty(T, d, dtype=inp["x"].dtype, device=dev)
             loss = torch.empty(1, dtype=torch.float32, device=dev)
@@ -176,7 +179,7 @@ def small_batch_latency(B, torch, sp, inp, dt, stream, sizes=(1, 16, 64), iters=
 
             def call(i, c):
                 x = inp["x"][i * T:(i + 1) * T]
-                B.moe_layer_forward(cfg, x, inp["w_router"], inp["b_router"], None, inp["w1"], inp["b1"], inp["w2"],
+                B.moe_layer_forward(cfg, x, inp["w_router"], inp["b_router"], None, w1, inp["b1"], w2,
                                     inp["b2"], out, loss, c, ws=ws, stream=stream)
             for cold in (False, True):
                 for i in range(5):
@@ -239,15 +242,32 @@ def main(argv=None):
     esz = 2 if dt == B.MOE_BF16 else 4
     rnd = dict(noisy_gate_policy=B.MOE_NOISE_JITTER, second_expert_sampling=True, seed=12345) \
         if sp.get("random_gate") else {}
+    # Inference workloads keep the expert weights packed (moe_pack_expert_weight, once, before timing, as a
+    # server does after loading them); training workloads (backward, random gate) read the nn.Linear layout.
+    packable = (not sp.get("backward") and not sp.get("random_gate") and dt == B.MOE_BF16)
+    if packable:
+        try:
+            B.moe_workspace_size(B.make_config(T, d, E, k, sp["cf"], sp["min_cap"], sp["drop"], h, sp["act"], dt,
+                                               use_residual=bool(sp.get("residual")), packed_weights=True))
+        except B.MoeError:
+            packable = False
+    cfg_lin = B.make_config(T, d, E, k, sp["cf"], sp["min_cap"], sp["drop"], h, sp["act"], dt,
+                            save_preact=bool(sp.get("backward")), use_residual=bool(sp.get("residual")), **rnd)
     cfg = B.make_config(T, d, E, k, sp["cf"], sp["min_cap"], sp["drop"], h, sp["act"], dt,
-                        save_preact=bool(sp.get("backward")), use_residual=bool(sp.get("residual")), **rnd)
+                        save_preact=bool(sp.get("backward")), use_residual=bool(sp.get("residual")),
+                        packed_weights=packable, **rnd)
+    if packable:
+        wp = (B.pack_expert_weight(inp["w1"]), B.pack_expert_weight(inp["w2"]) if h else None)
+    else:
+        wp = (inp["w1"], inp["w2"])
     ws = torch.empty(B.moe_workspace_size(cfg), dtype=torch.uint8, device=dev)
     out = torch.empty_like(inp["x"])
     loss = torch.empty(1, dtype=torch.float32, device=dev)
     count = torch.empty(E, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
     if a.small_batch_only:
-        print(json.dumps(small_batch_latency(B, torch, sp, inp, dt, stream)), flush=True)
+        print(json.dumps(small_batch_latency(B, torch, sp, inp, dt, stream, packed=wp if packable else None)),
+              flush=True)
         return 0
 
     bwd = bool(sp.get("backward"))
@@ -278,28 +298,33 @@ def main(argv=None):
 
     res = bool(sp.get("residual"))
 
-    def step():
+    def step(c=cfg, w=wp):
         if res:
-            B.moe_residual_layer_forward(cfg, inp["x"], inp["w_router"], inp["b_router"], inp["logits"], inp["w1"],
-                                         inp["b1"], inp["w2"], inp["b2"], inp["mlp_w1"], inp["mlp_b1"],
+            B.moe_residual_layer_forward(c, inp["x"], inp["w_router"], inp["b_router"], inp["logits"], w[0],
+                                         inp["b1"], w[1], inp["b2"], inp["mlp_w1"], inp["mlp_b1"],
                                          inp["mlp_w2"], inp["mlp_b2"], inp["coef_w"], inp["coef_b"], out, loss,
                                          count, ws=ws, stream=stream)
         else:
-            B.moe_layer_forward(cfg, inp["x"], inp["w_router"], inp["b_router"], inp["logits"], inp["w1"],
-                                inp["b1"], inp["w2"], inp["b2"], out, loss, count, ws=ws, stream=stream)
+            B.moe_layer_forward(c, inp["x"], inp["w_router"], inp["b_router"], inp["logits"], w[0],
+                                inp["b1"], w[1], inp["b2"], out, loss, count, ws=ws, stream=stream)
         if bwd:
             backward()
 
-    for _ in range(a.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(a.steps):
-        step()
-    torch.cuda.synchronize()
-    el = time.perf_counter() - t0
+    def timed(*args):
+        for _ in range(a.warmup):
+            step(*args)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(a.steps):
+            step(*args)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
+    el = timed()
     ms_step = el / a.steps * 1e3
     value = T * a.steps / el
+    # the same forward on the nn.Linear weight layout (context for the packed figure)
+    el_lin = timed(cfg_lin, (inp["w1"], inp["w2"])) if packable else el
 
     # ---- per-stage breakdown: the same kernels called stage by stage, HIP
     # events recorded on the stream they run on
@@ -328,7 +353,7 @@ def main(argv=None):
         ev[1].record(stream)
         B.moe_dispatch(cfg, inp["x"], g["idx"], g["slot"], g["offset"], xd, stream=stream)
         ev[2].record(stream)
-        B.moe_expert_ffn(cfg, xd, g["offset"], inp["w1"], inp["b1"], inp["w2"], inp["b2"], a_p if bwd else None,
+        B.moe_expert_ffn(cfg, xd, g["offset"], wp[0], inp["b1"], wp[1], inp["b2"], a_p if bwd else None,
                          hd_p, yd_p, ws, stream=stream, h_ld=h_ld)
         ev[3].record(stream)
         B.moe_combine(cfg, yd_p, g["idx"], g["slot"], g["weight"], g["offset"], out, stream=stream)
@@ -432,10 +457,14 @@ def main(argv=None):
             "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
             "dtype": sp["dtype"], "data": "synthetic",
             "config": {"workload": describe(sp) + bwd_label(sp).replace(",", " +"),
-                       "tokens_per_step": T, "rows_kept": N},
+                       "tokens_per_step": T, "rows_kept": N,
+                       "expert_weights": ("packed (moe_pack_expert_weight, once before timing)" if packable
+                                          else "nn.Linear [E, out, in]")},
             "roofline": roofline, "stages": stages}
+    if packable:
+        line["nn_linear_weights"] = {"value": T * a.steps / el_lin, "ms_per_step": el_lin / a.steps * 1e3}
     if not a.no_small_batch and not bwd and not res and not sp.get("random_gate") and sp["h"] and dt == B.MOE_BF16:
-        line["small_batch"] = small_batch_latency(B, torch, sp, inp, dt, stream)
+        line["small_batch"] = small_batch_latency(B, torch, sp, inp, dt, stream, packed=wp if packable else None)
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(sp, inp)
     print(json.dumps(line), flush=True)
