@@ -35,7 +35,9 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-GEMM_SRC = os.path.join(ROOT, "mixture_experts_layer_39_amd", "csrc", "grouped_gemm.hip")
+# the expert GEMM's sources (the kernel, and the header holding its GELU)
+GEMM_SRC = tuple(os.path.join(ROOT, "mixture_experts_layer_39_amd", "csrc", f)
+                 for f in ("grouped_gemm.hip", "moe_internal.h"))
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -46,9 +48,12 @@ def describe(sp):
     return f"{sp['name']}: T={sp['T']} d={sp['d']} E={sp['E']} top-{sp['k']} FFN {ffn}, {drop}, {sp['dtype']}"
 
 
-def source_hash(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def source_hash(paths):
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def load_traffic(workload):
