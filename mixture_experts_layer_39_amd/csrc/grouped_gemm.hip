@@ -389,16 +389,18 @@ struct BigCtx {
   uint32_t kstride;             // K-contiguous: bytes between consecutive 64-wide K steps
 };
 
+// slice >= 0: features 64*slice .. +63 of the tile only (K-contiguous
+// feature operand, token-row tiles).
 template <int TOK, int FEAT, int MODE>
 __device__ __forceinline__ BigTile big_tile_desc(const BigArgs& a, const BigCtx& c, int tile, const int* s_pref,
-                                                 int ntf) {
+                                                 int ntf, int slice = -1) {
   using namespace big;
   const TileCoord tc = tile_coord(tile, s_pref, a.E, ntf);
   BigTile t;
   t.e = tc.e;
   t.row0 = a.offset[tc.e];
   const int rows = a.offset[tc.e + 1] - t.row0;
-  t.n0 = tc.nf * BF;
+  t.n0 = tc.nf * BF + (slice > 0 ? slice * 64 : 0);
   if constexpr (MODE == BM_WGRAD) {
     t.mbase = tc.mt * BT;
     t.mvalid = min(BT, a.M - t.mbase);
@@ -415,12 +417,16 @@ __device__ __forceinline__ BigTile big_tile_desc(const BigArgs& a, const BigCtx&
   // prefix of that list
   t.nbw = nvb > c.wt ? min(4, (nvb - c.wt + 1) >> 1) : 0;
   if (c.wave >= 2) {
-    const int ncols = min(BF, a.N - t.n0);
+    const int ncols = min(slice >= 0 ? 64 : BF, a.N - t.n0);
     if constexpr (FEAT == OP_KC) {
-      const bf16* p = a.feat + (int64_t)tc.e * a.feat_estride + (int64_t)t.n0 * a.feat_ld;
       // packed: the tile's K steps are consecutive 32 KB blocks whose rows
-      // past N are zero, so the descriptor covers all of them
-      t.lr = make_rsrc(p, a.feat_packed ? (uint32_t)(a.K / 64) * (256u * 128u) : (uint32_t)ncols * c.ld_bytes);
+      // past N are zero, so the descriptor covers all of them (from the
+      // slice's first row on)
+      const int64_t off = a.feat_packed ? (int64_t)(t.n0 - tc.nf * BF) * 64 + (int64_t)tc.nf * BF * a.feat_ld
+                                        : (int64_t)t.n0 * a.feat_ld;
+      const bf16* p = a.feat + (int64_t)tc.e * a.feat_estride + off;
+      t.lr = make_rsrc(p, a.feat_packed ? (uint32_t)(a.K / 64) * (256u * 128u) - (uint32_t)(t.n0 - tc.nf * BF) * 128u
+                                        : (uint32_t)ncols * c.ld_bytes);
     } else {
       const int krows = MODE == BM_WGRAD ? rows : a.K;
       const bf16* p = a.feat + (int64_t)tc.e * a.feat_estride + (MODE == BM_WGRAD ? (int64_t)t.row0 * a.feat_ld : 0) +
@@ -448,14 +454,19 @@ __device__ __forceinline__ BigTile big_tile_desc(const BigArgs& a, const BigCtx&
 // the K step's 32 KB block of the tile) in the scalar offset.
 // Transposed: K rows 2i, 2i+1 of this wave's 32, 512 bytes each; the K row
 // goes in the per-lane offset (K rows past the end read as zero).
-__device__ __forceinline__ void big_issue_one(const BigCtx& c, __amdgpu_buffer_rsrc_t lr, int stage, int kstep, int i) {
+// nfw: 32-feature blocks per feature-side wave (4, or 1 in a 64-feature
+// slice, whose waves load 4 instructions each).
+__device__ __forceinline__ void big_issue_one(const BigCtx& c, __amdgpu_buffer_rsrc_t lr, int stage, int kstep, int i,
+                                              int nfw = 4) {
   using namespace big;
   // both layouts put load i of this wave at the same LDS offset: 16 KB per
-  // wave, 1 KB per instruction (8 rows x 128 B, or 2 K rows x 512 B)
-  unsigned char* dst = c.smem + stage * STAGE + c.lds_op + (c.wave & 1) * 16384 + i * 1024;
+  // wave (4 KB per wave in a slice), 1 KB per instruction (8 rows x 128 B,
+  // or 2 K rows x 512 B)
+  const bool fw = c.wave >= 2;
+  unsigned char* dst = c.smem + stage * STAGE + c.lds_op + (c.wave & 1) * (fw ? 4096 * nfw : 16384) + i * 1024;
   // wave-uniform row offset and K offset, chosen without a branch
-  const uint32_t g = c.wave >= 2 ? (uint32_t)((i >> 2) * 32 + (i & 3) * 4) : (uint32_t)(i * 8);
-  const uint32_t kc_row = c.sbase + g * c.ld_bytes;
+  const uint32_t g = fw ? (uint32_t)((i >> 2) * 32 + (i & 3) * 4) : (uint32_t)(i * 8);
+  const uint32_t kc_row = (fw ? (uint32_t)(c.wave & 1) * 32u * (uint32_t)nfw * c.ld_bytes : c.sbase) + g * c.ld_bytes;
   const uint32_t tr_row = (uint32_t)(kstep * 64 + (c.wave & 1) * 32 + 2 * i) * c.ld_bytes;
   const uint32_t vrow = c.tr ? tr_row : kc_row;
   const uint32_t soff = c.tr ? 0u : (uint32_t)kstep * c.kstride;
@@ -463,9 +474,11 @@ __device__ __forceinline__ void big_issue_one(const BigCtx& c, __amdgpu_buffer_r
                                            ((i & 1) ? c.vbase_o : c.vbase_e) + vrow, soff, 0, 0);
 }
 
+template <int NF = 4>
 __device__ __forceinline__ void big_issue(const BigCtx& c, __amdgpu_buffer_rsrc_t lr, int stage, int kstep) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) big_issue_one(c, lr, stage, kstep, i);
+  for (int i = 0; i < 16; ++i)
+    if (c.wave < 2 || i < 4 * NF) big_issue_one(c, lr, stage, kstep, i, NF);
 }
 
 // This tile's bias (zero without one) into LDS for the epilogue.
@@ -484,13 +497,13 @@ __device__ __forceinline__ float agpr_read(float v) {
 }
 
 // The accumulator block blk = ff*4 + tt, read out of its AGPRs (constant
-// indices inside each case; blocks with tt >= NB do not exist).
-template <int NB>
-__device__ __forceinline__ void acc_block(const f32x16 (&acc)[4][4], int blk, float (&v)[16]) {
+// indices inside each case; blocks with tt >= NB or ff >= NF do not exist).
+template <int NB, int NF>
+__device__ __forceinline__ void acc_block(const f32x16 (&acc)[NF][4], int blk, float (&v)[16]) {
   switch (blk) {
 #define MOE_AB(FF, TT)                                              \
   case FF * 4 + TT:                                                 \
-    if constexpr (TT < NB) {                                        \
+    if constexpr (TT < NB && FF < NF) {                             \
       _Pragma("unroll") for (int r = 0; r < 16; ++r) v[r] = agpr_read(acc[FF][TT][r]); \
     }                                                               \
     break;
@@ -601,24 +614,27 @@ __device__ __forceinline__ bf16x8 tr_frag(const unsigned char* tile, int i, int 
   return __builtin_bit_cast(bf16x8, r);
 }
 
-// One wave's share of a tile with NB valid 32-row token blocks (NB in 0..4):
-// every wave runs the same K steps and barriers; MFMAs of absent blocks are
-// not issued at all.  Accumulators live only inside this function.  K step s
-// of this tile sits in stage (s + sb) & 1; its step 0 was issued before the
-// call.  If there is a next tile, its step 0 is issued into the stage this
-// tile's step nk-2 used (the other stage when nk == 1), which is stage 0 of
-// the next tile's numbering with sb' = (sb + nk) & 1.
-template <int NB, int EPI, int ACT, int TOK, int FEAT, int MODE>
+// One wave's share of a tile with NB valid 32-row token blocks (NB in 0..4)
+// and NF 32-feature blocks (4; 1 in a 64-feature slice): every wave runs the
+// same K steps and barriers; MFMAs of absent blocks are not issued at all,
+// and each 32x32 block sees the same MFMA sequence whatever NB and NF.
+// Accumulators live only inside this function.  K step s of this tile sits
+// in stage (s + sb) & 1; its step 0 was issued before the call unless
+// `cold`.  If there is a next tile (always a whole one), its step 0 is
+// issued into the stage this tile's step nk-2 used (the other stage when
+// nk == 1), which is stage 0 of the next tile's numbering with
+// sb' = (sb + nk) & 1.
+template <int NB, int NF, int EPI, int ACT, int TOK, int FEAT, int MODE>
 __device__ __forceinline__ void big_tile(const BigArgs& a, const BigCtx& c, const BigTile& t, int sb, bool has_next,
-                                         __amdgpu_buffer_rsrc_t next_lr, const float* s_bias) {
+                                         __amdgpu_buffer_rsrc_t next_lr, const float* s_bias, bool cold) {
   using namespace big;
   unsigned char* smem = c.smem;
   const int nk = t.nk, wt = c.wt, wf = c.wf, h = c.h, r32 = c.r32;
   const int N = a.N;
   const int lane = threadIdx.x & 63, lane16 = lane & 15, mh = (lane >> 4) & 1, q4 = lane & 3;
-  f32x16 acc[4][4];
+  f32x16 acc[NF][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NF; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -628,9 +644,9 @@ __device__ __forceinline__ void big_tile(const BigArgs& a, const BigCtx& c, cons
   // (about 1000 cycles) ahead of their use.  Sub-step i of a 64-wide K step
   // covers, for lane half h, the 8 K values of chunk h*4+i (the same order
   // on both operands, which leaves the dot product alone).
-  bf16x8 fa[4][4], fb[4][NB > 0 ? NB : 1];
-  constexpr int NM = 4 * NB;       // MFMAs per sub-step
-  constexpr int NR = 4 + NB;       // fragment reads per sub-step
+  bf16x8 fa[4][NF], fb[4][NB > 0 ? NB : 1];
+  constexpr int NM = NF * NB;      // MFMAs per sub-step
+  constexpr int NR = NF + NB;      // fragment reads per sub-step
   // transposed-read source columns of this lane within a 32-wide block: the
   // token side reads columns in order, the feature side in the permuted order
   // that gives each lane 16 consecutive output features
@@ -643,8 +659,8 @@ __device__ __forceinline__ void big_tile(const BigArgs& a, const BigCtx& c, cons
     const unsigned char* Xs = smem + stage * STAGE;
     const unsigned char* Ws = Xs + TILE_BYTES;
     const int sw = (((h * 4 + i) ^ ((r32 >> 1) & 7)) * 16);
-    const bool tokr = NB > 0 && (r == 0 || r >= 5);
-    const int tt = r == 0 ? 0 : r - 4;
+    const bool tokr = NB > 0 && (r == 0 || r >= NF + 1);
+    const int tt = r == 0 ? 0 : r - NF;
     const int ff = NB > 0 ? r - 1 : r;
     if (tokr) {
       if constexpr (TOK == OP_KC)
@@ -653,14 +669,14 @@ __device__ __forceinline__ void big_tile(const BigArgs& a, const BigCtx& c, cons
         fb[set][tt] = tr_frag(Xs, i, h, lane16, (wt + 2 * tt) * 32 + tok_col);
     } else {
       if constexpr (FEAT == OP_KC)
-        fa[set][ff] = *reinterpret_cast<const bf16x8*>(Ws + (wf * 128 + ff * 32 + r32) * BKB + sw);
+        fa[set][ff] = *reinterpret_cast<const bf16x8*>(Ws + (wf * 32 * NF + ff * 32 + r32) * BKB + sw);
       else
-        fa[set][ff] = tr_frag(Ws, i, h, lane16, wf * 128 + ff * 32 + feat_col);
+        fa[set][ff] = tr_frag(Ws, i, h, lane16, wf * 32 * NF + ff * 32 + feat_col);
     }
   };
-  // MFMA j of a sub-step: token block j / 4 with feature block j % 4
+  // MFMA j of a sub-step: token block j / NF with feature block j % NF
   auto mfma1 = [&](int set, int j) {
-    const int tt = j >> 2, ff = j & 3;
+    const int tt = j / NF, ff = j % NF;
     acc[ff][tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][ff], fb[set][tt], acc[ff][tt], 0, 0, 0);
   };
   // One sub-step in a fixed issue order: each MFMA is followed by its share
@@ -679,11 +695,12 @@ __device__ __forceinline__ void big_tile(const BigArgs& a, const BigCtx& c, cons
         if constexpr (NM > 0) {
 #pragma unroll
           for (int q = j * 8 / NM; q < (j + 1) * 8 / NM && j < NM; ++q)
-            big_issue_one(c, llr, lstage, lkstep, lhalf * 8 + q);
+            if (c.wave < 2 || lhalf * 8 + q < 4 * NF) big_issue_one(c, llr, lstage, lkstep, lhalf * 8 + q, NF);
         } else {
           if (j == 0) {
 #pragma unroll
-            for (int q = 0; q < 8; ++q) big_issue_one(c, llr, lstage, lkstep, lhalf * 8 + q);
+            for (int q = 0; q < 8; ++q)
+              if (c.wave < 2 || lhalf * 8 + q < 4 * NF) big_issue_one(c, llr, lstage, lkstep, lhalf * 8 + q, NF);
           }
         }
       }
@@ -705,10 +722,11 @@ __device__ __forceinline__ void big_tile(const BigArgs& a, const BigCtx& c, cons
   // this tile, else step 0 of the next tile, else nothing (a descriptor with
   // no records: the loads return zeros and touch no memory).
   const __amdgpu_buffer_rsrc_t tail_lr = has_next ? next_lr : no_lr;
+  if (cold) big_issue<NF>(c, t.lr, sb & 1, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_s_barrier();
-  if (nk > 1) big_issue(c, t.lr, (sb + 1) & 1, 1);
-  else big_issue(c, tail_lr, (sb + 1) & 1, 0);
+  if (nk > 1) big_issue<NF>(c, t.lr, (sb + 1) & 1, 1);
+  else big_issue<NF>(c, tail_lr, (sb + 1) & 1, 0);
 #pragma unroll
   for (int r = 0; r < NR; ++r) read1(sb, 0, 0, r);
   __builtin_amdgcn_sched_barrier(0);
@@ -737,13 +755,13 @@ __device__ __forceinline__ void big_tile(const BigArgs& a, const BigCtx& c, cons
   // one compact loop over the accumulator blocks keeps the epilogue small
   // enough to stay in the instruction cache
 #pragma nounroll
-  for (int blk = 0; blk < 16; ++blk) {
+  for (int blk = 0; blk < 4 * NF; ++blk) {
     const int ff = blk >> 2, tt = blk & 3;
     const int rloc = (wt + 2 * tt) * 32 + r32;
-    const int fl = wf * 128 + ff * 32 + h * 16;   // column offset within the tile
+    const int fl = wf * 32 * NF + ff * 32 + h * 16;   // column offset within the tile
     if (tt >= NB || t.n0 + fl >= N) continue;
     float v[16];
-    acc_block<NB>(acc, blk, v);
+    acc_block<NB, NF>(acc, blk, v);
     if (rloc < t.mvalid) big_store<EPI, ACT, MODE>(a, v, t, rloc, fl, s_bias);
   }
 }
@@ -762,14 +780,31 @@ void gemm_bf16_big_kernel(BigArgs a) {
   big_prefix<MODE>(a.offset, E, mtw, s_pref);
   __syncthreads();
   const int total = s_pref[E] * ntf;
-  // this XCD's contiguous share of the tiles, walked with stride L by its L
-  // workgroups (XCDs take workgroups round-robin)
-  const int per_xcd = gridDim.x / kXcds;
-  const int share = (total + kXcds - 1) / kXcds;
+  // Tail split (forward token-row tiles): when the tiles leave a last round
+  // that at most a quarter of the workgroups would run (R = total mod G of
+  // them), every workgroup runs exactly floor(total / G) whole tiles and the
+  // R leftover tiles run as four 64-feature slices each, on four workgroups
+  // of the leftover tile's XCD, after their whole tiles.  A slice gives the
+  // same bits as the whole tile (each 32x32 block, the same MFMA sequence).
+  const int G = gridDim.x;
+  int R = 0;
+  if constexpr (MODE == BM_ROWS && FEAT == OP_KC) {
+    // the slice map below needs 4 * ceil(R / 8) workgroups per XCD
+    if (total > G && (total % G) * 4 <= G && ((total % G + kXcds - 1) / kXcds) * 4 <= G / kXcds) R = total % G;
+  }
+  const int F = total - R;   // whole tiles
+  // this XCD's contiguous share of the whole tiles, walked with stride L by
+  // its L workgroups (XCDs take workgroups round-robin)
+  const int per_xcd = G / kXcds;
+  const int share = (F + kXcds - 1) / kXcds;
   const int xcd = blockIdx.x % kXcds;
-  const int t_end = min(total, (xcd + 1) * share);
-  int tile = xcd * share + (int)blockIdx.x / kXcds;
-  if (tile >= t_end) return;
+  const int loc = (int)blockIdx.x / kXcds;
+  const int t_end = min(F, (xcd + 1) * share);
+  int tile = xcd * share + loc;
+  // this workgroup's slice: leftover tile (loc / 4) * 8 + xcd, slice loc % 4
+  const int slice_tile = (loc / 4) * kXcds + xcd;
+  const bool has_slice = slice_tile < R;
+  if (tile >= t_end && !has_slice) return;
 
   // the wave index is uniform across the wave; say so, so that descriptor
   // and LDS-base choices below stay in scalar registers
@@ -818,28 +853,48 @@ void gemm_bf16_big_kernel(BigArgs a) {
     c.sbase = 0;
   }
 
-  BigTile cur = big_tile_desc<TOK, FEAT, MODE>(a, c, tile, s_pref, ntf);
-  big_issue(c, cur.lr, 0, 0);
-  if constexpr (EPI == BE_ACT) big_bias(a, cur, s_bias[0]);
   int sb = 0, par = 0;
-  for (;;) {
-    const int next = tile + per_xcd;
-    const bool has_next = next < t_end;
-    BigTile nt = cur;
-    if (has_next) nt = big_tile_desc<TOK, FEAT, MODE>(a, c, next, s_pref, ntf);
-    switch (cur.nbw) {
-      case 4: big_tile<4, EPI, ACT, TOK, FEAT, MODE>(a, c, cur, sb, has_next, nt.lr, s_bias[par]); break;
-      case 3: big_tile<3, EPI, ACT, TOK, FEAT, MODE>(a, c, cur, sb, has_next, nt.lr, s_bias[par]); break;
-      case 2: big_tile<2, EPI, ACT, TOK, FEAT, MODE>(a, c, cur, sb, has_next, nt.lr, s_bias[par]); break;
-      case 1: big_tile<1, EPI, ACT, TOK, FEAT, MODE>(a, c, cur, sb, has_next, nt.lr, s_bias[par]); break;
-      default: big_tile<0, EPI, ACT, TOK, FEAT, MODE>(a, c, cur, sb, has_next, nt.lr, s_bias[par]); break;
+  if (tile < t_end) {
+    BigTile cur = big_tile_desc<TOK, FEAT, MODE>(a, c, tile, s_pref, ntf);
+    big_issue(c, cur.lr, 0, 0);
+    if constexpr (EPI == BE_ACT) big_bias(a, cur, s_bias[0]);
+    for (;;) {
+      const int next = tile + per_xcd;
+      const bool has_next = next < t_end;
+      BigTile nt = cur;
+      if (has_next) nt = big_tile_desc<TOK, FEAT, MODE>(a, c, next, s_pref, ntf);
+      switch (cur.nbw) {
+        case 4: big_tile<4, 4, EPI, ACT, TOK, FEAT, MODE>(a, c, cur, sb, has_next, nt.lr, s_bias[par], false); break;
+        case 3: big_tile<3, 4, EPI, ACT, TOK, FEAT, MODE>(a, c, cur, sb, has_next, nt.lr, s_bias[par], false); break;
+        case 2: big_tile<2, 4, EPI, ACT, TOK, FEAT, MODE>(a, c, cur, sb, has_next, nt.lr, s_bias[par], false); break;
+        case 1: big_tile<1, 4, EPI, ACT, TOK, FEAT, MODE>(a, c, cur, sb, has_next, nt.lr, s_bias[par], false); break;
+        default: big_tile<0, 4, EPI, ACT, TOK, FEAT, MODE>(a, c, cur, sb, has_next, nt.lr, s_bias[par], false); break;
+      }
+      // the next tile's numbering starts at the stage this tile's step nk-2
+      // used, whose last reads came before this tile's last barrier
+      sb = (sb + cur.nk) & 1;
+      par ^= 1;
+      if (!has_next) break;
+      if constexpr (EPI == BE_ACT) big_bias(a, nt, s_bias[par]);   // visible after the next tile's first barrier
+      cur = nt;
+      tile = next;
     }
-    if (!has_next) break;
-    sb = (sb + cur.nk) & 1;
-    par ^= 1;
-    if constexpr (EPI == BE_ACT) big_bias(a, nt, s_bias[par]);   // visible after the next tile's first barrier
-    cur = nt;
-    tile = next;
+  }
+  if constexpr (MODE == BM_ROWS && FEAT == OP_KC) {
+    if (has_slice) {
+      const BigTile st = big_tile_desc<TOK, FEAT, MODE>(a, c, F + slice_tile, s_pref, ntf, loc % 4);
+      if (st.n0 < a.N) {   // uniform: the slice's first feature
+        if constexpr (EPI == BE_ACT) big_bias(a, st, s_bias[par]);   // visible after the slice's first barrier
+        const __amdgpu_buffer_rsrc_t none = make_rsrc(a.tok, 0);
+        switch (st.nbw) {
+          case 4: big_tile<4, 1, EPI, ACT, TOK, FEAT, MODE>(a, c, st, sb, false, none, s_bias[par], true); break;
+          case 3: big_tile<3, 1, EPI, ACT, TOK, FEAT, MODE>(a, c, st, sb, false, none, s_bias[par], true); break;
+          case 2: big_tile<2, 1, EPI, ACT, TOK, FEAT, MODE>(a, c, st, sb, false, none, s_bias[par], true); break;
+          case 1: big_tile<1, 1, EPI, ACT, TOK, FEAT, MODE>(a, c, st, sb, false, none, s_bias[par], true); break;
+          default: big_tile<0, 1, EPI, ACT, TOK, FEAT, MODE>(a, c, st, sb, false, none, s_bias[par], true); break;
+        }
+      }
+    }
   }
 }
 

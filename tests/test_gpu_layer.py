@@ -195,6 +195,53 @@ def test_token_output_independent_of_the_batch():
         assert torch.equal(small[0][key], big[0][key][:n]), key
 
 
+def _tail_split_runs(G):
+    """Tokens routed (given logits, k = 1, no drop) to 8 experts in blocks of
+    8192, so that each expert has 32 row tiles of 256 rows; the second batch
+    puts 8 more tokens for expert 7 in front, which gives it a 33rd tile.
+    With d = 256 (one feature tile in Linear 2) and h = 2048 (eight in
+    Linear 1) the second batch has 257 and 2056 tiles: on 256 workgroups
+    each GEMM's last round (1 and 8 tiles) runs as 64-feature slices, and
+    the last tile of expert 7 holds tokens of the first batch."""
+    E, d, h, per = 8, 256, 2048, 8192
+    g = torch.Generator(device=DEV)
+    g.manual_seed(4242)
+    T = E * per
+    x = (torch.randn(T + 8, d, generator=g, device=DEV)).to(torch.bfloat16)
+    choice = torch.cat([torch.full((8,), E - 1), torch.arange(T) // per]).to(DEV)
+    logits = torch.randn(T + 8, E, generator=g, device=DEV) * 0.1
+    logits[torch.arange(T + 8, device=DEV), choice] += 8.0
+    w = dict(w1=(torch.randn(E, h, d, generator=g, device=DEV) * 0.02).to(torch.bfloat16),
+             b1=(torch.randn(E, h, generator=g, device=DEV) * 0.02).to(torch.bfloat16),
+             w2=(torch.randn(E, d, h, generator=g, device=DEV) * 0.02).to(torch.bfloat16),
+             b2=(torch.randn(E, d, generator=g, device=DEV) * 0.02).to(torch.bfloat16))
+    outs = []
+    for lo in (8, 0):   # the plain batch, then the one with the extra tokens in front
+        n = T + 8 - lo
+        cfg = B.make_config(n, d, E, 1, 1.0, 0, False, h, B.MOE_ACT_GELU, B.MOE_BF16, small_batch=-1)
+        ws = workspace(cfg, DEV)
+        out = torch.empty(n, d, dtype=torch.bfloat16, device=DEV)
+        loss = torch.empty(1, dtype=torch.float32, device=DEV)
+        count = torch.empty(E, dtype=torch.int32, device=DEV)
+        B.moe_layer_forward(cfg, x[lo:], None, None, logits[lo:].contiguous(), w["w1"], w["b1"], w["w2"], w["b2"],
+                            out, loss, count, ws=ws)
+        outs.append((out, count))
+    torch.cuda.synchronize()
+    return outs
+
+
+def test_gemm_tail_slices_match_whole_tiles():
+    """The expert GEMMs split a short last round of tiles into 64-feature
+    slices; a token's output rows must not depend on whether its tile ran
+    whole or as slices."""
+    G = torch.cuda.get_device_properties(0).multi_processor_count // 8 * 8
+    if not (257 > G and (257 % G) * 4 <= G):
+        pytest.skip(f"{G} workgroups: 257 tiles leave no short last round on this device")
+    (plain, c0), (extra, c1) = _tail_split_runs(G)
+    assert int(c1[7]) == 8200 and int(c0[7]) == 8192
+    assert torch.equal(plain, extra[8:])
+
+
 FULL = ["top2_e8", "top2_e64", "skew_e16", "nodrop_e128"]
 
 
