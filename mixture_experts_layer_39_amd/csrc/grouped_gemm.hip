@@ -782,15 +782,17 @@ void gemm_bf16_big_kernel(BigArgs a) {
   const int total = s_pref[E] * ntf;
   // Tail split (forward token-row tiles): when the tiles leave a last round
   // that at most a quarter of the workgroups would run (R = total mod G of
-  // them), every workgroup runs exactly floor(total / G) whole tiles and the
-  // R leftover tiles run as four 64-feature slices each, on four workgroups
-  // of the leftover tile's XCD, after their whole tiles.  A slice gives the
-  // same bits as the whole tile (each 32x32 block, the same MFMA sequence).
+  // them; or all tiles, when there are at most G / 4), every workgroup runs
+  // exactly floor(total / G) whole tiles and the R leftover tiles run as
+  // four 64-feature slices each, on four workgroups of the leftover tile's
+  // XCD, after their whole tiles.  A slice gives the same bits as the whole
+  // tile (each 32x32 block, the same MFMA sequence).
   const int G = gridDim.x;
   int R = 0;
   if constexpr (MODE == BM_ROWS && FEAT == OP_KC) {
     // the slice map below needs 4 * ceil(R / 8) workgroups per XCD
-    if (total > G && (total % G) * 4 <= G && ((total % G + kXcds - 1) / kXcds) * 4 <= G / kXcds) R = total % G;
+    const int r = total % G;
+    if ((total > G || total * 4 <= G) && r * 4 <= G && ((r + kXcds - 1) / kXcds) * 4 <= G / kXcds) R = r;
   }
   const int F = total - R;   // whole tiles
   // this XCD's contiguous share of the whole tiles, walked with stride L by
@@ -968,11 +970,13 @@ hipError_t launch_big(const BigArgs& a, hipStream_t s) {
                                      hipFuncAttributeMaxDynamicSharedMemorySize, big::LDS);
   if (e != hipSuccess) return e;
   // at most one workgroup per CU (LDS use allows no more), never more than
-  // the worst-case tile count, a whole number per XCD
+  // the worst-case tile count (four slices per tile on the forward path,
+  // which splits a short round of tiles), a whole number per XCD
   const int64_t ntf = (a.N + big::BF - 1) / big::BF;
   const int64_t mtiles = MODE == BM_WGRAD ? (int64_t)a.E * ((a.M + big::BT - 1) / big::BT)
                                           : (a.max_rows + big::BT - 1) / big::BT + a.E;
-  int64_t grid = std::min<int64_t>(mtiles * ntf, device_cus());
+  const int64_t units = (MODE == BM_ROWS && FEAT == OP_KC ? 4 : 1) * mtiles * ntf;
+  int64_t grid = std::min<int64_t>(units, device_cus());
   grid = std::max<int64_t>(kXcds, grid / kXcds * kXcds);
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), big::LDS, s, a);
   return hipGetLastError();
