@@ -459,7 +459,10 @@ moe_status moe_residual_layer_backward(const moe_config* cfg, const void* x, con
 
 /* Device addresses, inside a workspace ws, of the intermediates that
  * moe_layer_forward leaves there (valid until the next call that uses ws):
- * packed x_disp [rows, d], a_save [rows, h] (only with cfg->save_preact),
+ * packed x_disp [rows, d] (with cfg->save_preact always; without it the
+ * multi-kernel forward may skip the copy, its first Linear then loading each
+ * packed row from x through a row map kept in the workspace, and x_disp is
+ * not written), a_save [rows, h] (only with cfg->save_preact),
  * h_disp [rows, h], y_disp [rows, d] and expert_offset [E+1] int32.  The
  * rows of h_disp are contiguous with cfg->save_preact; without it the
  * forward may keep them at a pitch of h + 64 elements, in a region sized

@@ -41,7 +41,9 @@ def sources():
 # phases with grid barriers, so every workgroup must be resident at once, and
 # scratch allocation can limit how many are; a variant of it that spilled to
 # scratch also computed its second Linear wrongly (with every barrier met).
-NO_SCRATCH = {"decode.hip": ("decode_kernel",)}
+# The large-tile GEMM keeps its tile state in registers; scratch there means
+# part of it went to memory, which costs that kernel a large part of its speed.
+NO_SCRATCH = {"decode.hip": ("decode_kernel",), "grouped_gemm.hip": ("gemm_bf16_big_kernel",)}
 
 
 def _scratch_sizes(remarks):

@@ -16,6 +16,8 @@
 // T times, not k*T).  Combine is the gather form: each output row is written
 // exactly once, the fp32 sum runs in choice order with no atomics, and a
 // token whose claims were all dropped gets zeros.
+#include <algorithm>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -137,6 +139,40 @@ __global__ __launch_bounds__(256) void dispatch_finalize_kernel(const u32x4* __r
   }
 }
 
+// The dispatch as a row map, for the inference forward whose first Linear
+// gathers its token rows itself: row_tok[expert_offset[e] + slot] = t for
+// every kept claim (t, j), one thread per token; the _finalize variant also
+// turns the gate's in-tile ranks into the final slots first, as
+// dispatch_finalize_kernel does.
+__global__ __launch_bounds__(256) void row_map_finalize_kernel(GateArgs g, int32_t* __restrict__ row_tok) {
+  const int k = g.k, E = g.E;
+  const int64_t T = g.T, C = g.C;
+  for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < T; t += (int64_t)gridDim.x * 256) {
+    const int64_t tile = t / g.tile_tokens;
+    const int e0 = g.expert_idx[t * k], q0 = g.slot[t * k];
+    const int e1 = k == 2 ? g.expert_idx[t * k + 1] : 0, q1 = k == 2 ? g.slot[t * k + 1] : 0;
+    int64_t s0 = (int64_t)q0 + g.tile_cnt[(int64_t)e0 * g.num_tiles + tile];
+    int64_t s1 = k == 2 ? (int64_t)q1 + g.tile_cnt[(int64_t)(E + e1) * g.num_tiles + tile] + g.demand[e1] : -1;
+    if (C >= 0 && s0 >= C) s0 = -1;
+    if (C >= 0 && s1 >= C) s1 = -1;
+    g.slot[t * k] = (int32_t)s0;
+    if (k == 2) g.slot[t * k + 1] = (int32_t)s1;
+    if (s0 >= 0) row_tok[g.expert_offset[e0] + s0] = (int32_t)t;
+    if (s1 >= 0) row_tok[g.expert_offset[e1] + s1] = (int32_t)t;
+  }
+}
+
+__global__ __launch_bounds__(256) void row_map_kernel(const int32_t* __restrict__ expert_idx,
+                                                      const int32_t* __restrict__ slot,
+                                                      const int32_t* __restrict__ offset,
+                                                      int32_t* __restrict__ row_tok, int64_t T, int k) {
+  for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < T; t += (int64_t)gridDim.x * 256) {
+    const Claims c = token_claims<false>(expert_idx, slot, nullptr, offset, t, k);
+    if (c.r0 >= 0) row_tok[c.r0] = (int32_t)t;
+    if (c.r1 >= 0) row_tok[c.r1] = (int32_t)t;
+  }
+}
+
 template <int DT>
 __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ y,
                                                       const int32_t* __restrict__ expert_idx,
@@ -224,6 +260,21 @@ hipError_t launch_dispatch_finalize(const void* x, const GateArgs& g, void* x_di
   if (g.T == 0) return hipSuccess;
   hipLaunchKernelGGL(dispatch_finalize_kernel, dim3(row_grid(g.T)), dim3(256), 0, s, static_cast<const u32x4*>(x), g,
                      static_cast<u32x4*>(x_disp), row_bytes / 16);
+  return hipGetLastError();
+}
+
+hipError_t launch_row_map(const int32_t* expert_idx, const int32_t* slot, const int32_t* expert_offset,
+                          int32_t* row_tok, int64_t T, int k, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const unsigned grid = (unsigned)std::min<int64_t>((T + 255) / 256, 4096);
+  hipLaunchKernelGGL(row_map_kernel, dim3(grid), dim3(256), 0, s, expert_idx, slot, expert_offset, row_tok, T, k);
+  return hipGetLastError();
+}
+
+hipError_t launch_row_map_finalize(const GateArgs& g, int32_t* row_tok, hipStream_t s) {
+  if (g.T == 0) return hipSuccess;
+  const unsigned grid = (unsigned)std::min<int64_t>((g.T + 255) / 256, 4096);
+  hipLaunchKernelGGL(row_map_finalize_kernel, dim3(grid), dim3(256), 0, s, g, row_tok);
   return hipGetLastError();
 }
 

@@ -311,7 +311,10 @@ constexpr int LDS = 2 * STAGE;                 // double buffered
 constexpr int TRB = 512;                       // bytes of one K row of a transposed tile
 }  // namespace big
 
-enum { OP_KC = 0, OP_TR = 1 };          // operand layout
+// operand layout; OP_GATHER: K-contiguous token rows gathered through a
+// packed-row -> token map (the inference forward's first Linear reads x
+// itself instead of a dispatched copy)
+enum { OP_KC = 0, OP_TR = 1, OP_GATHER = 2 };
 enum { BM_ROWS = 0, BM_WGRAD = 1 };     // token-row tiles / weight-gradient tiles
 enum { BE_ACT = 0, BE_DACT = 1, BE_STORE = 2, BE_F32 = 3 };   // epilogue
 
@@ -331,6 +334,8 @@ struct BigArgs {
   int64_t y_ld, y_estride;  // output row pitch; per-expert output stride (weight gradients)
   int32_t E, N, K, M, act;  // K: contraction (token-row tiles); M: output rows (weight gradients)
   int32_t feat_packed;      // K-contiguous feature operand in packed blocks of 256 rows x 64 K
+  const int32_t* tok_map;   // OP_GATHER: token row of each packed row
+  int64_t tok_rows;         // OP_GATHER: rows of the token operand
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -376,6 +381,7 @@ struct BigTile {
   int mbase, mvalid;      // first tile row (expert-relative, or output row) and row count
   int n0, nk;             // first feature, 64-wide K steps
   int nbw;                // this wave's valid 32-row token blocks (0..4)
+  const int32_t* map;     // OP_GATHER: the token row of each tile row (tok_map from the tile's first row)
   __amdgpu_buffer_rsrc_t lr;   // the operand this wave loads (token or feature side)
 };
 
@@ -387,6 +393,7 @@ struct BigCtx {
   uint32_t vbase_e, vbase_o;    // per-lane load offsets for even / odd instructions
   uint32_t sbase, ld_bytes;     // per-wave row base; bytes between operand rows
   uint32_t kstride;             // K-contiguous: bytes between consecutive 64-wide K steps
+  uint32_t ch_e, ch_o;          // K-contiguous: this lane's chunk byte offset for even / odd instructions
 };
 
 // slice >= 0: features 64*slice .. +63 of the tile only (K-contiguous
@@ -397,6 +404,7 @@ __device__ __forceinline__ BigTile big_tile_desc(const BigArgs& a, const BigCtx&
   using namespace big;
   const TileCoord tc = tile_coord(tile, s_pref, a.E, ntf);
   BigTile t;
+  t.map = nullptr;
   t.e = tc.e;
   t.row0 = a.offset[tc.e];
   const int rows = a.offset[tc.e + 1] - t.row0;
@@ -434,7 +442,12 @@ __device__ __forceinline__ BigTile big_tile_desc(const BigArgs& a, const BigCtx&
       t.lr = make_rsrc(p, krows > 0 ? (uint32_t)(((int64_t)(krows - 1) * a.feat_ld + ncols) * 2) : 0u);
     }
   } else {
-    if constexpr (TOK == OP_KC) {
+    if constexpr (TOK == OP_GATHER) {
+      // the whole token matrix; each load's source row comes from the map
+      // (big_map_load / big_map_offsets)
+      t.lr = make_rsrc(a.tok, (uint32_t)(a.tok_rows * c.ld_bytes));
+      t.map = a.tok_map + t.row0 + t.mbase;
+    } else if constexpr (TOK == OP_KC) {
       const bf16* p = a.tok + (int64_t)(t.row0 + t.mbase) * a.tok_ld;
       t.lr = make_rsrc(p, (uint32_t)t.mvalid * c.ld_bytes);
     } else {
@@ -456,8 +469,11 @@ __device__ __forceinline__ BigTile big_tile_desc(const BigArgs& a, const BigCtx&
 // goes in the per-lane offset (K rows past the end read as zero).
 // nfw: 32-feature blocks per feature-side wave (4, or 1 in a 64-feature
 // slice, whose waves load 4 instructions each).
+// GATHER: the token waves take their per-lane byte offset from gv (load i's
+// gathered row and chunk, from big_map_offsets) instead of the tile row.
+template <bool GATHER = false>
 __device__ __forceinline__ void big_issue_one(const BigCtx& c, __amdgpu_buffer_rsrc_t lr, int stage, int kstep, int i,
-                                              int nfw = 4) {
+                                              int nfw = 4, uint32_t gv = 0) {
   using namespace big;
   // both layouts put load i of this wave at the same LDS offset: 16 KB per
   // wave (4 KB per wave in a slice), 1 KB per instruction (8 rows x 128 B,
@@ -470,15 +486,40 @@ __device__ __forceinline__ void big_issue_one(const BigCtx& c, __amdgpu_buffer_r
   const uint32_t tr_row = (uint32_t)(kstep * 64 + (c.wave & 1) * 32 + 2 * i) * c.ld_bytes;
   const uint32_t vrow = c.tr ? tr_row : kc_row;
   const uint32_t soff = c.tr ? 0u : (uint32_t)kstep * c.kstride;
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(lr, (__attribute__((address_space(3))) void*)dst, 16,
-                                           ((i & 1) ? c.vbase_o : c.vbase_e) + vrow, soff, 0, 0);
+  uint32_t voff = ((i & 1) ? c.vbase_o : c.vbase_e) + vrow;
+  if constexpr (GATHER) {
+    if (!fw) voff = gv;
+  }
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(lr, (__attribute__((address_space(3))) void*)dst, 16, voff, soff, 0, 0);
 }
 
-template <int NF = 4>
-__device__ __forceinline__ void big_issue(const BigCtx& c, __amdgpu_buffer_rsrc_t lr, int stage, int kstep) {
+template <int NF = 4, bool GATHER = false>
+__device__ __forceinline__ void big_issue(const BigCtx& c, __amdgpu_buffer_rsrc_t lr, int stage, int kstep,
+                                          const uint32_t (&gv)[16]) {
 #pragma unroll
   for (int i = 0; i < 16; ++i)
-    if (c.wave < 2 || i < 4 * NF) big_issue_one(c, lr, stage, kstep, i, NF);
+    if (c.wave < 2 || i < 4 * NF) big_issue_one<GATHER>(c, lr, stage, kstep, i, NF, gv[i]);
+}
+
+// Gathered token rows, token waves: raw[i] = the token row that load i of
+// this lane reads (tile row (wave&1)*128 + 8i + lane/8), or -1 past the
+// tile's nvalid rows; then the loads' byte offsets (row and this lane's
+// chunk; a row of -1 becomes an offset past every descriptor's end, which
+// reads zeros).  The two are separate so that the map loads can be issued
+// long before their values are needed.
+__device__ __forceinline__ void big_map_load(const BigCtx& c, const int32_t* map, int nvalid, int32_t (&raw)[16]) {
+  const int lrow = (threadIdx.x & 63) >> 3;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = (c.wave & 1) * 128 + 8 * i + lrow;
+    raw[i] = (c.wave < 2 && r < nvalid) ? map[r] : -1;
+  }
+}
+
+__device__ __forceinline__ void big_map_offsets(const BigCtx& c, const int32_t (&raw)[16], uint32_t (&gv)[16]) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    gv[i] = raw[i] < 0 ? 0xF0000000u : (uint32_t)raw[i] * c.ld_bytes + ((i & 1) ? c.ch_o : c.ch_e);
 }
 
 // This tile's bias (zero without one) into LDS for the epilogue.
@@ -626,7 +667,9 @@ __device__ __forceinline__ bf16x8 tr_frag(const unsigned char* tile, int i, int 
 // sb' = (sb + nk) & 1.
 template <int NB, int NF, int EPI, int ACT, int TOK, int FEAT, int MODE>
 __device__ __forceinline__ void big_tile(const BigArgs& a, const BigCtx& c, const BigTile& t, int sb, bool has_next,
-                                         __amdgpu_buffer_rsrc_t next_lr, const float* s_bias, bool cold) {
+                                         __amdgpu_buffer_rsrc_t next_lr, const int32_t* next_map, int next_valid,
+                                         uint32_t (&gv)[16], const float* s_bias, bool cold) {
+  constexpr bool GATHER = TOK == OP_GATHER;
   using namespace big;
   unsigned char* smem = c.smem;
   const int nk = t.nk, wt = c.wt, wf = c.wf, h = c.h, r32 = c.r32;
@@ -663,7 +706,7 @@ __device__ __forceinline__ void big_tile(const BigArgs& a, const BigCtx& c, cons
     const int tt = r == 0 ? 0 : r - NF;
     const int ff = NB > 0 ? r - 1 : r;
     if (tokr) {
-      if constexpr (TOK == OP_KC)
+      if constexpr (TOK != OP_TR)
         fb[set][tt] = *reinterpret_cast<const bf16x8*>(Xs + ((wt + 2 * tt) * 32 + r32) * BKB + sw);
       else
         fb[set][tt] = tr_frag(Xs, i, h, lane16, (wt + 2 * tt) * 32 + tok_col);
@@ -695,12 +738,16 @@ __device__ __forceinline__ void big_tile(const BigArgs& a, const BigCtx& c, cons
         if constexpr (NM > 0) {
 #pragma unroll
           for (int q = j * 8 / NM; q < (j + 1) * 8 / NM && j < NM; ++q)
-            if (c.wave < 2 || lhalf * 8 + q < 4 * NF) big_issue_one(c, llr, lstage, lkstep, lhalf * 8 + q, NF);
+            if (c.wave < 2 || lhalf * 8 + q < 4 * NF)
+              big_issue_one<GATHER>(c, llr, lstage, lkstep, lhalf * 8 + q, NF,
+                                    gv[lhalf * 8 + q]);
         } else {
           if (j == 0) {
 #pragma unroll
             for (int q = 0; q < 8; ++q)
-              if (c.wave < 2 || lhalf * 8 + q < 4 * NF) big_issue_one(c, llr, lstage, lkstep, lhalf * 8 + q, NF);
+              if (c.wave < 2 || lhalf * 8 + q < 4 * NF)
+                big_issue_one<GATHER>(c, llr, lstage, lkstep, lhalf * 8 + q, NF,
+                                      gv[lhalf * 8 + q]);
           }
         }
       }
@@ -722,11 +769,22 @@ __device__ __forceinline__ void big_tile(const BigArgs& a, const BigCtx& c, cons
   // this tile, else step 0 of the next tile, else nothing (a descriptor with
   // no records: the loads return zeros and touch no memory).
   const __amdgpu_buffer_rsrc_t tail_lr = has_next ? next_lr : no_lr;
-  if (cold) big_issue<NF>(c, t.lr, sb & 1, 0);
+  // GATHER: gv holds this tile's load offsets until the loads turn to the
+  // next tile's first K step; the next tile's map is read during the first
+  // K step, a step before the barrier that waits for it
+  int32_t nraw[16];
+  if (cold) big_issue<NF, GATHER>(c, t.lr, sb & 1, 0, gv);
   __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_s_barrier();
-  if (nk > 1) big_issue<NF>(c, t.lr, (sb + 1) & 1, 1);
-  else big_issue<NF>(c, tail_lr, (sb + 1) & 1, 0);
+  if (nk > 1) {
+    big_issue<NF, GATHER>(c, t.lr, (sb + 1) & 1, 1, gv);
+  } else {
+    if constexpr (GATHER) {
+      big_map_load(c, next_map, has_next ? next_valid : 0, nraw);
+      big_map_offsets(c, nraw, gv);
+    }
+    big_issue<NF, GATHER>(c, tail_lr, (sb + 1) & 1, 0, gv);
+  }
 #pragma unroll
   for (int r = 0; r < NR; ++r) read1(sb, 0, 0, r);
   __builtin_amdgcn_sched_barrier(0);
@@ -741,6 +799,10 @@ __device__ __forceinline__ void big_tile(const BigArgs& a, const BigCtx& c, cons
     __builtin_amdgcn_s_barrier();
     const bool more = kt + 2 < nk;
     const __amdgpu_buffer_rsrc_t llr = more ? t.lr : tail_lr;
+    if constexpr (GATHER) {
+      if (kt == 0) big_map_load(c, next_map, has_next ? next_valid : 0, nraw);
+      if (!more) big_map_offsets(c, nraw, gv);
+    }
     substep(Loads{}, 2, cur ^ 1, 0, 0, llr, cur, more ? kt + 2 : 0, 0);
     substep(Loads{}, 3, cur ^ 1, 1, 1, llr, cur, more ? kt + 2 : 0, 1);
   }
@@ -844,6 +906,8 @@ void gemm_bf16_big_kernel(BigArgs a) {
     const uint32_t vrow = (uint32_t)(wave >= 2 ? (((lrow >> 2) & 1) * 16 + (lrow & 3)) : lrow) * c.ld_bytes;
     c.vbase_e = vrow + chunk_e * 16;
     c.vbase_o = vrow + chunk_o * 16;
+    c.ch_e = chunk_e * 16;
+    c.ch_o = chunk_o * 16;
     c.sbase = (uint32_t)(wave & 1) * 128 * c.ld_bytes;
   } else {
     // Transposed: load i moves K rows r, r+1 (r = (wave&1)*32 + 2i), lane j
@@ -856,9 +920,18 @@ void gemm_bf16_big_kernel(BigArgs a) {
   }
 
   int sb = 0, par = 0;
+  // OP_GATHER: the token waves' load offsets of the tile in hand (see big_tile)
+  uint32_t gv[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) gv[i] = 0u;
   if (tile < t_end) {
     BigTile cur = big_tile_desc<TOK, FEAT, MODE>(a, c, tile, s_pref, ntf);
-    big_issue(c, cur.lr, 0, 0);
+    if constexpr (TOK == OP_GATHER) {
+      int32_t raw[16];
+      big_map_load(c, cur.map, cur.mvalid, raw);
+      big_map_offsets(c, raw, gv);
+    }
+    big_issue<4, TOK == OP_GATHER>(c, cur.lr, 0, 0, gv);
     if constexpr (EPI == BE_ACT) big_bias(a, cur, s_bias[0]);
     for (;;) {
       const int next = tile + per_xcd;
@@ -866,11 +939,11 @@ void gemm_bf16_big_kernel(BigArgs a) {
       BigTile nt = cur;
       if (has_next) nt = big_tile_desc<TOK, FEAT, MODE>(a, c, next, s_pref, ntf);
       switch (cur.nbw) {
-        case 4: big_tile<4, 4, EPI, ACT, TOK, FEAT, MODE>(a, c, cur, sb, has_next, nt.lr, s_bias[par], false); break;
-        case 3: big_tile<3, 4, EPI, ACT, TOK, FEAT, MODE>(a, c, cur, sb, has_next, nt.lr, s_bias[par], false); break;
-        case 2: big_tile<2, 4, EPI, ACT, TOK, FEAT, MODE>(a, c, cur, sb, has_next, nt.lr, s_bias[par], false); break;
-        case 1: big_tile<1, 4, EPI, ACT, TOK, FEAT, MODE>(a, c, cur, sb, has_next, nt.lr, s_bias[par], false); break;
-        default: big_tile<0, 4, EPI, ACT, TOK, FEAT, MODE>(a, c, cur, sb, has_next, nt.lr, s_bias[par], false); break;
+        case 4: big_tile<4, 4, EPI, ACT, TOK, FEAT, MODE>(a, c, cur, sb, has_next, nt.lr, nt.map, nt.mvalid, gv, s_bias[par], false); break;
+        case 3: big_tile<3, 4, EPI, ACT, TOK, FEAT, MODE>(a, c, cur, sb, has_next, nt.lr, nt.map, nt.mvalid, gv, s_bias[par], false); break;
+        case 2: big_tile<2, 4, EPI, ACT, TOK, FEAT, MODE>(a, c, cur, sb, has_next, nt.lr, nt.map, nt.mvalid, gv, s_bias[par], false); break;
+        case 1: big_tile<1, 4, EPI, ACT, TOK, FEAT, MODE>(a, c, cur, sb, has_next, nt.lr, nt.map, nt.mvalid, gv, s_bias[par], false); break;
+        default: big_tile<0, 4, EPI, ACT, TOK, FEAT, MODE>(a, c, cur, sb, has_next, nt.lr, nt.map, nt.mvalid, gv, s_bias[par], false); break;
       }
       // the next tile's numbering starts at the stage this tile's step nk-2
       // used, whose last reads came before this tile's last barrier
@@ -887,13 +960,18 @@ void gemm_bf16_big_kernel(BigArgs a) {
       const BigTile st = big_tile_desc<TOK, FEAT, MODE>(a, c, F + slice_tile, s_pref, ntf, loc % 4);
       if (st.n0 < a.N) {   // uniform: the slice's first feature
         if constexpr (EPI == BE_ACT) big_bias(a, st, s_bias[par]);   // visible after the slice's first barrier
+        if constexpr (TOK == OP_GATHER) {
+          int32_t raw[16];
+          big_map_load(c, st.map, st.mvalid, raw);
+          big_map_offsets(c, raw, gv);
+        }
         const __amdgpu_buffer_rsrc_t none = make_rsrc(a.tok, 0);
         switch (st.nbw) {
-          case 4: big_tile<4, 1, EPI, ACT, TOK, FEAT, MODE>(a, c, st, sb, false, none, s_bias[par], true); break;
-          case 3: big_tile<3, 1, EPI, ACT, TOK, FEAT, MODE>(a, c, st, sb, false, none, s_bias[par], true); break;
-          case 2: big_tile<2, 1, EPI, ACT, TOK, FEAT, MODE>(a, c, st, sb, false, none, s_bias[par], true); break;
-          case 1: big_tile<1, 1, EPI, ACT, TOK, FEAT, MODE>(a, c, st, sb, false, none, s_bias[par], true); break;
-          default: big_tile<0, 1, EPI, ACT, TOK, FEAT, MODE>(a, c, st, sb, false, none, s_bias[par], true); break;
+          case 4: big_tile<4, 1, EPI, ACT, TOK, FEAT, MODE>(a, c, st, sb, false, none, nullptr, 0, gv, s_bias[par], true); break;
+          case 3: big_tile<3, 1, EPI, ACT, TOK, FEAT, MODE>(a, c, st, sb, false, none, nullptr, 0, gv, s_bias[par], true); break;
+          case 2: big_tile<2, 1, EPI, ACT, TOK, FEAT, MODE>(a, c, st, sb, false, none, nullptr, 0, gv, s_bias[par], true); break;
+          case 1: big_tile<1, 1, EPI, ACT, TOK, FEAT, MODE>(a, c, st, sb, false, none, nullptr, 0, gv, s_bias[par], true); break;
+          default: big_tile<0, 1, EPI, ACT, TOK, FEAT, MODE>(a, c, st, sb, false, none, nullptr, 0, gv, s_bias[par], true); break;
         }
       }
     }
@@ -1012,6 +1090,15 @@ hipError_t launch_bf16_big(const GemmArgs& g, hipStream_t s) {
   a.K = g.K;
   a.M = 0;
   a.act = g.act;
+  if (g.x_map) {
+    // rows gathered from the token matrix: one 32-bit descriptor covers it
+    if (g.x_ld && g.x_ld != g.K) return hipErrorInvalidValue;
+    if (g.x_rows * g.K * 2 >= (int64_t(1) << 31)) return hipErrorNotSupported;
+    a.tok_ld = g.K;
+    a.tok_map = g.x_map;
+    a.tok_rows = g.x_rows;
+    return launch_big_act<BE_ACT, OP_GATHER, OP_KC, BM_ROWS>(a, s);
+  }
   return launch_big_act<BE_ACT, OP_KC, OP_KC, BM_ROWS>(a, s);
 }
 
@@ -1137,7 +1224,7 @@ hipError_t launch_pack_expert_weight(const void* w, void* wp, int E, int64_t N, 
 
 hipError_t launch_grouped_gemm(const GemmArgs& a, int dtype, hipStream_t s) {
   if (a.max_rows <= 0) return hipSuccess;
-  if (a.w_packed && !grouped_gemm_is_big(a.K, a.N, dtype)) return hipErrorNotSupported;
+  if ((a.w_packed || a.x_map) && !grouped_gemm_is_big(a.K, a.N, dtype)) return hipErrorNotSupported;
   const bool pitched = (a.x_ld && a.x_ld != a.K) || (a.y_ld && a.y_ld != a.N);
   if (pitched && (a.x_ld && a.x_ld < a.K || a.y_ld && a.y_ld < a.N || a.x_ld > a.K + 64)) return hipErrorInvalidValue;
   if (grouped_gemm_is_big(a.K, a.N, dtype)) return launch_bf16_big(a, s);

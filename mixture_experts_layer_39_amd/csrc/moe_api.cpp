@@ -88,6 +88,7 @@ struct Layout {
   int tiles, tile_tokens;
   size_t tile_cnt, me_tile, me_sum, demand, gate_sync, gate_end, idx, slot, weight, offset;
   size_t x_disp, a_save, h_disp, y_disp, d_act;
+  size_t row_tok;   // inference forward: token of each packed row (the first Linear gathers x through it)
   int64_t h_ld;   // row pitch (elements) of h_disp in the layer forward
   size_t dec_logits, dec_prob, dec_part, dec_bar;   // small-batch forward: logits, probabilities, partial logits, barrier
   // backward regions (save_preact == 1 only)
@@ -125,6 +126,7 @@ Layout layout_of(const moe_config* c) {
   L.weight = take((size_t)L.T * k * 4);
   L.offset = take((size_t)(E + 1) * 4);
   L.x_disp = take((size_t)L.rows * d * s);
+  L.row_tok = take((size_t)L.rows * 4);
   L.a_save = take((c->save_preact && h > 0) ? (size_t)L.rows * h * s : 0);
   // Without save_preact nothing outside the forward reads h_disp, and the
   // second Linear reads it faster with an odd number of 128-byte lines per
@@ -242,16 +244,20 @@ moe_status run_gate(const moe_config* c, const Layout& L, const void* x, const v
   return MOE_OK;
 }
 
-// h_ld: row pitch of h_disp (and a_save) in elements.
+// h_ld: row pitch of h_disp (and a_save) in elements.  row_tok non-null:
+// x_disp is the token matrix [T, d] itself and the first Linear reads packed
+// row r from its row row_tok[r].
 moe_status run_ffn(const moe_config* c, const Layout& L, const void* x_disp, const int32_t* offset,
                    const void* w1, const void* b1, const void* w2, const void* b2, void* a_save,
-                   void* h_disp, void* y_disp, int64_t h_ld, hipStream_t s) {
+                   void* h_disp, void* y_disp, int64_t h_ld, hipStream_t s, const int32_t* row_tok = nullptr) {
   const int d = c->hidden_size, h = c->ffn_hidden;
   GemmArgs g;
   g.offset = offset;
   g.max_rows = L.rows;
   g.E = c->num_experts;
   g.w_packed = c->packed_weights;
+  g.x_map = row_tok;
+  g.x_rows = L.T;
   if (h > 0) {
     g.X = x_disp;
     g.W = w1;
@@ -263,6 +269,7 @@ moe_status run_ffn(const moe_config* c, const Layout& L, const void* x_disp, con
     g.act = c->activation;
     g.y_ld = h_ld;
     MOE_TRY_HIP(launch_grouped_gemm(g, c->dtype, s));
+    g.x_map = nullptr;
     g.X = h_disp;
     g.W = w2;
     g.bias = b2;
@@ -305,10 +312,23 @@ moe_status forward_experts(const moe_config* cfg, const Layout& L, const void* x
   void* hd = cfg->ffn_hidden > 0 ? at<void>(ws, L.h_disp) : nullptr;
   void* as = (cfg->save_preact && cfg->ffn_hidden > 0) ? at<void>(ws, L.a_save) : nullptr;
   void* yd = at<void>(ws, L.y_disp);
+  // Inference on the large-tile GEMM: no dispatched copy of x; a row map
+  // (4 bytes per packed row) tells the first Linear which token row each
+  // packed row is, and it loads that row of x directly.  Training keeps the
+  // copy, which the backward reads.
+  const int d = cfg->hidden_size, n1 = cfg->ffn_hidden > 0 ? cfg->ffn_hidden : d;
+  if (!cfg->save_preact && grouped_gemm_is_big(d, n1, cfg->dtype) && L.T * d * 2 < (int64_t(1) << 31)) {
+    int32_t* rt = at<int32_t>(ws, L.row_tok);
+    if (ga.T >= 0)
+      MOE_TRY_HIP(launch_row_map_finalize(ga, rt, s));
+    else
+      MOE_TRY_HIP(launch_row_map(idx, sl, off, rt, L.T, cfg->k, s));
+    return run_ffn(cfg, L, x, off, w1, b1, w2, b2, as, hd, yd, L.h_ld, s, rt);
+  }
   if (ga.T >= 0)
-    MOE_TRY_HIP(launch_dispatch_finalize(x, ga, xd, cfg->hidden_size * esize(cfg), s));
+    MOE_TRY_HIP(launch_dispatch_finalize(x, ga, xd, d * esize(cfg), s));
   else
-    MOE_TRY_HIP(launch_dispatch(x, idx, sl, off, xd, L.T, cfg->k, cfg->hidden_size * esize(cfg), s));
+    MOE_TRY_HIP(launch_dispatch(x, idx, sl, off, xd, L.T, cfg->k, d * esize(cfg), s));
   return run_ffn(cfg, L, xd, off, w1, b1, w2, b2, as, hd, yd, L.h_ld, s);
 }
 

@@ -109,6 +109,11 @@ hipError_t launch_dispatch(const void* x, const int32_t* expert_idx, const int32
 // Dispatch with the gate's slot fix-up fused in (g as the gate ran it, its
 // slots still the in-tile ranks): writes the final slots and the packed rows.
 hipError_t launch_dispatch_finalize(const void* x, const GateArgs& g, void* x_disp, int row_bytes, hipStream_t s);
+// The dispatch as a row map (packed row -> token) for a first Linear that
+// gathers its rows from x: from final slots, or with the slot fix-up fused in.
+hipError_t launch_row_map(const int32_t* expert_idx, const int32_t* slot, const int32_t* expert_offset,
+                          int32_t* row_tok, int64_t T, int k, hipStream_t s);
+hipError_t launch_row_map_finalize(const GateArgs& g, int32_t* row_tok, hipStream_t s);
 hipError_t launch_combine(const void* y_disp, const int32_t* expert_idx, const int32_t* slot,
                           const float* weight, const int32_t* expert_offset, void* out,
                           int64_t T, int k, int d, int dtype, hipStream_t s);
@@ -127,6 +132,10 @@ struct GemmArgs {
   int64_t x_ld = 0, y_ld = 0;  // row pitches of X and Y (and Apre) in elements; 0: K and N.
                                // Other pitches only where grouped_gemm_is_big holds.
   int32_t w_packed = 0;        // W in the packed layout (moe_pack_expert_weight); big path only
+  const int32_t* x_map = nullptr;  // non-null: X is the token matrix [x_rows, K] and packed row r
+                                   // reads X row x_map[r] (the dispatch folded into the loads;
+                                   // big path, bf16, contiguous X only)
+  int64_t x_rows = 0;
 };
 hipError_t launch_grouped_gemm(const GemmArgs& a, int dtype, hipStream_t s);
 // Whether launch_grouped_gemm runs this shape on the large-tile kernel.

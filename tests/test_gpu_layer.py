@@ -109,6 +109,37 @@ def test_layer_parity_small(name, T):
     assert torch.equal(g2["offset"], off)
 
 
+# (workload, overrides): d = 64, 128, 192 give 1, 2, 3 K steps in the first
+# Linear (the map of the next tile is read at the first step and used at the
+# last); h = 0 is a single Linear that gathers; k = 1; experts left without
+# rows; a ragged token count that leaves part-filled tiles
+GATHER = [("top2_e64", dict(T=777, d=64, h=256, E=6)), ("top2_e64", dict(T=901, d=128, h=192, E=5)),
+          ("nodrop_e128", dict(T=613, d=192, h=320, E=7)), ("top2_e8", dict(T=1500, d=256, E=8)),
+          ("top2_e8", dict(T=999, d=320, E=3, k=1)), ("skew_e16", dict(T=2053, d=256, h=512, E=16)),
+          ("top2_e64", dict(T=40, d=128, h=256, E=64))]
+
+
+@pytest.mark.parametrize("name,kw", GATHER, ids=lambda v: str(v))
+def test_gathered_first_linear(name, kw):
+    """The inference forward's first Linear loads each packed row from x
+    through the row map instead of reading a dispatched copy: the same output
+    bits as the training forward (which copies), and the oracle's output."""
+    sp = spec(name, logits_given=True, **kw)
+    inp = with_given_logits(make_inputs(sp, DEV))
+    g0, out0, _, _ = run_fused(sp, inp, cfg_of(sp, save_preact=0, small_batch=-1))
+    out0 = out0.clone()
+    g1, out1, _, _ = run_fused(sp, inp, cfg_of(sp, save_preact=1, small_batch=-1))
+    torch.cuda.synchronize()
+    assert torch.equal(out0, out1)
+    for key in ("idx", "slot", "weight", "count", "loss"):
+        assert torch.equal(g0[key], g1[key]), key
+    x, w1, b1, w2, b2 = oracle_inputs(inp)
+    r = O.layer_forward(x, f64(inp["logits"]), w1, b1, w2, b2, k=sp["k"], capacity_factor=sp["cf"],
+                        min_capacity=sp["min_cap"], drop_tokens=sp["drop"], act=sp["act"], dtype=sp["dtype"])
+    np.testing.assert_array_equal(i64(g0["slot"]), r["slot"])
+    close(f64(out0), r["out"], RTOL[sp["dtype"]])
+
+
 @pytest.mark.parametrize("name,T", [("top2_e64", 1000), ("nodrop_e128", 700), ("skew_e16", 549)], ids=str)
 def test_layer_padded_intermediate(name, T):
     """Without save_preact the forward keeps h_disp at a row pitch of h + 64
@@ -249,9 +280,11 @@ FULL = ["top2_e8", "top2_e64", "skew_e16", "nodrop_e128"]
 @pytest.mark.parametrize("name", FULL)
 def test_layer_full_size(name):
     """Full size, in the launch configuration the benchmark times (inference:
-    no saved pre-activation, h_disp at the layer's own pitch): every routing
-    output bit-exact, every packed row of x_disp bit-exact, and every element
-    of h_disp, y_disp and out against the whole oracle forward."""
+    no saved pre-activation, h_disp at the layer's own pitch, the first
+    Linear gathering its rows from x instead of a dispatched copy): every
+    routing output bit-exact, and every element of h_disp, y_disp and out
+    against the whole oracle forward; the dispatch entry point on the same
+    routing gives every packed row of the oracle's x_disp bit-exact."""
     sp = spec(name, logits_given=True)
     inp = with_given_logits(make_inputs(sp, DEV))
     cfg = cfg_of(sp)
@@ -272,7 +305,12 @@ def test_layer_full_size(name):
         assert (r["expert_count"] <= C).all()
     assert r["expert_count"].sum() == k * T - int((r["slot"] < 0).sum())
     n = int(r["expert_offset"][-1])
-    np.testing.assert_array_equal(f64(view(v["x_disp"], n, d, tdt, ws)), r["x_disp"])
+    off = view(v["offset"], 1, E + 1, torch.int32, ws)[0].clone()
+    np.testing.assert_array_equal(i64(off), r["expert_offset"])
+    xd = torch.full((max(B.moe_max_rows(cfg), 1), d), 7.0, dtype=tdt, device=DEV)
+    B.moe_dispatch(cfg, inp["x"], g["idx"], g["slot"], off, xd)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(f64(xd[:n]), r["x_disp"])
     rt = RTOL[sp["dtype"]]
     if h > 0:
         ld = B.moe_workspace_h_ld(cfg)
