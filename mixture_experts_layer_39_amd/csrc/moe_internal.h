@@ -47,7 +47,12 @@ __device__ __forceinline__ float gelu_fast(float x) {
   p = fmaf(p, s, -0x1.d56212p-2f);
   p = fmaf(p, s, -0x1.26ba2cp+0f);
   p = fmaf(p, s, -0x1.ffff32p-1f);
-  return fmaf(-s, __builtin_amdgcn_exp2f(p), fmaxf(x, 0.f));
+  // max(x, 0) as one v_max: fmaxf adds a second instruction to quiet a
+  // signalling NaN in x, which is not needed here (a NaN x already makes s,
+  // and so the result, NaN)
+  float xp;
+  asm("v_max_f32 %0, 0, %1" : "=v"(xp) : "v"(x));
+  return fmaf(-s, __builtin_amdgcn_exp2f(p), xp);
 }
 
 template <int ACT>
