@@ -305,11 +305,16 @@ __global__ __launch_bounds__(WT * WF * 64) void gemm_bf16_kernel(GemmArgs a) {
 //    expert's ragged row count (experts without rows are zero-filled apart).
 namespace big {
 constexpr int BT = 256, BF = 256, BKB = 128;  // BKB: bytes of one row's K step
-constexpr int TILE_BYTES = 256 * BKB;          // one operand tile (both layouts)
-constexpr int STAGE = 2 * TILE_BYTES;          // token tile + feature tile
-constexpr int LDS = 2 * STAGE;                 // double buffered
+constexpr int TILE_BYTES = 256 * BKB;          // one 256-row operand tile (both layouts)
 constexpr int TRB = 512;                       // bytes of one K row of a transposed tile
+// RB: 32-row token blocks per token-side wave: 4 (256-row token tiles), or
+// 5 (320 rows) for the forward Linears on K-contiguous operands where the
+// caller asks for it (GemmArgs::tile_rows).
+constexpr int rows_of(int rb) { return 64 * rb; }
+constexpr int stage_of(int rb) { return rows_of(rb) * BKB + TILE_BYTES; }   // token tile + feature tile
+constexpr int lds_of(int rb) { return 2 * stage_of(rb); }                    // double buffered
 }  // namespace big
+
 
 // operand layout; OP_GATHER: K-contiguous token rows gathered through a
 // packed-row -> token map (the inference forward's first Linear reads x
@@ -345,7 +350,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // Per-expert tile counts (exclusive prefix in s_pref[0..E]), by wavefront 0:
 // token-row tiles ceil(rows/256), or mtw weight-gradient row tiles for every
 // expert that has rows.
-template <int MODE>
+template <int MODE, int BTR>
 __device__ __forceinline__ void big_prefix(const int32_t* __restrict__ offset, int E, int mtw, int* s_pref) {
   const int lane = threadIdx.x & 63;
   if ((threadIdx.x >> 6) == 0) {
@@ -355,7 +360,7 @@ __device__ __forceinline__ void big_prefix(const int32_t* __restrict__ offset, i
     for (int r = 0; r < 4; ++r) {
       const int e = lane * 4 + r;
       const int rows = e < E ? offset[e + 1] - offset[e] : 0;
-      c[r] = MODE == BM_WGRAD ? (rows > 0 ? mtw : 0) : (rows + big::BT - 1) / big::BT;
+      c[r] = MODE == BM_WGRAD ? (rows > 0 ? mtw : 0) : (rows + BTR - 1) / BTR;
       s += c[r];
     }
     int incl = s;
@@ -380,7 +385,7 @@ struct BigTile {
   int e, row0;            // expert, its first packed row
   int mbase, mvalid;      // first tile row (expert-relative, or output row) and row count
   int n0, nk;             // first feature, 64-wide K steps
-  int nbw;                // this wave's valid 32-row token blocks (0..4)
+  int nbw;                // this wave's valid 32-row token blocks (0..RB)
   const int32_t* map;     // OP_GATHER: the token row of each tile row (tok_map from the tile's first row)
   __amdgpu_buffer_rsrc_t lr;   // the operand this wave loads (token or feature side)
 };
@@ -394,6 +399,9 @@ struct BigCtx {
   uint32_t sbase, ld_bytes;     // per-wave row base; bytes between operand rows
   uint32_t kstride;             // K-contiguous: bytes between consecutive 64-wide K steps
   uint32_t ch_e, ch_o;          // K-contiguous: this lane's chunk byte offset for even / odd instructions
+  uint32_t stage_bytes;         // one stage: token tile + feature tile
+  uint32_t tok_half;            // bytes of a token-side wave's half of the token tile
+  int rb;                       // 32-row token blocks per token-side wave
 };
 
 // slice >= 0: features 64*slice .. +63 of the tile only (K-contiguous
@@ -423,7 +431,7 @@ __device__ __forceinline__ BigTile big_tile_desc(const BigArgs& a, const BigCtx&
   const int nvb = (t.mvalid + 31) >> 5;                        // valid 32-row blocks
   // this wave's token blocks are wt, wt+2, wt+4, wt+6; the valid ones are a
   // prefix of that list
-  t.nbw = nvb > c.wt ? min(4, (nvb - c.wt + 1) >> 1) : 0;
+  t.nbw = nvb > c.wt ? min(c.rb, (nvb - c.wt + 1) >> 1) : 0;
   if (c.wave >= 2) {
     const int ncols = min(slice >= 0 ? 64 : BF, a.N - t.n0);
     if constexpr (FEAT == OP_KC) {
@@ -471,7 +479,7 @@ __device__ __forceinline__ BigTile big_tile_desc(const BigArgs& a, const BigCtx&
 // slice, whose waves load 4 instructions each).
 // GATHER: the token waves take their per-lane byte offset from gv (load i's
 // gathered row and chunk, from big_map_offsets) instead of the tile row.
-template <bool GATHER = false>
+template <bool GATHER, bool SOFF>
 __device__ __forceinline__ void big_issue_one(const BigCtx& c, __amdgpu_buffer_rsrc_t lr, int stage, int kstep, int i,
                                               int nfw = 4, uint32_t gv = 0) {
   using namespace big;
@@ -479,26 +487,40 @@ __device__ __forceinline__ void big_issue_one(const BigCtx& c, __amdgpu_buffer_r
   // wave (4 KB per wave in a slice), 1 KB per instruction (8 rows x 128 B,
   // or 2 K rows x 512 B)
   const bool fw = c.wave >= 2;
-  unsigned char* dst = c.smem + stage * STAGE + c.lds_op + (c.wave & 1) * (fw ? 4096 * nfw : 16384) + i * 1024;
+  unsigned char* dst = c.smem + stage * c.stage_bytes + c.lds_op + (c.wave & 1) * (fw ? 4096u * nfw : c.tok_half) +
+                       i * 1024;
   // wave-uniform row offset and K offset, chosen without a branch
   const uint32_t g = fw ? (uint32_t)((i >> 2) * 32 + (i & 3) * 4) : (uint32_t)(i * 8);
   const uint32_t kc_row = (fw ? (uint32_t)(c.wave & 1) * 32u * (uint32_t)nfw * c.ld_bytes : c.sbase) + g * c.ld_bytes;
   const uint32_t tr_row = (uint32_t)(kstep * 64 + (c.wave & 1) * 32 + 2 * i) * c.ld_bytes;
   const uint32_t vrow = c.tr ? tr_row : kc_row;
-  const uint32_t soff = c.tr ? 0u : (uint32_t)kstep * c.kstride;
-  uint32_t voff = ((i & 1) ? c.vbase_o : c.vbase_e) + vrow;
+  uint32_t soff, voff;
+  if constexpr (SOFF) {
+    // the row in the scalar offset (both offsets count towards the range
+    // check): no per-load VGPR, which the 320-row tile needs for its fifth
+    // accumulator block; with the VGPR to spare the per-lane form is faster
+    soff = vrow + (uint32_t)kstep * c.kstride;
+    voff = (i & 1) ? c.vbase_o : c.vbase_e;
+  } else {
+    soff = c.tr ? 0u : (uint32_t)kstep * c.kstride;
+    voff = ((i & 1) ? c.vbase_o : c.vbase_e) + vrow;
+  }
   if constexpr (GATHER) {
-    if (!fw) voff = gv;
+    if (!fw) {
+      voff = gv;
+      soff = (uint32_t)kstep * c.kstride;
+    }
   }
   __builtin_amdgcn_raw_ptr_buffer_load_lds(lr, (__attribute__((address_space(3))) void*)dst, 16, voff, soff, 0, 0);
 }
 
-template <int NF = 4, bool GATHER = false>
+template <int NF, bool GATHER, int RB>
 __device__ __forceinline__ void big_issue(const BigCtx& c, __amdgpu_buffer_rsrc_t lr, int stage, int kstep,
                                           const uint32_t (&gv)[16]) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i)
-    if (c.wave < 2 || i < 4 * NF) big_issue_one<GATHER>(c, lr, stage, kstep, i, NF, gv[i]);
+  for (int i = 0; i < 4 * RB; ++i)
+    if (c.wave < 2 || i < 4 * NF) big_issue_one<GATHER, RB == 5>(c, lr, stage, kstep, i, NF, gv[i < 16 ? i : 15]);
+  static_assert(!GATHER || RB == 4, "gathered token rows use 256-row tiles");
 }
 
 // Gathered token rows, token waves: raw[i] = the token row that load i of
@@ -537,14 +559,26 @@ __device__ __forceinline__ float agpr_read(float v) {
   return r;
 }
 
+// One MFMA whose accumulator the register allocator must keep in VGPRs: a
+// 320-row tile needs 320 accumulators per lane, 64 more than the AGPR file
+// holds, and with the compiler choosing the register class of every MFMA it
+// copied accumulators between the two files on every K step.  The 32x32x16
+// MFMA is 8 passes; the only later readers of these registers are the
+// following MFMAs on the same block (a sub-step later, with the
+// back-to-back accumulation the hardware supports) and the epilogue, which
+// waits out the write-to-VALU-read interval first (big_tile).
+__device__ __forceinline__ void mfma_vacc(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+
 // The accumulator block blk = ff*4 + tt, read out of its AGPRs (constant
 // indices inside each case; blocks with tt >= NB or ff >= NF do not exist).
-template <int NB, int NF>
-__device__ __forceinline__ void acc_block(const f32x16 (&acc)[NF][4], int blk, float (&v)[16]) {
+template <int NB, int NF, int RB>
+__device__ __forceinline__ void acc_block(const f32x16 (&acc)[NF][RB], int blk, float (&v)[16]) {
   switch (blk) {
 #define MOE_AB(FF, TT)                                              \
-  case FF * 4 + TT:                                                 \
-    if constexpr (TT < NB && FF < NF) {                             \
+  case FF * RB + TT:                                                \
+    if constexpr (TT < NB && FF < NF && TT < RB) {                  \
       _Pragma("unroll") for (int r = 0; r < 16; ++r) v[r] = agpr_read(acc[FF][TT][r]); \
     }                                                               \
     break;
@@ -553,6 +587,14 @@ __device__ __forceinline__ void acc_block(const f32x16 (&acc)[NF][4], int blk, f
     MOE_AB(2, 0) MOE_AB(2, 1) MOE_AB(2, 2) MOE_AB(2, 3)
     MOE_AB(3, 0) MOE_AB(3, 1) MOE_AB(3, 2) MOE_AB(3, 3)
 #undef MOE_AB
+#define MOE_AB5(FF)                                                 \
+  case RB == 5 ? FF * RB + 4 : 100 + FF:                            \
+    if constexpr (RB == 5 && 4 < NB && FF < NF) {                   \
+      _Pragma("unroll") for (int r = 0; r < 16; ++r) v[r] = acc[FF][RB - 1][r]; \
+    }                                                               \
+    break;
+    MOE_AB5(0) MOE_AB5(1) MOE_AB5(2) MOE_AB5(3)
+#undef MOE_AB5
     default: break;
   }
 }
@@ -665,21 +707,23 @@ __device__ __forceinline__ bf16x8 tr_frag(const unsigned char* tile, int i, int 
 // issued into the stage this tile's step nk-2 used (the other stage when
 // nk == 1), which is stage 0 of the next tile's numbering with
 // sb' = (sb + nk) & 1.
-template <int NB, int NF, int EPI, int ACT, int TOK, int FEAT, int MODE>
+template <int NB, int NF, int EPI, int ACT, int TOK, int FEAT, int MODE, int RB>
 __device__ __forceinline__ void big_tile(const BigArgs& a, const BigCtx& c, const BigTile& t, int sb, bool has_next,
                                          __amdgpu_buffer_rsrc_t next_lr, const int32_t* next_map, int next_valid,
                                          uint32_t (&gv)[16], const float* s_bias, bool cold) {
   constexpr bool GATHER = TOK == OP_GATHER;
+  static_assert(RB == 4 || (RB == 5 && TOK == OP_KC && FEAT == OP_KC && MODE == BM_ROWS), "320-row tiles: forward only");
+  constexpr int LPH = 2 * RB;      // loads per half of a K step's loads (token side: 4 * RB in all)
   using namespace big;
   unsigned char* smem = c.smem;
   const int nk = t.nk, wt = c.wt, wf = c.wf, h = c.h, r32 = c.r32;
   const int N = a.N;
   const int lane = threadIdx.x & 63, lane16 = lane & 15, mh = (lane >> 4) & 1, q4 = lane & 3;
-  f32x16 acc[NF][4];
+  f32x16 acc[NF][RB];
 #pragma unroll
   for (int i = 0; i < NF; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < RB; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
   // Fragment registers: four sets, so that sub-step i+2's fragments are read
@@ -699,8 +743,8 @@ __device__ __forceinline__ void big_tile(const BigArgs& a, const BigCtx& c, cons
   // MFMAs consume them: token block 0, the four feature blocks, then the
   // other token blocks
   auto read1 = [&](int stage, int i, int set, int r) {
-    const unsigned char* Xs = smem + stage * STAGE;
-    const unsigned char* Ws = Xs + TILE_BYTES;
+    const unsigned char* Xs = smem + stage * stage_of(RB);
+    const unsigned char* Ws = Xs + rows_of(RB) * BKB;
     const int sw = (((h * 4 + i) ^ ((r32 >> 1) & 7)) * 16);
     const bool tokr = NB > 0 && (r == 0 || r >= NF + 1);
     const int tt = r == 0 ? 0 : r - NF;
@@ -720,11 +764,17 @@ __device__ __forceinline__ void big_tile(const BigArgs& a, const BigCtx& c, cons
   // MFMA j of a sub-step: token block j / NF with feature block j % NF
   auto mfma1 = [&](int set, int j) {
     const int tt = j / NF, ff = j % NF;
+    if constexpr (NB == 5) {
+      if (tt == 4) {   // the fifth token block: accumulators in VGPRs
+        mfma_vacc(acc[ff][4], fa[set][ff], fb[set][4]);
+        return;
+      }
+    }
     acc[ff][tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][ff], fb[set][tt], acc[ff][tt], 0, 0, 0);
   };
   // One sub-step in a fixed issue order: each MFMA is followed by its share
   // of the fragment reads of the sub-step two ahead (one after each of the
-  // first NR MFMAs) and, when loading, of half (lhalf) of the 16
+  // first NR MFMAs) and, when loading, of half (lhalf) of the 4 * RB
   // global->LDS loads, so that the memory instructions issue in the shadow
   // of the MFMAs instead of in a bubble.
   auto substep = [&](auto loads, int mset, int rstage, int ri, int rset, __amdgpu_buffer_rsrc_t llr, int lstage,
@@ -737,17 +787,17 @@ __device__ __forceinline__ void big_tile(const BigArgs& a, const BigCtx& c, cons
       if constexpr (LOADS) {
         if constexpr (NM > 0) {
 #pragma unroll
-          for (int q = j * 8 / NM; q < (j + 1) * 8 / NM && j < NM; ++q)
-            if (c.wave < 2 || lhalf * 8 + q < 4 * NF)
-              big_issue_one<GATHER>(c, llr, lstage, lkstep, lhalf * 8 + q, NF,
-                                    gv[lhalf * 8 + q]);
+          for (int q = j * LPH / NM; q < (j + 1) * LPH / NM && j < NM; ++q)
+            if (c.wave < 2 || lhalf * LPH + q < 4 * NF)
+              big_issue_one<GATHER, RB == 5>(c, llr, lstage, lkstep, lhalf * LPH + q, NF,
+                                    gv[(lhalf * LPH + q) & 15]);
         } else {
           if (j == 0) {
 #pragma unroll
-            for (int q = 0; q < 8; ++q)
-              if (c.wave < 2 || lhalf * 8 + q < 4 * NF)
-                big_issue_one<GATHER>(c, llr, lstage, lkstep, lhalf * 8 + q, NF,
-                                      gv[lhalf * 8 + q]);
+            for (int q = 0; q < LPH; ++q)
+              if (c.wave < 2 || lhalf * LPH + q < 4 * NF)
+                big_issue_one<GATHER, RB == 5>(c, llr, lstage, lkstep, lhalf * LPH + q, NF,
+                                      gv[(lhalf * LPH + q) & 15]);
           }
         }
       }
@@ -773,17 +823,17 @@ __device__ __forceinline__ void big_tile(const BigArgs& a, const BigCtx& c, cons
   // next tile's first K step; the next tile's map is read during the first
   // K step, a step before the barrier that waits for it
   int32_t nraw[16];
-  if (cold) big_issue<NF, GATHER>(c, t.lr, sb & 1, 0, gv);
+  if (cold) big_issue<NF, GATHER, RB>(c, t.lr, sb & 1, 0, gv);
   __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_s_barrier();
   if (nk > 1) {
-    big_issue<NF, GATHER>(c, t.lr, (sb + 1) & 1, 1, gv);
+    big_issue<NF, GATHER, RB>(c, t.lr, (sb + 1) & 1, 1, gv);
   } else {
     if constexpr (GATHER) {
       big_map_load(c, next_map, has_next ? next_valid : 0, nraw);
       big_map_offsets(c, nraw, gv);
     }
-    big_issue<NF, GATHER>(c, tail_lr, (sb + 1) & 1, 0, gv);
+    big_issue<NF, GATHER, RB>(c, tail_lr, (sb + 1) & 1, 0, gv);
   }
 #pragma unroll
   for (int r = 0; r < NR; ++r) read1(sb, 0, 0, r);
@@ -814,21 +864,24 @@ __device__ __forceinline__ void big_tile(const BigArgs& a, const BigCtx& c, cons
     substep(NoLoads{}, 3, cur, -1, 0, no_lr, 0, 0, 0);
   }
 
+  // the fifth block's accumulators come from MFMAs the compiler cannot see
+  // into: wait out the MFMA-write to VALU-read interval before any read
+  if constexpr (NB == 5) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
   // one compact loop over the accumulator blocks keeps the epilogue small
   // enough to stay in the instruction cache
 #pragma nounroll
-  for (int blk = 0; blk < 4 * NF; ++blk) {
-    const int ff = blk >> 2, tt = blk & 3;
+  for (int blk = 0; blk < RB * NF; ++blk) {
+    const int ff = blk / RB, tt = blk - ff * RB;
     const int rloc = (wt + 2 * tt) * 32 + r32;
     const int fl = wf * 32 * NF + ff * 32 + h * 16;   // column offset within the tile
     if (tt >= NB || t.n0 + fl >= N) continue;
     float v[16];
-    acc_block<NB, NF>(acc, blk, v);
+    acc_block<NB, NF, RB>(acc, blk, v);
     if (rloc < t.mvalid) big_store<EPI, ACT, MODE>(a, v, t, rloc, fl, s_bias);
   }
 }
 
-template <int EPI, int ACT, int TOK, int FEAT, int MODE>
+template <int EPI, int ACT, int TOK, int FEAT, int MODE, int RB>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void gemm_bf16_big_kernel(BigArgs a) {
   using namespace big;
@@ -839,7 +892,7 @@ void gemm_bf16_big_kernel(BigArgs a) {
   const int E = a.E, N = a.N;
   const int ntf = (N + BF - 1) / BF;
   const int mtw = MODE == BM_WGRAD ? (a.M + BT - 1) / BT : 0;
-  big_prefix<MODE>(a.offset, E, mtw, s_pref);
+  big_prefix<MODE, rows_of(RB)>(a.offset, E, mtw, s_pref);
   __syncthreads();
   const int total = s_pref[E] * ntf;
   // Tail split (forward token-row tiles): when the tiles leave a last round
@@ -881,7 +934,10 @@ void gemm_bf16_big_kernel(BigArgs a) {
   c.h = lane >> 5;
   c.r32 = lane & 31;
   c.wave = wave;
-  c.lds_op = wave >= 2 ? TILE_BYTES : 0;
+  c.rb = RB;
+  c.stage_bytes = stage_of(RB);
+  c.tok_half = 32 * RB * BKB;
+  c.lds_op = wave >= 2 ? rows_of(RB) * BKB : 0;
   c.tr = wave >= 2 ? FEAT == OP_TR : TOK == OP_TR;
   c.ld_bytes = (uint32_t)((wave >= 2 ? a.feat_ld : a.tok_ld) * 2);
   c.kstride = 128;
@@ -908,7 +964,7 @@ void gemm_bf16_big_kernel(BigArgs a) {
     c.vbase_o = vrow + chunk_o * 16;
     c.ch_e = chunk_e * 16;
     c.ch_o = chunk_o * 16;
-    c.sbase = (uint32_t)(wave & 1) * 128 * c.ld_bytes;
+    c.sbase = (uint32_t)(wave & 1) * 32 * RB * c.ld_bytes;
   } else {
     // Transposed: load i moves K rows r, r+1 (r = (wave&1)*32 + 2i), lane j
     // filling slot j % 32 of row r + j / 32; slot p of K row r holds chunk
@@ -931,7 +987,7 @@ void gemm_bf16_big_kernel(BigArgs a) {
       big_map_load(c, cur.map, cur.mvalid, raw);
       big_map_offsets(c, raw, gv);
     }
-    big_issue<4, TOK == OP_GATHER>(c, cur.lr, 0, 0, gv);
+    big_issue<4, TOK == OP_GATHER, RB>(c, cur.lr, 0, 0, gv);
     if constexpr (EPI == BE_ACT) big_bias(a, cur, s_bias[0]);
     for (;;) {
       const int next = tile + per_xcd;
@@ -939,11 +995,15 @@ void gemm_bf16_big_kernel(BigArgs a) {
       BigTile nt = cur;
       if (has_next) nt = big_tile_desc<TOK, FEAT, MODE>(a, c, next, s_pref, ntf);
       switch (cur.nbw) {
-        case 4: big_tile<4, 4, EPI, ACT, TOK, FEAT, MODE>(a, c, cur, sb, has_next, nt.lr, nt.map, nt.mvalid, gv, s_bias[par], false); break;
-        case 3: big_tile<3, 4, EPI, ACT, TOK, FEAT, MODE>(a, c, cur, sb, has_next, nt.lr, nt.map, nt.mvalid, gv, s_bias[par], false); break;
-        case 2: big_tile<2, 4, EPI, ACT, TOK, FEAT, MODE>(a, c, cur, sb, has_next, nt.lr, nt.map, nt.mvalid, gv, s_bias[par], false); break;
-        case 1: big_tile<1, 4, EPI, ACT, TOK, FEAT, MODE>(a, c, cur, sb, has_next, nt.lr, nt.map, nt.mvalid, gv, s_bias[par], false); break;
-        default: big_tile<0, 4, EPI, ACT, TOK, FEAT, MODE>(a, c, cur, sb, has_next, nt.lr, nt.map, nt.mvalid, gv, s_bias[par], false); break;
+        case 5:
+          if constexpr (RB == 5)
+            big_tile<5, 4, EPI, ACT, TOK, FEAT, MODE, RB>(a, c, cur, sb, has_next, nt.lr, nt.map, nt.mvalid, gv, s_bias[par], false);
+          break;
+        case 4: big_tile<4, 4, EPI, ACT, TOK, FEAT, MODE, RB>(a, c, cur, sb, has_next, nt.lr, nt.map, nt.mvalid, gv, s_bias[par], false); break;
+        case 3: big_tile<3, 4, EPI, ACT, TOK, FEAT, MODE, RB>(a, c, cur, sb, has_next, nt.lr, nt.map, nt.mvalid, gv, s_bias[par], false); break;
+        case 2: big_tile<2, 4, EPI, ACT, TOK, FEAT, MODE, RB>(a, c, cur, sb, has_next, nt.lr, nt.map, nt.mvalid, gv, s_bias[par], false); break;
+        case 1: big_tile<1, 4, EPI, ACT, TOK, FEAT, MODE, RB>(a, c, cur, sb, has_next, nt.lr, nt.map, nt.mvalid, gv, s_bias[par], false); break;
+        default: big_tile<0, 4, EPI, ACT, TOK, FEAT, MODE, RB>(a, c, cur, sb, has_next, nt.lr, nt.map, nt.mvalid, gv, s_bias[par], false); break;
       }
       // the next tile's numbering starts at the stage this tile's step nk-2
       // used, whose last reads came before this tile's last barrier
@@ -967,11 +1027,15 @@ void gemm_bf16_big_kernel(BigArgs a) {
         }
         const __amdgpu_buffer_rsrc_t none = make_rsrc(a.tok, 0);
         switch (st.nbw) {
-          case 4: big_tile<4, 1, EPI, ACT, TOK, FEAT, MODE>(a, c, st, sb, false, none, nullptr, 0, gv, s_bias[par], true); break;
-          case 3: big_tile<3, 1, EPI, ACT, TOK, FEAT, MODE>(a, c, st, sb, false, none, nullptr, 0, gv, s_bias[par], true); break;
-          case 2: big_tile<2, 1, EPI, ACT, TOK, FEAT, MODE>(a, c, st, sb, false, none, nullptr, 0, gv, s_bias[par], true); break;
-          case 1: big_tile<1, 1, EPI, ACT, TOK, FEAT, MODE>(a, c, st, sb, false, none, nullptr, 0, gv, s_bias[par], true); break;
-          default: big_tile<0, 1, EPI, ACT, TOK, FEAT, MODE>(a, c, st, sb, false, none, nullptr, 0, gv, s_bias[par], true); break;
+          case 5:
+            if constexpr (RB == 5)
+              big_tile<5, 1, EPI, ACT, TOK, FEAT, MODE, RB>(a, c, st, sb, false, none, nullptr, 0, gv, s_bias[par], true);
+            break;
+          case 4: big_tile<4, 1, EPI, ACT, TOK, FEAT, MODE, RB>(a, c, st, sb, false, none, nullptr, 0, gv, s_bias[par], true); break;
+          case 3: big_tile<3, 1, EPI, ACT, TOK, FEAT, MODE, RB>(a, c, st, sb, false, none, nullptr, 0, gv, s_bias[par], true); break;
+          case 2: big_tile<2, 1, EPI, ACT, TOK, FEAT, MODE, RB>(a, c, st, sb, false, none, nullptr, 0, gv, s_bias[par], true); break;
+          case 1: big_tile<1, 1, EPI, ACT, TOK, FEAT, MODE, RB>(a, c, st, sb, false, none, nullptr, 0, gv, s_bias[par], true); break;
+          default: big_tile<0, 1, EPI, ACT, TOK, FEAT, MODE, RB>(a, c, st, sb, false, none, nullptr, 0, gv, s_bias[par], true); break;
         }
       }
     }
@@ -1041,30 +1105,31 @@ int device_cus() {
   return cached[dev];
 }
 
-template <int EPI, int ACT, int TOK, int FEAT, int MODE>
+template <int EPI, int ACT, int TOK, int FEAT, int MODE, int RB = 4>
 hipError_t launch_big(const BigArgs& a, hipStream_t s) {
-  auto kern = gemm_bf16_big_kernel<EPI, ACT, TOK, FEAT, MODE>;
+  auto kern = gemm_bf16_big_kernel<EPI, ACT, TOK, FEAT, MODE, RB>;
+  constexpr int lds = big::lds_of(RB);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, big::LDS);
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
   // at most one workgroup per CU (LDS use allows no more), never more than
   // the worst-case tile count (four slices per tile on the forward path,
   // which splits a short round of tiles), a whole number per XCD
   const int64_t ntf = (a.N + big::BF - 1) / big::BF;
   const int64_t mtiles = MODE == BM_WGRAD ? (int64_t)a.E * ((a.M + big::BT - 1) / big::BT)
-                                          : (a.max_rows + big::BT - 1) / big::BT + a.E;
+                                          : (a.max_rows + big::rows_of(RB) - 1) / big::rows_of(RB) + a.E;
   const int64_t units = (MODE == BM_ROWS && FEAT == OP_KC ? 4 : 1) * mtiles * ntf;
   int64_t grid = std::min<int64_t>(units, device_cus());
   grid = std::max<int64_t>(kXcds, grid / kXcds * kXcds);
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), big::LDS, s, a);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), lds, s, a);
   return hipGetLastError();
 }
 
-template <int EPI, int TOK, int FEAT, int MODE>
+template <int EPI, int TOK, int FEAT, int MODE, int RB = 4>
 hipError_t launch_big_act(const BigArgs& a, hipStream_t s) {
-  if (a.act == ACT_GELU) return launch_big<EPI, ACT_GELU, TOK, FEAT, MODE>(a, s);
-  if (a.act == ACT_RELU) return launch_big<EPI, ACT_RELU, TOK, FEAT, MODE>(a, s);
-  return launch_big<EPI, ACT_NONE, TOK, FEAT, MODE>(a, s);
+  if (a.act == ACT_GELU) return launch_big<EPI, ACT_GELU, TOK, FEAT, MODE, RB>(a, s);
+  if (a.act == ACT_RELU) return launch_big<EPI, ACT_RELU, TOK, FEAT, MODE, RB>(a, s);
+  return launch_big<EPI, ACT_NONE, TOK, FEAT, MODE, RB>(a, s);
 }
 
 hipError_t launch_bf16_big(const GemmArgs& g, hipStream_t s) {
@@ -1099,6 +1164,7 @@ hipError_t launch_bf16_big(const GemmArgs& g, hipStream_t s) {
     a.tok_rows = g.x_rows;
     return launch_big_act<BE_ACT, OP_GATHER, OP_KC, BM_ROWS>(a, s);
   }
+  if (g.tile_rows == 320) return launch_big_act<BE_ACT, OP_KC, OP_KC, BM_ROWS, 5>(a, s);
   return launch_big_act<BE_ACT, OP_KC, OP_KC, BM_ROWS>(a, s);
 }
 

@@ -4,6 +4,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "moe.h"
@@ -244,6 +245,22 @@ moe_status run_gate(const moe_config* c, const Layout& L, const void* x, const v
   return MOE_OK;
 }
 
+// Row tile height for the forward Linears of a layer.  Every row tile
+// streams its expert's whole weight tile, so an expert with a few rows more
+// than a multiple of 256 pays for a nearly empty tile.  320-row tiles (a
+// fifth 32-row block per token-side wave, the row offsets of the loads in
+// scalar registers to make room for its accumulators) put up to 640 rows in
+// two tiles; they cost more per tile, and they pay off where the largest
+// expert (the capacity when tokens are dropped, else the mean) needs fewer
+// row tiles with them and at most three: with more tiles per expert the
+// weights come back from the L2 in groups of row tiles anyway.
+int forward_tile_rows(const moe_config* c, const Layout& L) {
+  const int64_t E = c->num_experts, kt = L.T * c->k;
+  const int64_t m = L.C >= 0 ? std::min(L.C, kt) : (kt + E - 1) / E;
+  const int64_t t5 = (m + 319) / 320, t4 = (m + 255) / 256;
+  return (m > 0 && t5 < t4 && t5 <= 3) ? 320 : 256;
+}
+
 // h_ld: row pitch of h_disp (and a_save) in elements.  row_tok non-null:
 // x_disp is the token matrix [T, d] itself and the first Linear reads packed
 // row r from its row row_tok[r].
@@ -258,6 +275,7 @@ moe_status run_ffn(const moe_config* c, const Layout& L, const void* x_disp, con
   g.w_packed = c->packed_weights;
   g.x_map = row_tok;
   g.x_rows = L.T;
+  g.tile_rows = forward_tile_rows(c, L);
   if (h > 0) {
     g.X = x_disp;
     g.W = w1;
@@ -314,10 +332,13 @@ moe_status forward_experts(const moe_config* cfg, const Layout& L, const void* x
   void* yd = at<void>(ws, L.y_disp);
   // Inference on the large-tile GEMM: no dispatched copy of x; a row map
   // (4 bytes per packed row) tells the first Linear which token row each
-  // packed row is, and it loads that row of x directly.  Training keeps the
-  // copy, which the backward reads.
+  // packed row is, and it loads that row of x directly.  The gathering form
+  // runs 256-row tiles; where the layer's Linears take 320-row tiles the
+  // copy stays (the taller tiles gain more than the copy costs).  Training
+  // keeps the copy, which the backward reads.
   const int d = cfg->hidden_size, n1 = cfg->ffn_hidden > 0 ? cfg->ffn_hidden : d;
-  if (!cfg->save_preact && grouped_gemm_is_big(d, n1, cfg->dtype) && L.T * d * 2 < (int64_t(1) << 31)) {
+  if (!cfg->save_preact && grouped_gemm_is_big(d, n1, cfg->dtype) && L.T * d * 2 < (int64_t(1) << 31) &&
+      forward_tile_rows(cfg, L) == 256) {
     int32_t* rt = at<int32_t>(ws, L.row_tok);
     if (ga.T >= 0)
       MOE_TRY_HIP(launch_row_map_finalize(ga, rt, s));

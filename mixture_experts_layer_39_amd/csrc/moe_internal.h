@@ -141,6 +141,8 @@ struct GemmArgs {
                                    // reads X row x_map[r] (the dispatch folded into the loads;
                                    // big path, bf16, contiguous X only)
   int64_t x_rows = 0;
+  int32_t tile_rows = 256;         // row tile height of the large-tile GEMM: 256, or 320 (K-contiguous X,
+                                   // no x_map): an expert of up to 640 rows in two row tiles, not three
 };
 hipError_t launch_grouped_gemm(const GemmArgs& a, int dtype, hipStream_t s);
 // Whether launch_grouped_gemm runs this shape on the large-tile kernel.

@@ -273,6 +273,51 @@ def test_gemm_tail_slices_match_whole_tiles():
     assert torch.equal(plain, extra[8:])
 
 
+def _tail_split_runs_320(G):
+    """The same check with 320-row tiles: 128 experts, 127 of them with 600
+    rows (two row tiles, of 320 and 280 rows) and the last with 640 (two full
+    tiles), so the mean of 601 rows puts the layer's Linears on 320-row
+    tiles; the second batch puts 320 more tokens for the last expert in
+    front, which gives it a third full tile: 257 row tiles, the last of them
+    (holding tokens of the first batch) run as 64-feature slices with five
+    32-row blocks per token-side wave."""
+    E, d, h, per, last, extra = 128, 256, 2048, 600, 640, 320
+    g = torch.Generator(device=DEV)
+    g.manual_seed(4243)
+    T = (E - 1) * per + last
+    x = (torch.randn(T + extra, d, generator=g, device=DEV)).to(torch.bfloat16)
+    choice = torch.cat([torch.full((extra,), E - 1), torch.arange(E - 1).repeat_interleave(per),
+                        torch.full((last,), E - 1)]).to(DEV)
+    logits = torch.randn(T + extra, E, generator=g, device=DEV) * 0.1
+    logits[torch.arange(T + extra, device=DEV), choice] += 8.0
+    w = dict(w1=(torch.randn(E, h, d, generator=g, device=DEV) * 0.02).to(torch.bfloat16),
+             b1=(torch.randn(E, h, generator=g, device=DEV) * 0.02).to(torch.bfloat16),
+             w2=(torch.randn(E, d, h, generator=g, device=DEV) * 0.02).to(torch.bfloat16),
+             b2=(torch.randn(E, d, generator=g, device=DEV) * 0.02).to(torch.bfloat16))
+    outs = []
+    for lo in (extra, 0):
+        n = T + extra - lo
+        cfg = B.make_config(n, d, E, 1, 1.0, 0, False, h, B.MOE_ACT_GELU, B.MOE_BF16, small_batch=-1)
+        ws = workspace(cfg, DEV)
+        out = torch.empty(n, d, dtype=torch.bfloat16, device=DEV)
+        loss = torch.empty(1, dtype=torch.float32, device=DEV)
+        count = torch.empty(E, dtype=torch.int32, device=DEV)
+        B.moe_layer_forward(cfg, x[lo:], None, None, logits[lo:].contiguous(), w["w1"], w["b1"], w["w2"], w["b2"],
+                            out, loss, count, ws=ws)
+        outs.append((out, count))
+    torch.cuda.synchronize()
+    return outs
+
+
+def test_gemm_tail_slices_match_whole_tiles_320():
+    G = torch.cuda.get_device_properties(0).multi_processor_count // 8 * 8
+    if not (257 > G and (257 % G) * 4 <= G):
+        pytest.skip(f"{G} workgroups: 257 tiles leave no short last round on this device")
+    (plain, c0), (extra, c1) = _tail_split_runs_320(G)
+    assert int(c1[-1]) == 960 and int(c0[-1]) == 640 and int(c0[0]) == 600
+    assert torch.equal(plain, extra[320:])
+
+
 FULL = ["top2_e8", "top2_e64", "skew_e16", "nodrop_e128"]
 
 
@@ -280,8 +325,9 @@ FULL = ["top2_e8", "top2_e64", "skew_e16", "nodrop_e128"]
 @pytest.mark.parametrize("name", FULL)
 def test_layer_full_size(name):
     """Full size, in the launch configuration the benchmark times (inference:
-    no saved pre-activation, h_disp at the layer's own pitch, the first
-    Linear gathering its rows from x instead of a dispatched copy): every
+    no saved pre-activation, h_disp at the layer's own pitch; at top2_e8,
+    whose x is under 16 MiB, the first Linear gathers its rows from x instead
+    of reading a dispatched copy): every
     routing output bit-exact, and every element of h_disp, y_disp and out
     against the whole oracle forward; the dispatch entry point on the same
     routing gives every packed row of the oracle's x_disp bit-exact."""
