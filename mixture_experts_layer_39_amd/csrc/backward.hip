@@ -366,36 +366,41 @@ __global__ __launch_bounds__(256) void router_pack_kernel(const uint16_t* __rest
 
 __device__ __forceinline__ bf16x8 ld8(const uint16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
-// Workgroup: 32 tokens, all d features in chunks of 256.  Per chunk, phase
-// 1: wave w computes the router term for the 32 tokens (MFMA columns) and
-// features 64w .. +63 of the chunk (two 32-row MFMA blocks; row l&31 is
-// feature fmap(l&31), so accumulator register r of lane l is feature
-// 16*(l>>5) + r of its block) and writes it to LDS as [token][feature] fp32.
-// Phase 2: wave w takes tokens 8w .. 8w+7, two per instruction (half a
-// wavefront covers a token's 256 features as 16-byte vectors), adds the
+// Workgroup: 32 * TB tokens, all d features in chunks of 256.  Per chunk,
+// phase 1: wave w computes the router term for the tokens (TB blocks of 32
+// MFMA columns) and features 64w .. +63 of the chunk (two 32-row MFMA
+// blocks; row l&31 is feature fmap(l&31), so accumulator register r of lane
+// l is feature 16*(l>>5) + r of its block) and writes it to LDS as
+// [token][feature] fp32.  Each chunk streams the packed router weight's
+// 64 KB for the chunk from L2, so TB = 2 halves that stream per token (it
+// was the larger part of the kernel's operand traffic at 32 tokens).
+// Phase 2: wave w takes tokens 8*TB*w .. +8*TB-1, two per instruction (half
+// a wavefront covers a token's 256 features as 16-byte vectors), adds the
 // token's gathered dX_disp rows and the router term and stores the row
 // segment.  One workgroup walks each token's rows from start to end, and its
 // B fragments (the tokens' logit gradient) are loaded once for all chunks.
 // The gathered rows of a chunk are issued after its operand loads (loads
 // complete in order, so the K loop never waits on them).  EPK = Ep / 16 K
 // steps (0: no router term).
-constexpr int kIgTok = 32, kIgFeat = 256, kIgPitch = kIgFeat + 4;
+constexpr int kIgFeat = 256, kIgPitch = kIgFeat + 4;
 
-template <int EPK>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) void input_grad_kernel(InputGradArgs a) {
+template <int EPK, int TB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TB == 1 ? 4 : 2, 8)))
+void input_grad_kernel(InputGradArgs a) {
+  constexpr int kIgTok = 32 * TB;     // tokens per workgroup
+  constexpr int NP = 4 * TB;          // phase 2: token pairs per wave
   __shared__ __attribute__((aligned(16))) float tile[EPK > 0 ? kIgTok : 1][kIgPitch];
   constexpr int Ep = EPK * 16;
-  constexpr bool HOIST = false;       // B fragments reloaded per chunk (L1 hits): registers go to occupancy
   const int d = a.d, k = a.k;
   const int64_t t0 = (int64_t)blockIdx.x * kIgTok;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 31, hh = lane >> 5;
 
-  // phase 2: this lane's token pair rows (token 8w + 2i + hh), -1 if none
-  int64_t rw0[4], rw1[4];
+  // phase 2: this lane's token pair rows (token 8*TB*w + 2i + hh), -1 if none
+  int64_t rw0[NP], rw1[NP];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t t = t0 + 8 * wave + 2 * i + hh;
+  for (int i = 0; i < NP; ++i) {
+    const int64_t t = t0 + 8 * TB * wave + 2 * i + hh;
     rw0[i] = rw1[i] = -1;
     if (t < a.T) {
       const int s0 = a.slot[t * k];
@@ -407,27 +412,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
     }
   }
 
-  // phase 1 operands
-  const int64_t tb = t0 + n;
-  const bool tv = tb < a.T;
+  // phase 1 operands: the B fragments (the tokens' logit gradient, hi and
+  // lo) are reloaded per chunk from L1 rather than kept in registers
   const bf16x8 zero = {};
-  const uint16_t* brow = EPK > 0 ? a.dl_hl + (tv ? tb : 0) * 2 * Ep + 8 * hh : nullptr;
-  bf16x8 bh[HOIST ? (EPK > 0 ? EPK : 1) : 1], bl[HOIST ? (EPK > 0 ? EPK : 1) : 1];
-  if constexpr (HOIST && EPK > 0) {
+  const uint16_t* brow[TB];
+  bool tv[TB];
 #pragma unroll
-    for (int ks = 0; ks < EPK; ++ks) {
-      bh[ks] = tv ? ld8(brow + ks * 16) : zero;
-      bl[ks] = tv ? ld8(brow + Ep + ks * 16) : zero;
-    }
+  for (int b = 0; b < TB; ++b) {
+    const int64_t tb = t0 + 32 * b + n;
+    tv[b] = tb < a.T;
+    brow[b] = EPK > 0 ? a.dl_hl + (tv[b] ? tb : 0) * 2 * Ep + 8 * hh : nullptr;
   }
 
   for (int f0 = 0; f0 < d; f0 += kIgFeat) {
     const int fl = f0 + 8 * n;            // phase 2: this lane's 8 features
     const bool fin = fl < d;
-    uint4 g0[4], g1[4];
+    uint4 g0[NP], g1[NP];
     auto gather = [&]() {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < NP; ++i) {
         g0[i] = g1[i] = make_uint4(0u, 0u, 0u, 0u);
         if (fin && rw0[i] >= 0) g0[i] = *reinterpret_cast<const uint4*>(a.dx_disp + rw0[i] * d + fl);
         if (fin && rw1[i] >= 0) g1[i] = *reinterpret_cast<const uint4*>(a.dx_disp + rw1[i] * d + fl);
@@ -436,20 +439,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
     if constexpr (EPK > 0) {
       const int fw = f0 + 64 * wave;
       const int nb = min(2, (d - fw) / 32);     // valid feature blocks (wave-uniform, may be <= 0)
-      f32x16 acc[2];
+      f32x16 acc[2][TB];
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[b][r] = 0.f;
+        for (int c = 0; c < TB; ++c)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[b][c][r] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < EPK; ++ks) {
-        bf16x8 h, l;
-        if constexpr (HOIST) {
-          h = bh[ks];
-          l = bl[ks];
-        } else {
-          h = tv ? ld8(brow + ks * 16) : zero;
-          l = tv ? ld8(brow + Ep + ks * 16) : zero;
+        bf16x8 h[TB], l[TB];
+#pragma unroll
+        for (int c = 0; c < TB; ++c) {
+          h[c] = tv[c] ? ld8(brow[c] + ks * 16) : zero;
+          l[c] = tv[c] ? ld8(brow[c] + Ep + ks * 16) : zero;
         }
         bf16x8 av[2];
 #pragma unroll
@@ -460,30 +463,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
           gather();
           __builtin_amdgcn_sched_barrier(0);
         }
-        // hi products of both blocks, then lo: never two MFMAs back to back on one accumulator
+        // hi products of every block, then lo: never two MFMAs back to back on one accumulator
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
-          if (b < nb) acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[b], h, acc[b], 0, 0, 0);
+        for (int c = 0; c < TB; ++c)
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
-          if (b < nb) acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[b], l, acc[b], 0, 0, 0);
+          for (int b = 0; b < 2; ++b)
+            if (b < nb) acc[b][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[b], h[c], acc[b][c], 0, 0, 0);
+#pragma unroll
+        for (int c = 0; c < TB; ++c)
+#pragma unroll
+          for (int b = 0; b < 2; ++b)
+            if (b < nb) acc[b][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[b], l[c], acc[b][c], 0, 0, 0);
       }
       __syncthreads();   // the previous chunk's phase 2 has read the tile
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        float4* dst = reinterpret_cast<float4*>(&tile[n][64 * wave + 32 * b + 16 * hh]);
+      for (int c = 0; c < TB; ++c)
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          dst[q] = make_float4(acc[b][4 * q], acc[b][4 * q + 1], acc[b][4 * q + 2], acc[b][4 * q + 3]);
-      }
+        for (int b = 0; b < 2; ++b) {
+          float4* dst = reinterpret_cast<float4*>(&tile[32 * c + n][64 * wave + 32 * b + 16 * hh]);
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            dst[q] = make_float4(acc[b][c][4 * q], acc[b][c][4 * q + 1], acc[b][c][4 * q + 2], acc[b][c][4 * q + 3]);
+        }
       __syncthreads();
     } else {
       gather();
     }
 
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int tl = 8 * wave + 2 * i + hh;
+    for (int i = 0; i < NP; ++i) {
+      const int tl = 8 * TB * wave + 2 * i + hh;
       const int64_t t = t0 + tl;
       if (t >= a.T || !fin) continue;
       const uint32_t u0[4] = {g0[i].x, g0[i].y, g0[i].z, g0[i].w};
@@ -652,23 +661,31 @@ hipError_t launch_router_pack(const void* w_router, uint16_t* wfrag, int E, int 
   return hipGetLastError();
 }
 
-hipError_t launch_input_grad(const InputGradArgs& a, hipStream_t s) {
-  if (a.T == 0) return hipSuccess;
-  const int64_t tiles = (a.T + kIgTok - 1) / kIgTok;
+template <int TB>
+hipError_t launch_input_grad_tb(const InputGradArgs& a, hipStream_t s) {
+  const int64_t tiles = (a.T + 32 * TB - 1) / (32 * TB);
   const dim3 grid((unsigned)tiles);
   switch (a.dl_hl ? a.Ep / 16 : 0) {
-    case 0: hipLaunchKernelGGL(input_grad_kernel<0>, grid, dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL(input_grad_kernel<2>, grid, dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL(input_grad_kernel<4>, grid, dim3(256), 0, s, a); break;
-    case 6: hipLaunchKernelGGL(input_grad_kernel<6>, grid, dim3(256), 0, s, a); break;
-    case 8: hipLaunchKernelGGL(input_grad_kernel<8>, grid, dim3(256), 0, s, a); break;
-    case 10: hipLaunchKernelGGL(input_grad_kernel<10>, grid, dim3(256), 0, s, a); break;
-    case 12: hipLaunchKernelGGL(input_grad_kernel<12>, grid, dim3(256), 0, s, a); break;
-    case 14: hipLaunchKernelGGL(input_grad_kernel<14>, grid, dim3(256), 0, s, a); break;
-    case 16: hipLaunchKernelGGL(input_grad_kernel<16>, grid, dim3(256), 0, s, a); break;
+    case 0: hipLaunchKernelGGL((input_grad_kernel<0, TB>), grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((input_grad_kernel<2, TB>), grid, dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((input_grad_kernel<4, TB>), grid, dim3(256), 0, s, a); break;
+    case 6: hipLaunchKernelGGL((input_grad_kernel<6, TB>), grid, dim3(256), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((input_grad_kernel<8, TB>), grid, dim3(256), 0, s, a); break;
+    case 10: hipLaunchKernelGGL((input_grad_kernel<10, TB>), grid, dim3(256), 0, s, a); break;
+    case 12: hipLaunchKernelGGL((input_grad_kernel<12, TB>), grid, dim3(256), 0, s, a); break;
+    case 14: hipLaunchKernelGGL((input_grad_kernel<14, TB>), grid, dim3(256), 0, s, a); break;
+    case 16: hipLaunchKernelGGL((input_grad_kernel<16, TB>), grid, dim3(256), 0, s, a); break;
     default: return hipErrorNotSupported;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_input_grad(const InputGradArgs& a, hipStream_t s) {
+  if (a.T == 0) return hipSuccess;
+  // 64 tokens per workgroup once that still gives every CU two workgroups
+  // (the router term's weight stream per token halves); 32 below that
+  if (a.dl_hl && a.T >= (int64_t)64 * 2 * device_cus()) return launch_input_grad_tb<2>(a, s);
+  return launch_input_grad_tb<1>(a, s);
 }
 
 hipError_t launch_router_wgrad(const RouterWgradArgs& a, hipStream_t s) {

@@ -1092,19 +1092,6 @@ hipError_t launch_bf16(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Number of compute units of the current device (the persistent grid).
-int device_cus() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
-  }
-  return cached[dev];
-}
-
 template <int EPI, int ACT, int TOK, int FEAT, int MODE, int RB = 4>
 hipError_t launch_big(const BigArgs& a, hipStream_t s) {
   auto kern = gemm_bf16_big_kernel<EPI, ACT, TOK, FEAT, MODE, RB>;
@@ -1169,6 +1156,19 @@ hipError_t launch_bf16_big(const GemmArgs& g, hipStream_t s) {
 }
 
 }  // namespace
+
+// Number of compute units of the current device (the persistent grid).
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
 
 // The four GEMMs of the expert backward on the large-tile kernel (transposed
 // operands read with ds_read_b64_tr_b16), or hipErrorNotSupported when the

@@ -145,6 +145,8 @@ struct GemmArgs {
                                    // no x_map): an expert of up to 640 rows in two row tiles, not three
 };
 hipError_t launch_grouped_gemm(const GemmArgs& a, int dtype, hipStream_t s);
+// Compute units of the current device (cached per device).
+int device_cus();
 // Whether launch_grouped_gemm runs this shape on the large-tile kernel.
 bool grouped_gemm_is_big(int64_t K, int64_t N, int dtype);
 // Expert weight [E, N, K] (bf16) into the packed layout: blocks of 256 rows

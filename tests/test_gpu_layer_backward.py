@@ -120,6 +120,11 @@ DB_CASES = [  # T, d, E, k, cf, router
     (257, 256, 64, 2, 1.0, True),
     (130, 96, 5, 1, 0.6, True),
     (70, 2048, 256, 2, 1.0, True),
+    # from 2 x 64 tokens per CU on, 64-token workgroups (two 32-token MFMA
+    # blocks for the router term); a ragged last workgroup, a partial
+    # feature chunk
+    (32805, 512, 64, 2, 1.0, True),
+    (33000, 320, 128, 2, 0.9, True),
 ]
 
 
