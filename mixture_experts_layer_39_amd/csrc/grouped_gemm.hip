@@ -519,7 +519,7 @@ __device__ __forceinline__ void big_issue(const BigCtx& c, __amdgpu_buffer_rsrc_
                                           const uint32_t (&gv)[16]) {
 #pragma unroll
   for (int i = 0; i < 4 * RB; ++i)
-    if (c.wave < 2 || i < 4 * NF) big_issue_one<GATHER, RB == 5>(c, lr, stage, kstep, i, NF, gv[i < 16 ? i : 15]);
+    if (c.wave < 2 || i < 4 * NF) big_issue_one<GATHER, RB == 5>(c, lr, stage, kstep, i, NF, gv[GATHER ? i : 0]);   // gathering: RB == 4, 16 loads
   static_assert(!GATHER || RB == 4, "gathered token rows use 256-row tiles");
 }
 
@@ -790,14 +790,14 @@ __device__ __forceinline__ void big_tile(const BigArgs& a, const BigCtx& c, cons
           for (int q = j * LPH / NM; q < (j + 1) * LPH / NM && j < NM; ++q)
             if (c.wave < 2 || lhalf * LPH + q < 4 * NF)
               big_issue_one<GATHER, RB == 5>(c, llr, lstage, lkstep, lhalf * LPH + q, NF,
-                                    gv[(lhalf * LPH + q) & 15]);
+                                    gv[GATHER ? lhalf * LPH + q : 0]);
         } else {
           if (j == 0) {
 #pragma unroll
             for (int q = 0; q < LPH; ++q)
               if (c.wave < 2 || lhalf * LPH + q < 4 * NF)
                 big_issue_one<GATHER, RB == 5>(c, llr, lstage, lkstep, lhalf * LPH + q, NF,
-                                      gv[(lhalf * LPH + q) & 15]);
+                                      gv[GATHER ? lhalf * LPH + q : 0]);
           }
         }
       }
