@@ -46,6 +46,8 @@ CASES = [
     (BANDS, 128, 256, B.MOE_ACT_GELU, None),
     (BANDS, 128, 256, B.MOE_ACT_GELU, 1.3),
     (BANDS, 192, 0, B.MOE_ACT_NONE, 1.3),
+    (BANDS, 128, 320, B.MOE_ACT_GELU, 1.3),   # 320-row tiles, a part-filled feature tile (N = 320)
+    (BANDS, 64, 128, B.MOE_ACT_RELU, 1.3),    # 320-row tiles with 1 and 2 K steps
 ]
 
 
