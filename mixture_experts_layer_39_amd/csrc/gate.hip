@@ -938,6 +938,8 @@ __device__ void gate_counts_and_loss(const GateArgs& a) {
   const int64_t C = a.C;
   const int d0 = tid < E ? a.demand[tid] : 0;
   const int d1 = (tid < E && K == 2) ? a.demand[E + tid] : 0;
+  // loaded with the demand, not after the offsets' scan
+  const double msum = (tid < E && a.loss_kind == LOSS_BALANCE && T > 0) ? a.me_sum[tid] : 0.0;
   int kept = 0;
   if (tid < E) {
     int64_t kp;
@@ -959,7 +961,7 @@ __device__ void gate_counts_and_loss(const GateArgs& a) {
   double loss = 0.0;
   if (T > 0) {
     if (a.loss_kind == LOSS_BALANCE) {
-      const double term = tid < E ? (a.me_sum[tid] / (double)T) * ((double)d0 / (double)T) : 0.0;
+      const double term = tid < E ? (msum / (double)T) * ((double)d0 / (double)T) : 0.0;
       loss = (double)E * block_sum(term, s_wd);
     } else {
       const double denom = (double)K * (double)T;
@@ -986,20 +988,29 @@ __global__ __launch_bounds__(256) void gate_scan_kernel(GateArgs a) {
   // each thread owns a contiguous run of tiles
   const int per = (nt + 255) / 256;
   const int lo = min(nt, tid * per), hi = min(nt, lo + per);
-  int sum = 0;
-  for (int i = lo; i < hi; ++i) sum += col[i];
+  // the column's counts and (choice-0 columns) the expert's per-tile
+  // probability sums are loaded together, before the scan's barriers
+  // (the run's first count stays in a register for the prefix pass: up to
+  // 256 tiles that is the whole run)
+  const int first = lo < hi ? col[lo] : 0;
+  int sum = first;
+  for (int i = lo + 1; i < hi; ++i) sum += col[i];
+  double m = 0.0;   // probability mass of expert c: runs in tile order, then a fixed tree
+  if (c < E)
+    for (int i = lo; i < hi; ++i) m += (double)a.me_tile[(int64_t)i * E + c];
   const int incl = block_incl_scan(sum, s_wi);
   int run = incl - sum;
-  for (int i = lo; i < hi; ++i) {
+  if (lo < hi) {
+    col[lo] = run;
+    run += first;
+  }
+  for (int i = lo + 1; i < hi; ++i) {
     const int v = col[i];
     col[i] = run;
     run += v;
   }
   if (tid == 255) a.demand[c] = incl;
   if (c < E) {
-    // probability mass of expert c: runs in tile order, then a fixed tree
-    double m = 0.0;
-    for (int i = lo; i < hi; ++i) m += (double)a.me_tile[(int64_t)i * E + c];
     m = block_sum(m, s_wd);
     if (tid == 0) a.me_sum[c] = m;
   }
