@@ -62,11 +62,33 @@ __device__ __forceinline__ Claims token_claims(const int32_t* __restrict__ exper
 // shape (T = 16384, d = 2048).
 constexpr int kUnroll = 4;
 
-// One token row to ND packed rows, kUnroll vectors per lane and pass.
+// The first pass of a token row (its first kUnroll * 64 vectors), loaded
+// before the token's index loads so that the row and the indices are in
+// flight together.
+__device__ __forceinline__ void load_first_pass(const u32x4* __restrict__ src, int lane, int nvec,
+                                                u32x4 (&pre)[kUnroll]) {
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const int v = lane + u * 64;
+    pre[u] = v < nvec ? __builtin_nontemporal_load(src + v) : u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+// One token row to ND packed rows, kUnroll vectors per lane and pass; the
+// first pass comes from pre.
 template <int ND>
 __device__ __forceinline__ void copy_row(const u32x4* __restrict__ src, u32x4* __restrict__ d0,
-                                         u32x4* __restrict__ d1, int lane, int nvec) {
-  int v0 = lane;
+                                         u32x4* __restrict__ d1, int lane, int nvec,
+                                         const u32x4 (&pre)[kUnroll]) {
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const int v = lane + u * 64;
+    if (v < nvec) {
+      __builtin_nontemporal_store(pre[u], d0 + v);
+      if constexpr (ND == 2) __builtin_nontemporal_store(pre[u], d1 + v);
+    }
+  }
+  int v0 = lane + kUnroll * 64;
   for (; v0 + (kUnroll - 1) * 64 < nvec; v0 += kUnroll * 64) {
     u32x4 val[kUnroll];
 #pragma unroll
@@ -94,13 +116,15 @@ __global__ __launch_bounds__(256) void dispatch_kernel(const u32x4* __restrict__
   const int64_t wave_id = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
   for (int64_t t = wave_id; t < T; t += nwaves) {
+    const u32x4* src = x + t * nvec;
+    u32x4 pre[kUnroll];
+    load_first_pass(src, lane, nvec, pre);
     const Claims c = token_claims<false>(expert_idx, slot, nullptr, offset, t, k);
     if (c.r0 < 0 && c.r1 < 0) continue;
-    const u32x4* src = x + t * nvec;
     // one branch per token, outside the copy, so that the stores of a pass
     // issue back to back
-    if (c.r0 >= 0 && c.r1 >= 0) copy_row<2>(src, x_disp + c.r0 * nvec, x_disp + c.r1 * nvec, lane, nvec);
-    else copy_row<1>(src, x_disp + (c.r0 >= 0 ? c.r0 : c.r1) * nvec, nullptr, lane, nvec);
+    if (c.r0 >= 0 && c.r1 >= 0) copy_row<2>(src, x_disp + c.r0 * nvec, x_disp + c.r1 * nvec, lane, nvec, pre);
+    else copy_row<1>(src, x_disp + (c.r0 >= 0 ? c.r0 : c.r1) * nvec, nullptr, lane, nvec, pre);
   }
 }
 
@@ -120,6 +144,9 @@ __global__ __launch_bounds__(256) void dispatch_finalize_kernel(const u32x4* __r
   const int k = g.k, E = g.E;
   const int64_t T = g.T, C = g.C;
   for (int64_t t = wave_id; t < T; t += nwaves) {
+    const u32x4* src = x + t * nvec;
+    u32x4 pre[kUnroll];
+    load_first_pass(src, lane, nvec, pre);
     const int64_t tile = t / g.tile_tokens;
     const int e0 = g.expert_idx[t * k], q0 = g.slot[t * k];
     const int e1 = k == 2 ? g.expert_idx[t * k + 1] : 0, q1 = k == 2 ? g.slot[t * k + 1] : 0;
@@ -136,9 +163,8 @@ __global__ __launch_bounds__(256) void dispatch_finalize_kernel(const u32x4* __r
     const int64_t r0 = s0 >= 0 ? o0 + s0 : -1;
     const int64_t r1 = s1 >= 0 ? o1 + s1 : -1;
     if (r0 < 0 && r1 < 0) continue;
-    const u32x4* src = x + t * nvec;
-    if (r0 >= 0 && r1 >= 0) copy_row<2>(src, x_disp + r0 * nvec, x_disp + r1 * nvec, lane, nvec);
-    else copy_row<1>(src, x_disp + (r0 >= 0 ? r0 : r1) * nvec, nullptr, lane, nvec);
+    if (r0 >= 0 && r1 >= 0) copy_row<2>(src, x_disp + r0 * nvec, x_disp + r1 * nvec, lane, nvec, pre);
+    else copy_row<1>(src, x_disp + (r0 >= 0 ? r0 : r1) * nvec, nullptr, lane, nvec, pre);
   }
 }
 
