@@ -446,18 +446,36 @@ void input_grad_kernel(InputGradArgs a) {
         for (int c = 0; c < TB; ++c)
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[b][c][r] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < EPK; ++ks) {
-        bf16x8 h[TB], l[TB];
+      // with 64 tokens (TB = 2, 256 registers) the operands of step ks + 1
+      // are loaded while step ks's MFMAs run; 32-token workgroups keep the
+      // register budget of four waves per SIMD and load each step's own
+      constexpr bool PIPE = TB == 2;
+      bf16x8 hn[TB], ln[TB], avn[2];
+      auto load_ops = [&](int ks) {
 #pragma unroll
         for (int c = 0; c < TB; ++c) {
-          h[c] = tv[c] ? ld8(brow[c] + ks * 16) : zero;
-          l[c] = tv[c] ? ld8(brow[c] + Ep + ks * 16) : zero;
+          hn[c] = tv[c] ? ld8(brow[c] + ks * 16) : zero;
+          ln[c] = tv[c] ? ld8(brow[c] + Ep + ks * 16) : zero;
         }
-        bf16x8 av[2];
 #pragma unroll
         for (int b = 0; b < 2; ++b)
-          av[b] = b < nb ? ld8(a.wfrag + (((int64_t)(fw / 32 + b) * EPK + ks) * 64 + lane) * 8) : zero;
+          avn[b] = b < nb ? ld8(a.wfrag + (((int64_t)(fw / 32 + b) * EPK + ks) * 64 + lane) * 8) : zero;
+      };
+      if constexpr (PIPE) load_ops(0);
+#pragma unroll
+      for (int ks = 0; ks < EPK; ++ks) {
+        if constexpr (!PIPE) load_ops(ks);
+        bf16x8 h[TB], l[TB], av[2];
+#pragma unroll
+        for (int c = 0; c < TB; ++c) {
+          h[c] = hn[c];
+          l[c] = ln[c];
+        }
+        av[0] = avn[0];
+        av[1] = avn[1];
+        if constexpr (PIPE) {
+          if (ks + 1 < EPK) load_ops(ks + 1);
+        }
         if (ks == EPK - 1) {
           __builtin_amdgcn_sched_barrier(0);
           gather();
